@@ -1,0 +1,158 @@
+"""Expert FFN (GMM1, activation, requantization, GMM2) and the weighted combine.
+
+MegaMoE page, "A8W8-FP quantization scenario":
+  stage 1  X_e, S_X,e = Q_MX(X[T_e])                (routing.gather_rows)
+  stage 2  G_e = DQ(X_e) . DQ(W1_e^(G)),  U_e = DQ(X_e) . DQ(W1_e^(U)),
+           A_e = Activation(G_e, U_e),  A^_e, S_A,e = Q_MX(A_e)  (same FP8 type)
+  stage 3  O_e = DQ(A^_e) . DQ(W2_e)
+  stage 4  Y[i] = sum_k W[i,k] O[pi(i,k)] + sum_s O_s^shared[i],  Y is BF16
+"Activation function formulas": sigma(z) = 1/(1+e^-z), SiLU(z) = z sigma(z),
+swiglu A = SiLU(G_c) * U_c, with c = +inf when no clamp is configured.
+"MXFP quantization scenario constraints": weight1 (E, 2I, H) and weight2
+(E, H, I), each output channel holding its K-contiguous inputs; G is the first
+I output channels of weight1 and U the last I ("first N/2 columns ... last N/2
+columns" of the logical H x 2I matrix).
+
+Readings: accumulations are float64 on exact dequantized operands; the
+activation is evaluated in float64 and rounded once to fp32 before the MX
+requantization (the pages do not give A's precision); the combine sums in
+float64 in k order, then the shared experts, and rounds once to bf16 (one GPU:
+no bf16 wire format between expert output and combine).
+"""
+
+from __future__ import annotations
+
+import numpy as np
+
+from . import mxfp, routing
+
+
+def silu(z):
+    z = np.asarray(z, dtype=np.float64)
+    return z / (1.0 + np.exp(-z))
+
+
+def swiglu(g, u):
+    """A = SiLU(G) * U (no clamp)."""
+    return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def gmm(aq, sa, wq, ws, fmt):
+    """DQ_MX(A) . DQ_MX(W)^T for W stored (out, in): float64 [m, out]."""
+    ad = mxfp.dequantize(aq, sa, fmt)
+    wd = mxfp.dequantize(wq, ws, fmt)
+    return ad @ wd.T
+
+
+def expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt):
+    """Stages 2-3 for the rows of one expert. xq/sx: [m, H] codes/scales."""
+    inter = w2q.shape[1]
+    h1 = gmm(xq, sx, w1q, w1s, fmt)
+    a = mxfp.fp32_round(swiglu(h1[:, :inter], h1[:, inter:]))
+    aq, sa = mxfp.quantize(a, fmt)
+    o = gmm(aq, sa, w2q, w2s, fmt)
+    return dict(h1=h1, a=a, aq=aq, sa=sa, o=o)
+
+
+def _getter(weights):
+    """weights: either a tuple of stacked arrays (w1q, w1s, w2q, w2s) with a leading
+    expert axis, or a callable e -> (w1q[e], w1s[e], w2q[e], w2s[e])."""
+    if callable(weights):
+        return weights
+    w1q, w1s, w2q, w2s = weights
+    return lambda e: (w1q[e], w1s[e], w2q[e], w2s[e])
+
+
+def combine(o_rows, expanded_row_idx, topk_weights, shared_o=()):
+    """Stage 4: Y[t] = bf16( sum_k w[t,k] O[row(t,k)] + sum_s O_s[t] ), float64 sum."""
+    w = np.asarray(topk_weights, dtype=np.float64)
+    n, k = w.shape
+    idx = np.asarray(expanded_row_idx).reshape(n, k)
+    y = np.zeros((n, o_rows.shape[1]), dtype=np.float64)
+    for j in range(k):
+        y += w[:, j:j + 1] * o_rows[idx[:, j]]
+    for o_s in shared_o:
+        y += o_s
+    return mxfp.bf16_round(y)
+
+
+def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=()) -> dict:
+    """The whole layer on all tokens, in the permuted (expert-contiguous) order.
+
+    x: [N, H] values (bf16 as float64); topk_ids int [N, K]; topk_weights [N, K];
+    weights: see _getter; shared: list of (w1q, w1s, w2q, w2s) per shared expert.
+    Returns routing, xq/sx (permuted), h1 [F, 2I], a, aq, sa, o [F, H],
+    shared outputs, y (float64 bf16 values) and expert_token_nums (int32 [E])."""
+    x = np.asarray(x, dtype=np.float64)
+    get = _getter(weights)
+    quant_mode = {"e5m2": 2, "e4m3": 3}[fmt]
+    r = routing.init_routing(topk_ids, num_experts)
+    k = r["topk"]
+    xq, sx = routing.gather_rows(x, r["sorted_row_idx"], k, quant_mode)
+    flat = xq.shape[0]
+    parts = {}
+    for e in range(num_experts):
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        if hi > lo:
+            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt)
+    hidden = x.shape[1]
+    inter = get(0)[2].shape[1]
+    out = dict(routing=r, xq=xq, sx=sx,
+               h1=np.zeros((flat, 2 * inter)), a=np.zeros((flat, inter)),
+               aq=np.zeros((flat, inter), np.uint8),
+               sa=np.zeros((flat, mxfp.scale_cols(inter)), np.uint8),
+               o=np.zeros((flat, hidden)))
+    for e, p in parts.items():
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        for name in ("h1", "a", "aq", "sa", "o"):
+            out[name][lo:hi] = p[name]
+    shared_o = []
+    if shared:
+        xq_tok, sx_tok = mxfp.quantize(x, fmt)
+        out["xq_tok"], out["sx_tok"] = xq_tok, sx_tok
+        for sw in shared:
+            shared_o.append(expert_ffn(xq_tok, sx_tok, *sw, fmt)["o"])
+    out["shared_o"] = shared_o
+    full_scatter = routing.inverse(r["sorted_row_idx"])
+    out["y"] = combine(out["o"], full_scatter, topk_weights, shared_o)
+    out["expert_token_nums"] = r["counts"].astype(np.int32)
+    return out
+
+
+def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=()) -> dict:
+    """The layer for selected tokens, one (token, k) at a time, with no permutation
+    (the "brute force" form of stage 1-4: each expert receives a copy of x_t).
+
+    Returns y [len(tokens), H] (bf16 values as float64) and, per (token, k), the
+    expert's h1 and o rows: h1[j, k], o[j, k]."""
+    x = np.asarray(x, dtype=np.float64)
+    ids = np.asarray(topk_ids)
+    w = np.asarray(topk_weights, dtype=np.float64)
+    get = _getter(weights)
+    tokens = list(tokens)
+    k = ids.shape[1]
+    cache = {}
+
+    def expert(e):
+        if e not in cache:
+            if len(cache) >= 16:
+                cache.clear()
+            cache[e] = get(e)
+        return cache[e]
+
+    ys, h1s, os_ = [], [], []
+    for t in tokens:
+        xq_t, sx_t = mxfp.quantize(x[t:t + 1], fmt)
+        acc = np.zeros((1, x.shape[1]))
+        h1_t, o_t = [], []
+        for j in range(k):
+            r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt)
+            acc = acc + w[t, j] * r["o"]
+            h1_t.append(r["h1"][0])
+            o_t.append(r["o"][0])
+        for sw in shared:
+            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt)["o"]
+        ys.append(mxfp.bf16_round(acc)[0])
+        h1s.append(h1_t)
+        os_.append(o_t)
+    return dict(y=np.array(ys), h1=np.array(h1s), o=np.array(os_))

@@ -1,0 +1,139 @@
+"""Pins for oracle.moe: activation, GEMMs, combine, the whole permuted layer.
+
+Independent references: closed forms of SiLU/SwiGLU, an exact integer GEMM on
+the same MX operands, a dense special case (one-hot input reproduces a weight
+row), and the per-token brute force (no permutation) which must equal the
+permuted layer bit for bit when the float64 GEMMs are exact.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import moe_inputs
+from oracle import moe, mxfp, routing
+
+
+def quantized_weights(cfg, n_experts=None, shared=False):
+    n_experts = cfg.experts if n_experts is None else n_experts
+    tag1, tag2 = ("sw1", "sw2") if shared else ("w1", "w2")
+    w1q, w1s, w2q, w2s = [], [], [], []
+    for e in range(n_experts):
+        a = moe_inputs.weight_master(cfg, tag1, e).double().numpy()
+        b = moe_inputs.weight_master(cfg, tag2, e).double().numpy()
+        q1, s1 = mxfp.quantize(a, cfg.fmt)
+        q2, s2 = mxfp.quantize(b, cfg.fmt)
+        w1q.append(q1); w1s.append(s1); w2q.append(q2); w2s.append(s2)
+    return tuple(np.stack(t) for t in (w1q, w1s, w2q, w2s))
+
+
+def layer_inputs(cfg):
+    x = moe_inputs.activations(cfg).double().numpy()
+    return x, moe_inputs.expert_ids(cfg), moe_inputs.gate_weights(cfg)
+
+
+def test_silu_closed_forms():
+    assert moe.silu(np.array([0.0]))[0] == 0.0
+    assert moe.silu(np.array([1.0]))[0] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    assert moe.silu(np.array([-2.0]))[0] == pytest.approx(-2.0 / (1.0 + math.exp(2.0)), rel=1e-15)
+    assert moe.silu(np.array([60.0]))[0] == pytest.approx(60.0, rel=1e-15)
+    assert moe.swiglu(np.array([0.0]), np.array([5.0]))[0] == 0.0
+
+
+def test_gate_is_first_half_up_is_second_half():
+    """x one-hot at k=0 with value 1, all scales 2^0: G = W1[n, 0], U = W1[I + n, 0].
+    With G=2, U=3 the activation is SiLU(2)*3 (swapping the halves would give SiLU(3)*2)."""
+    fmt, h, inter = "e4m3", 32, 32
+    one, two, three = 0x38, 0x40, 0x44
+    xq = np.zeros((1, h), np.uint8); xq[0, 0] = one
+    sx = np.full((1, 2), 127, np.uint8); sx[0, 1] = 0
+    w1q = np.zeros((2 * inter, h), np.uint8); w1q[:inter, 0] = two; w1q[inter:, 0] = three
+    w1s = np.full((2 * inter, 2), 127, np.uint8)
+    w2q = np.zeros((h, inter), np.uint8); w2s = np.full((h, 2), 127, np.uint8)
+    r = moe.expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt)
+    assert np.all(r["h1"][0, :inter] == 2.0) and np.all(r["h1"][0, inter:] == 3.0)
+    expect = np.float32(2.0 / (1.0 + math.exp(-2.0)) * 3.0)
+    assert np.all(r["a"][0] == expect)
+
+
+def test_one_hot_input_reproduces_weight_row():
+    rng = np.random.default_rng(1)
+    fmt = "e5m2"
+    wq = rng.integers(0, 0x7B, size=(48, 64)).astype(np.uint8)
+    ws = rng.integers(110, 140, size=(48, 2)).astype(np.uint8)
+    for k in (0, 17, 40, 63):
+        aq = np.zeros((1, 64), np.uint8); aq[0, k] = 0x3C          # 1.0 in E5M2
+        sa = np.full((1, 2), 127, np.uint8)
+        out = moe.gmm(aq, sa, wq, ws, fmt)[0]
+        assert np.array_equal(out, mxfp.dequantize(wq, ws, fmt)[:, k])
+
+
+def exact_int_gemm(aq, sa, wq, ws, fmt):
+    """The same product in exact integer arithmetic: every MX value is an integer
+    multiple of 2^(esub + b - 127); scale everything to integers and use Python ints."""
+    t = mxfp.decode_table(fmt)
+    esub = {"e4m3": -9, "e5m2": -16}[fmt]
+    ai = (t[aq] * 2.0 ** -esub).astype(np.int64)       # exact small integers
+    wi = (t[wq] * 2.0 ** -esub).astype(np.int64)
+    ga = np.repeat(sa[:, : aq.shape[1] // 32].astype(np.int64), 32, axis=1)
+    gw = np.repeat(ws[:, : wq.shape[1] // 32].astype(np.int64), 32, axis=1)
+    out = np.zeros((aq.shape[0], wq.shape[0]), dtype=object)
+    emin = int(ga.min() + gw.min())
+    for i in range(aq.shape[0]):
+        sh_a = ga[i] - emin
+        for n in range(wq.shape[0]):
+            terms = [int(a) * int(w) << int(s1 + s2) for a, w, s1, s2 in zip(ai[i], wi[n], sh_a, gw[n]) if a and w]
+            out[i, n] = sum(terms)
+    scale = 2.0 ** (2 * esub + emin - 254)
+    return out, scale
+
+
+def test_float64_gemm_is_exact_on_small_shapes():
+    cfg = moe_inputs.config("tiny")
+    x, ids, _ = layer_inputs(cfg)
+    w1q, w1s, _, _ = quantized_weights(cfg, n_experts=1)
+    xq, sx = mxfp.quantize(x[:6], cfg.fmt)
+    got = moe.gmm(xq, sx, w1q[0][:20], w1s[0][:20], cfg.fmt)
+    ints, scale = exact_int_gemm(xq, sx, w1q[0][:20], w1s[0][:20], cfg.fmt)
+    for i in range(6):
+        for n in range(20):
+            assert got[i, n] == float(ints[i, n]) * scale
+
+
+def test_brute_force_equals_permuted_layer_bitwise():
+    cfg = moe_inputs.config("tiny", shared=1)
+    x, ids, w = layer_inputs(cfg)
+    weights = quantized_weights(cfg)
+    shared = [tuple(a[0] for a in quantized_weights(cfg, 1, shared=True))]
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared)
+    bf = moe.per_token(x, ids, w, weights, cfg.fmt, range(cfg.tokens), shared=shared)
+    assert np.array_equal(full["y"], bf["y"])
+    inv = routing.inverse(full["routing"]["sorted_row_idx"]).reshape(cfg.tokens, cfg.topk)
+    for t in range(cfg.tokens):
+        for k in range(cfg.topk):
+            assert np.array_equal(full["h1"][inv[t, k]], bf["h1"][t, k])
+            assert np.array_equal(full["o"][inv[t, k]], bf["o"][t, k])
+    assert full["expert_token_nums"].sum() == cfg.flat
+    assert np.array_equal(full["y"], mxfp.bf16_round(full["y"]))
+
+
+def test_topk_one_unit_weight_is_plain_unpermute():
+    cfg = moe_inputs.config("tiny", topk=1)
+    x, ids, _ = layer_inputs(cfg)
+    weights = quantized_weights(cfg)
+    w = np.ones((cfg.tokens, 1), np.float32)
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts)
+    inv = routing.inverse(full["routing"]["sorted_row_idx"])
+    assert np.array_equal(full["y"], mxfp.bf16_round(full["o"][inv]))
+
+
+def test_zero_gate_weights_leave_the_shared_expert():
+    cfg = moe_inputs.config("tiny", shared=1)
+    x, ids, _ = layer_inputs(cfg)
+    weights = quantized_weights(cfg)
+    shared = [tuple(a[0] for a in quantized_weights(cfg, 1, shared=True))]
+    w = np.zeros((cfg.tokens, cfg.topk), np.float32)
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared)
+    xq, sx = mxfp.quantize(x, cfg.fmt)
+    dense = moe.expert_ffn(xq, sx, *shared[0], cfg.fmt)["o"]
+    assert np.array_equal(full["y"], mxfp.bf16_round(dense))

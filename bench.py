@@ -1,0 +1,253 @@
+"""Benchmark of the MI355X MoE-layer hot path (one GPU).
+
+Default workload (the MegaMoE decode-shaped layer): 128 tokens, hidden 7168,
+intermediate 2048, 256 experts all local, topK 8, MXFP8 E4M3 weights with E8M0
+scales, bf16 activations N(0,1), fp32 softmax gate weights. One step is one
+mega_moe call: routing -> gather + MX quantization -> GMM1 + SwiGLU + MX
+requantization -> GMM2 + weighted combine -> bf16 Y. Inputs and weights are
+resident in HBM before the timed region (weights are generated on the GPU with
+a seeded generator and quantized by the library's own MX quantizer, untimed).
+
+Prints one JSON line: MoE layer tokens/s, the roofline of the dominant kernel
+(its duration measured with HIP events that the library records on its stream
+at every stage boundary during the timed steps), and the CPU oracle timed on a
+bounded token sample of the same workload on this host.
+
+    python bench.py [--steps K] [--warmup W] [--config decode|prefill|skewed|tiny|routing]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+MXFP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 MFMA
+RIDGE = MXFP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
+
+
+def log(msg):
+    print(msg, file=sys.stderr, flush=True)
+
+
+def library_weights(torch, rp, moe_inputs, cfg, n_experts, shared):
+    t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
+    h, i = cfg.hidden, cfg.inter
+    q = rp.QUANT_E4M3 if cfg.fmt == "e4m3" else rp.QUANT_E5M2
+    w1q = torch.empty((n_experts, 2 * i, h), dtype=torch.uint8, device="cuda")
+    w1s = torch.empty((n_experts, 2 * i, h // 32), dtype=torch.uint8, device="cuda")
+    w2q = torch.empty((n_experts, h, i), dtype=torch.uint8, device="cuda")
+    w2s = torch.empty((n_experts, h, i // 32), dtype=torch.uint8, device="cuda")
+    for e in range(n_experts):
+        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t1, e, device="cuda"), q)
+        w1q[e].copy_(c); w1s[e].copy_(s)
+        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t2, e, device="cuda"), q)
+        w2q[e].copy_(c); w2s[e].copy_(s)
+    return w1q, w1s, w2q, w2s
+
+
+def layer_work(cfg, ids):
+    """Algorithmic bytes and flops of the two grouped GEMMs (per launch)."""
+    h, i, f = cfg.hidden, cfg.inter, cfg.flat
+    touched = int(np.unique(ids).size)
+    sc = 1.0 + 1.0 / 32.0
+    gmm1_bytes = touched * 2 * i * h * sc + f * h * sc + f * i * sc
+    gmm2_bytes = touched * h * i * sc + f * i * sc + cfg.tokens * h * 4
+    gmm1_flops = 2.0 * f * h * 2 * i
+    gmm2_flops = 2.0 * f * i * h
+    if cfg.shared:
+        n = cfg.tokens
+        gmm1_bytes_s = cfg.shared * (2 * i * h * sc + n * h * sc + n * i * sc)
+        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc)
+        shared = dict(bytes=gmm1_bytes_s + gmm2_bytes_s, flops=cfg.shared * 6.0 * n * h * i)
+    else:
+        shared = dict(bytes=0.0, flops=0.0)
+    return dict(touched=touched, gmm1=dict(bytes=gmm1_bytes, flops=gmm1_flops),
+                gmm2=dict(bytes=gmm2_bytes, flops=gmm2_flops), shared=shared)
+
+
+def roofline_entry(name, ms, work):
+    intensity = work["flops"] / max(work["bytes"], 1.0)
+    if intensity >= RIDGE:
+        achieved = work["flops"] / (ms * 1e-3) / 1e12
+        return dict(kernel=name, bound="mfma", achieved=round(achieved, 2), peak=MXFP8_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(achieved / MXFP8_PEAK_TFLOPS, 4), traffic=None,
+                    algorithmic_per_launch=work["flops"], avg_launch_ms=round(ms, 5))
+    achieved = work["bytes"] / (ms * 1e-3) / 1e9
+    return dict(kernel=name, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, algorithmic_per_launch=work["bytes"],
+                avg_launch_ms=round(ms, 5))
+
+
+def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs):
+    """The oracle (CPU, float64) on a bounded token sample: tokens/s of the per-token layer."""
+    from oracle import moe, mxfp
+    rng = np.random.default_rng(123)
+    tokens = rng.choice(cfg.tokens, size=sample_tokens, replace=False)
+    experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
+    cache = {}
+    for e in experts:  # inputs of the oracle: the sampled experts' weights, quantized by the oracle (untimed)
+        m1 = moe_inputs.weight_master(cfg, "w1", e, device="cuda").cpu().double().numpy()
+        m2 = moe_inputs.weight_master(cfg, "w2", e, device="cuda").cpu().double().numpy()
+        cache[e] = (*mxfp.quantize(m1, cfg.fmt), *mxfp.quantize(m2, cfg.fmt))
+    shared = []
+    for s in range(cfg.shared):
+        m1 = moe_inputs.weight_master(cfg, "sw1", s, device="cuda").cpu().double().numpy()
+        m2 = moe_inputs.weight_master(cfg, "sw2", s, device="cuda").cpu().double().numpy()
+        shared.append((*mxfp.quantize(m1, cfg.fmt), *mxfp.quantize(m2, cfg.fmt)))
+    x = x_cpu.double().numpy()
+    t0 = time.perf_counter()
+    moe.per_token(x, ids, w, lambda e: cache[e], cfg.fmt, tokens, shared=shared)
+    dt = time.perf_counter() - t0
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    except Exception:  # threadpoolctl missing: numpy's elementwise work is single-threaded
+        cores = 1
+    return dict(value=round(sample_tokens / dt, 4), unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{sample_tokens} tokens x topK {cfg.topk} experts ({len(experts)} distinct"
+                       f"{', plus shared' if cfg.shared else ''}), per-token float64 oracle, {dt:.1f} s",
+                seconds=round(dt, 2), host_cpus=os.cpu_count())
+
+
+def bench_mega(args, torch, rp, moe_inputs):
+    cfg = moe_inputs.config(args.config)
+    ids = moe_inputs.expert_ids(cfg)
+    x_cpu = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    log(f"[bench] {cfg.name}: generating weights on the GPU")
+    weights = library_weights(torch, rp, moe_inputs, cfg, cfg.experts, shared=False)
+    shared = library_weights(torch, rp, moe_inputs, cfg, cfg.shared, shared=True) if cfg.shared else None
+    x = x_cpu.cuda()
+    ids_d = torch.from_numpy(ids).cuda()
+    w_d = torch.from_numpy(w).cuda()
+    fmt = rp.FP8_E4M3 if cfg.fmt == "e4m3" else rp.FP8_E5M2
+    nbytes = rp.mega_moe_workspace_bytes(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    torch.cuda.synchronize()
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(rp.MEGA_STAGE_EVENTS)] for _ in range(args.steps)]
+    for st in evs:
+        for ev in st:
+            ev.record()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    log(f"[bench] timing {args.steps} steps")
+    t0 = time.perf_counter()
+    start.record()
+    for k in range(args.steps):
+        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, stage_events=evs[k])
+    end.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms = start.elapsed_time(end) / args.steps
+    stage_ms = {}
+    for j, name in enumerate(rp.MEGA_STAGES):
+        stage_ms[name] = float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
+    work = layer_work(cfg, ids)
+    roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], work["gmm1"]),
+            "gmm2_combine": roofline_entry("gmm2_combine_kernel", stage_ms["gmm2_combine"], work["gmm2"])}
+    dominant = max(roof, key=lambda k: stage_ms[k])
+    roofline = dict(roof[dominant])
+    roofline["other"] = {k: v for k, v in roof.items() if k != dominant}
+    total_bytes = work["gmm1"]["bytes"] + work["gmm2"]["bytes"] + work["shared"]["bytes"]
+    total_flops = work["gmm1"]["flops"] + work["gmm2"]["flops"] + work["shared"]["flops"]
+    out = dict(metric="MoE layer tokens/s", value=round(cfg.tokens / (ms * 1e-3), 1), unit="tokens/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="mxfp8 (fp8 e4m3/e5m2 x e8m0 scales, fp32 accumulate)",
+               data="synthetic (seeded; weights N(0,1/sqrt(fan_in)) quantized to MXFP8 on the GPU)",
+               config=dict(workload=f"{cfg.name}: {cfg.tokens} tokens, hidden {cfg.hidden}, inter {cfg.inter}, "
+                                    f"{cfg.experts} experts, topK {cfg.topk}, shared {cfg.shared}, {cfg.fmt}",
+                           tokens=cfg.tokens, hidden=cfg.hidden, inter=cfg.inter, experts=cfg.experts,
+                           topk=cfg.topk, shared=cfg.shared, fmt=cfg.fmt, touched_experts=work["touched"]),
+               roofline=roofline,
+               layer=dict(algorithmic_bytes=total_bytes, flops=total_flops,
+                          hbm_frac=round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                          mfma_frac=round(total_flops / (ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4)),
+               stages_ms={k: round(v, 5) for k, v in stage_ms.items()},
+               wall_ms_per_step=round(wall * 1e3 / args.steps, 5))
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_mega(cfg, ids, x_cpu, w, args.cpu_sample or (1 if cfg.shared else 2),
+                                                torch, moe_inputs)
+    else:
+        out["cpu_baseline"] = None
+    return out
+
+
+def bench_routing(args, torch, rp, moe_inputs):
+    cfg = moe_inputs.config("routing")
+    ids = moe_inputs.expert_ids(cfg)
+    x_cpu = moe_inputs.activations(cfg)
+    x = x_cpu.cuda()
+    ids_d = torch.from_numpy(ids).cuda()
+    s, e = cfg.active_range
+    q = rp.QUANT_E4M3
+    for _ in range(args.warmup):
+        rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(args.steps):
+        rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
+    end.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / args.steps
+    in_range = (ids >= s) & (ids < e)
+    avail = int(in_range.sum())
+    distinct = int(in_range.any(axis=1).sum())
+    h = cfg.hidden
+    alg = distinct * 2 * h + avail * (h + h // 32) + cfg.flat * 8 + (e - s) * 8
+    achieved = alg / (ms * 1e-3) / 1e9
+    out = dict(metric="MoeInitRoutingV3 rows/s", value=round(avail / (ms * 1e-3), 1), unit="rows/s", n_gpus=1,
+               steps=args.steps, warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True,
+               scaling="weak", vs_baseline=None, dtype="u8 (fp8 e4m3 codes + e8m0)", data="synthetic",
+               config=dict(workload=f"routing: {cfg.tokens} tokens x {h}, topK {cfg.topk}, {cfg.experts} experts, "
+                                    f"active [{s},{e}), scatter index, count histogram, MXFP8 E4M3",
+                           active_rows=avail, distinct_tokens=distinct),
+               roofline=dict(kernel="moe_init_routing (count, scan, scatter, permute_mx)", bound="hbm",
+                             achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                             frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, algorithmic_per_launch=alg,
+                             avg_launch_ms=round(ms, 5)),
+               cpu_baseline=None)
+    return out
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "routing"])
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU oracle sample")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
+              "expert-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import moe_inputs
+    import routing_permute_mxfp8_amd as rp
+    rp.load()
+    if args.config == "routing":
+        out = bench_routing(args, torch, rp, moe_inputs)
+    else:
+        out = bench_mega(args, torch, rp, moe_inputs)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

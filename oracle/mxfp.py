@@ -22,6 +22,8 @@ of scales; a padding scale (odd group count) is 0x00.
 
 from __future__ import annotations
 
+import functools
+
 import numpy as np
 
 GROUP = 32
@@ -34,8 +36,8 @@ FORMATS = {
 EMAX = {"e4m3": 8, "e5m2": 15}
 
 
-def decode_table(fmt: str) -> np.ndarray:
-    """float64[256]: the value of every code, from the sign/exponent/mantissa fields."""
+@functools.lru_cache(maxsize=None)
+def _decode_table(fmt: str) -> np.ndarray:
     eb, mb, bias, has_inf = FORMATS[fmt]
     out = np.empty(256, dtype=np.float64)
     for code in range(256):
@@ -51,7 +53,13 @@ def decode_table(fmt: str) -> np.ndarray:
         else:
             val = (1.0 + m / (1 << mb)) * 2.0 ** (e - bias)
         out[code] = sign * val
+    out.setflags(write=False)
     return out
+
+
+def decode_table(fmt: str) -> np.ndarray:
+    """float64[256]: the value of every code, from the sign/exponent/mantissa fields."""
+    return _decode_table(fmt)
 
 
 def max_finite(fmt: str) -> float:
@@ -108,7 +116,24 @@ def quantize(v, fmt: str):
 
     v: array [..., C] of finite values (any float dtype; taken exactly as float64).
     Returns (codes uint8 [..., C], scales uint8 [..., AlignUp(CeilDiv(C,32),2)]).
+    Rows are independent; large inputs are processed a block of rows at a time.
     """
+    v = np.asarray(v)
+    cols = v.shape[-1]
+    lead = v.shape[:-1]
+    flat = v.reshape(-1, cols)
+    step = max(1, (1 << 16) // max(cols, 1))
+    if flat.shape[0] > step:
+        codes = np.empty(flat.shape, dtype=np.uint8)
+        scales = np.empty((flat.shape[0], scale_cols(cols)), dtype=np.uint8)
+        for lo in range(0, flat.shape[0], step):
+            codes[lo:lo + step], scales[lo:lo + step] = _quantize_rows(flat[lo:lo + step], fmt)
+        return codes.reshape(lead + (cols,)), scales.reshape(lead + (scale_cols(cols),))
+    c, s = _quantize_rows(flat, fmt)
+    return c.reshape(lead + (cols,)), s.reshape(lead + (scale_cols(cols),))
+
+
+def _quantize_rows(v, fmt: str):
     v = np.asarray(v, dtype=np.float64)
     assert np.all(np.isfinite(v)), "MX quantization input must be finite"
     cols = v.shape[-1]

@@ -1,0 +1,337 @@
+"""Python binding of the MI355X MoE-layer hot path (libmoe_mx.so, C ABI in include/moe_mx.h).
+
+Argument marshalling only: outputs and workspaces are allocated with torch on the
+tensors' device, pointers and the current HIP stream are passed to the library,
+and every step of the computation runs in the library's HIP kernels. If the
+library has not been built (python -m routing_permute_mxfp8_amd.build, or
+__graft_entry__.build()) the calls raise; there is no fallback path.
+
+Byte conventions: FP8 codes and E8M0 scales are returned as torch.uint8 tensors
+(view them as torch.float8_e4m3fn / float8_e5m2 / float8_e8m0fnu if wanted);
+inputs may be uint8 or the matching float8 dtype.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .build import lib_path
+
+__all__ = [
+    "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "FP8_E5M2", "FP8_E4M3",
+    "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "token_permute",
+    "mega_moe", "mega_moe_workspace_bytes", "gmm1_swiglu_quant", "gmm2_combine", "combine_finalize",
+]
+
+QUANT_NONE, QUANT_E5M2, QUANT_E4M3 = -1, 2, 3
+FP8_E5M2, FP8_E4M3 = 23, 24
+_DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int32: 3, torch.int64: 4}
+_STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP"}
+
+
+class MoeError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_STATUS.get(status, status)}: {message}")
+        self.status = status
+
+
+class MegaArgs(ctypes.Structure):
+    _fields_ = [
+        ("x", ctypes.c_void_p), ("num_tokens", ctypes.c_int64), ("hidden", ctypes.c_int64),
+        ("topk_ids", ctypes.c_void_p), ("topk", ctypes.c_int64),
+        ("topk_weights", ctypes.c_void_p), ("topk_weights_dtype", ctypes.c_int),
+        ("num_experts", ctypes.c_int64), ("inter", ctypes.c_int64),
+        ("w1", ctypes.c_void_p), ("w1_scales", ctypes.c_void_p),
+        ("w2", ctypes.c_void_p), ("w2_scales", ctypes.c_void_p),
+        ("num_shared", ctypes.c_int64),
+        ("shared_w1", ctypes.c_void_p), ("shared_w1_scales", ctypes.c_void_p),
+        ("shared_w2", ctypes.c_void_p), ("shared_w2_scales", ctypes.c_void_p),
+        ("quant_out_dtype", ctypes.c_int), ("activation", ctypes.c_int),
+        ("y", ctypes.c_void_p), ("expert_token_nums", ctypes.c_void_p),
+        ("xq", ctypes.c_void_p), ("sx", ctypes.c_void_p), ("h1", ctypes.c_void_p),
+        ("aq", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("o", ctypes.c_void_p),
+        ("sorted_row_idx", ctypes.c_void_p),
+        ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+    ]
+
+MEGA_STAGE_EVENTS = 8
+MEGA_STAGES = ["routing", "permute_quant", "gmm1_swiglu_quant", "zero_accum", "gmm2_combine", "shared_experts",
+               "finalize"]
+
+
+_lib = None
+
+_I64, _INT, _VP, _SZ = ctypes.c_int64, ctypes.c_int, ctypes.c_void_p, ctypes.c_size_t
+_SIGS = {
+    "moe_last_error": ([], ctypes.c_char_p),
+    "moe_version": ([], _INT),
+    "moe_mx_scale_cols": ([_I64], _I64),
+    "moe_token_permute_out_rows": ([_I64, _I64], _I64),
+    "moe_mx_quantize": ([_VP, _INT, _I64, _I64, _INT, _VP, _VP, _VP], _INT),
+    "moe_init_routing_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "moe_init_routing": ([_VP, _INT, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
+                          _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
+    "moe_token_permute_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "moe_token_permute": ([_VP, _INT, _I64, _I64, _VP, _INT, _I64, _I64, _I64, _INT, _INT,
+                           _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
+    "mega_moe_workspace_size": ([ctypes.POINTER(MegaArgs), ctypes.POINTER(_SZ)], _INT),
+    "mega_moe": ([ctypes.POINTER(MegaArgs), _VP, _SZ, _VP], _INT),
+    "moe_gmm_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "moe_gmm1_swiglu_quant": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _VP, _VP, _VP,
+                               _VP, _SZ, _VP], _INT),
+    "moe_gmm2_combine": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _VP, _VP, _I64, _VP,
+                          _VP, _VP, _SZ, _VP], _INT),
+    "moe_combine_finalize": ([_VP, _I64, _I64, _VP, _VP], _INT),
+}
+
+
+def load(path: str | None = None) -> ctypes.CDLL:
+    """Load libmoe_mx.so (built in-tree); raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = path or lib_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run routing_permute_mxfp8_amd/build.py "
+                           "(the HIP library is required; there is no fallback)")
+    lib = ctypes.CDLL(path)
+    for name, (args, res) in _SIGS.items():
+        fn = getattr(lib, name)
+        fn.argtypes = args
+        fn.restype = res
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise MoeError(status, _lib.moe_last_error().decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _u8(t):
+    if t is None:
+        return None
+    return t if t.dtype == torch.uint8 else t.view(torch.uint8)
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _workspace(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def _need_gpu(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("tensors must be on the GPU")
+        if t is not None and not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def mx_scale_cols(cols: int) -> int:
+    return int(load().moe_mx_scale_cols(cols))
+
+
+def token_permute_out_rows(flat: int, num_out_tokens) -> int:
+    return int(load().moe_token_permute_out_rows(flat, 0 if num_out_tokens is None else int(num_out_tokens)))
+
+
+def mx_quantize(x: torch.Tensor, quant_mode: int = QUANT_E4M3):
+    """MX-quantize the rows of a 2-D bf16/fp16/fp32 tensor: (codes uint8 [R, C], scales uint8 [R, AlignUp(C/32, 2)])."""
+    lib = load()
+    _need_gpu(x)
+    rows, cols = x.shape
+    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    scales = torch.empty((rows, mx_scale_cols(cols)), dtype=torch.uint8, device=x.device)
+    _check(lib.moe_mx_quantize(_ptr(x), _DT[x.dtype], rows, cols, quant_mode, _ptr(codes), _ptr(scales),
+                               _stream(x.device)))
+    return codes, scales
+
+
+def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: int = QUANT_NONE,
+                 row_idx_type: int = 1, expert_tokens_num_type: int = 1):
+    """MoeInitRoutingV3 (dropless). Returns (expanded_x, expanded_row_idx, expert_tokens,
+    expanded_scale or None, available_idx_num) with expanded_x of shape [N*K, H]."""
+    lib = load()
+    _need_gpu(x, expert_idx)
+    n, h = x.shape
+    k = expert_idx.shape[1]
+    s, e = (0, expert_num) if active_range is None else active_range
+    flat = n * k
+    mx = quant_mode != QUANT_NONE
+    dev = x.device
+    ex = torch.empty((flat, h), dtype=torch.uint8 if mx else x.dtype, device=dev)
+    idx = torch.empty((flat,), dtype=torch.int32, device=dev)
+    tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
+    sc = torch.empty((flat, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx else None
+    avail = torch.empty((1,), dtype=torch.int64, device=dev)
+    nbytes = ctypes.c_size_t()
+    _check(lib.moe_init_routing_workspace_size(n, k, expert_num, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.moe_init_routing(_ptr(x), _DT[x.dtype], n, h, _ptr(expert_idx), k, expert_num, s, e, quant_mode,
+                                row_idx_type, expert_tokens_num_type, _ptr(ex), _ptr(idx), _ptr(tok), _ptr(sc),
+                                _ptr(avail), _ptr(ws), ws.numel(), _stream(dev)))
+    return ex, idx, tok, sc, avail
+
+
+def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = False, quant_mode: int = QUANT_NONE,
+                  *, num_experts: int):
+    """moe_token_permute: (permuted_tokens [M, H], sorted_indices int32 [F], expanded_scale or empty).
+
+    num_experts is the exclusive bound of the index values (the counting sort's bucket count)."""
+    lib = load()
+    _need_gpu(tokens, indices)
+    n, h = tokens.shape
+    topk = 1 if indices.dim() == 1 else indices.shape[1]
+    flat = indices.numel()
+    m = token_permute_out_rows(flat, num_out_tokens)
+    mx = quant_mode != QUANT_NONE
+    dev = tokens.device
+    out = torch.empty((m, h), dtype=torch.uint8 if mx else tokens.dtype, device=dev)
+    srt = torch.empty((flat,), dtype=torch.int32, device=dev)
+    sc = (torch.empty((m, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx
+          else torch.empty((0,), dtype=torch.float32, device=dev))
+    nbytes = ctypes.c_size_t()
+    _check(lib.moe_token_permute_workspace_size(flat, num_experts, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.moe_token_permute(_ptr(tokens), _DT[tokens.dtype], n, h, _ptr(indices), _DT[indices.dtype], topk,
+                                 num_experts, 0 if num_out_tokens is None else int(num_out_tokens),
+                                 int(bool(padded_mode)), quant_mode, _ptr(out), _ptr(srt),
+                                 _ptr(sc) if mx else None, _ptr(ws), ws.numel(), _stream(dev)))
+    return out, srt, sc
+
+
+def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
+                 debug):
+    n, h = x.shape
+    k = topk_ids.shape[1]
+    e, two_i, _ = w1.shape
+    a = MegaArgs()
+    a.x, a.num_tokens, a.hidden = _ptr(x), n, h
+    a.topk_ids, a.topk = _ptr(topk_ids), k
+    a.topk_weights, a.topk_weights_dtype = _ptr(topk_weights), _DT[topk_weights.dtype]
+    a.num_experts, a.inter = e, two_i // 2
+    a.w1, a.w1_scales, a.w2, a.w2_scales = _ptr(_u8(w1)), _ptr(_u8(w1_scales)), _ptr(_u8(w2)), _ptr(_u8(w2_scales))
+    if shared is not None:
+        sw1, ss1, sw2, ss2 = shared
+        a.num_shared = sw1.shape[0]
+        a.shared_w1, a.shared_w1_scales = _ptr(_u8(sw1)), _ptr(_u8(ss1))
+        a.shared_w2, a.shared_w2_scales = _ptr(_u8(sw2)), _ptr(_u8(ss2))
+    a.quant_out_dtype, a.activation = quant_out_dtype, 0
+    a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
+    for name in ("xq", "sx", "h1", "aq", "sa", "o", "sorted_row_idx"):
+        setattr(a, name, _ptr(debug.get(name)) if debug else None)
+    return a
+
+
+def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
+             quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None):
+    """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
+    debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
+
+    shared: None or (shared_w1, shared_w1_scales, shared_w2, shared_w2_scales) stacked
+    over the shared experts. workspace: optional preallocated uint8 device tensor.
+    stage_events: optional list of MEGA_STAGE_EVENTS torch.cuda.Event(enable_timing=True),
+    recorded by the library on the stream at the boundaries of MEGA_STAGES."""
+    lib = load()
+    _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
+    n, h = x.shape
+    k = topk_ids.shape[1]
+    e, two_i, _ = w1.shape
+    inter = two_i // 2
+    dev = x.device
+    y = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
+    etn = torch.empty((e,), dtype=torch.int32, device=dev)
+    dbg = None
+    if debug:
+        f = n * k
+        dbg = dict(xq=torch.empty((f, h), dtype=torch.uint8, device=dev),
+                   sx=torch.empty((f, h // 32), dtype=torch.uint8, device=dev),
+                   h1=torch.empty((f, 2 * inter), dtype=torch.float32, device=dev),
+                   aq=torch.empty((f, inter), dtype=torch.uint8, device=dev),
+                   sa=torch.empty((f, inter // 32), dtype=torch.uint8, device=dev),
+                   o=torch.empty((f, h), dtype=torch.float32, device=dev),
+                   sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
+    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg)
+    if stage_events is not None:
+        if len(stage_events) != MEGA_STAGE_EVENTS:
+            raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} events")
+        for ev in stage_events:
+            ev.record()   # make sure the underlying HIP event exists before the library records it
+        handles = (ctypes.c_void_p * MEGA_STAGE_EVENTS)(*[ev.cuda_event for ev in stage_events])
+        a.stage_events = ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p))
+    nbytes = ctypes.c_size_t()
+    _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    ws = workspace if workspace is not None and workspace.numel() >= nbytes.value else _workspace(nbytes.value, dev)
+    _check(lib.mega_moe(ctypes.byref(a), _ptr(ws), ws.numel(), _stream(dev)))
+    if debug:
+        return y, etn, dbg
+    return y, etn
+
+
+def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
+                             quant_out_dtype: int = FP8_E4M3) -> int:
+    lib = load()
+    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None)
+    nbytes = ctypes.c_size_t()
+    _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
+    return nbytes.value
+
+
+def gmm1_swiglu_quant(xq, sx, group_offsets, w1, w1_scales, quant_out_dtype: int = FP8_E4M3, want_h1: bool = False):
+    """Stage 2 on given operands: (aq uint8 [rows, I], sa uint8 [rows, I/32], h1 fp32 [rows, 2I] or None)."""
+    lib = load()
+    xq, sx, w1, w1_scales = _u8(xq), _u8(sx), _u8(w1), _u8(w1_scales)
+    _need_gpu(xq, sx, group_offsets, w1, w1_scales)
+    rows, h = xq.shape
+    g, two_i, _ = w1.shape
+    inter = two_i // 2
+    dev = xq.device
+    aq = torch.empty((rows, inter), dtype=torch.uint8, device=dev)
+    sa = torch.empty((rows, inter // 32), dtype=torch.uint8, device=dev)
+    h1 = torch.empty((rows, two_i), dtype=torch.float32, device=dev) if want_h1 else None
+    nbytes = ctypes.c_size_t()
+    _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.moe_gmm1_swiglu_quant(_ptr(xq), _ptr(sx), rows, h, inter, _ptr(group_offsets), g, _ptr(w1),
+                                     _ptr(w1_scales), quant_out_dtype, _ptr(aq), _ptr(sa), _ptr(h1), _ptr(ws),
+                                     ws.numel(), _stream(dev)))
+    return aq, sa, h1
+
+
+def gmm2_combine(aq, sa, group_offsets, w2, w2_scales, row_token, row_weight, y_accum,
+                 quant_out_dtype: int = FP8_E4M3, want_o: bool = False):
+    """Stages 3-4 on given operands: y_accum[row_token[r]] += row_weight[r] * O[r]; returns O (fp32) or None."""
+    lib = load()
+    aq, sa, w2, w2_scales = _u8(aq), _u8(sa), _u8(w2), _u8(w2_scales)
+    _need_gpu(aq, sa, group_offsets, w2, w2_scales, row_token, row_weight, y_accum)
+    rows, inter = aq.shape
+    g, h, _ = w2.shape
+    dev = aq.device
+    o = torch.empty((rows, h), dtype=torch.float32, device=dev) if want_o else None
+    nbytes = ctypes.c_size_t()
+    _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.moe_gmm2_combine(_ptr(aq), _ptr(sa), rows, inter, h, _ptr(group_offsets), g, _ptr(w2),
+                                _ptr(w2_scales), quant_out_dtype, _ptr(row_token), _ptr(row_weight),
+                                y_accum.shape[0], _ptr(y_accum), _ptr(o), _ptr(ws), ws.numel(), _stream(dev)))
+    return o
+
+
+def combine_finalize(y_accum):
+    """bf16 (round to nearest even) of an fp32 accumulation buffer."""
+    lib = load()
+    _need_gpu(y_accum)
+    n, h = y_accum.shape
+    y = torch.empty((n, h), dtype=torch.bfloat16, device=y_accum.device)
+    _check(lib.moe_combine_finalize(_ptr(y_accum), n, h, _ptr(y), _stream(y_accum.device)))
+    return y

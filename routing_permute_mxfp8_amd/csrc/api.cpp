@@ -1,0 +1,563 @@
+// C ABI of the MoE-layer hot path (include/moe_mx.h): host-side validation,
+// workspace carving and the launch sequence of each entry point. Every check
+// runs before the first launch; on an error nothing is enqueued. Error policy
+// follows the MegaMoE README (Constraints: errors are raised before the kernel
+// runs and report the bytes needed, without silent truncation or fallback).
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdarg>
+#include <cstdio>
+#include <string>
+
+#include "../../include/moe_mx.h"
+#include "internal.h"
+
+namespace {
+
+thread_local std::string g_error;
+
+moe_status fail(moe_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return st;
+}
+
+moe_status ok() {
+  g_error.clear();
+  return MOE_OK;
+}
+
+moe_status hip_fail(hipError_t e, const char* what) {
+  return fail(MOE_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// Bump allocator over the caller's workspace; with base == nullptr it only measures.
+struct Carver {
+  uint8_t* base;
+  size_t off = 0;
+  explicit Carver(void* b) : base(static_cast<uint8_t*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    off = (off + 255) & ~size_t(255);
+    T* p = base ? reinterpret_cast<T*>(base + off) : nullptr;
+    off += std::max<size_t>(count, 1) * sizeof(T);
+    return p;
+  }
+};
+
+int64_t scale_cols(int64_t cols) {
+  const int64_t g = (cols + 31) / 32;
+  return g + (g & 1);
+}
+
+// Chunking of the routing passes: chunk of 256 rows (<= 64Ki rows) or 1024, grown
+// until the per-chunk histogram table stays within 2Mi entries.
+void route_chunks(int64_t flat, int active, int* nch, int* chunk) {
+  int64_t c = flat <= 65536 ? 256 : 1024;
+  int64_t n = std::max<int64_t>(1, (flat + c - 1) / c);
+  while (n * std::max(active, 1) > (int64_t(1) << 21)) {
+    c *= 2;
+    n = std::max<int64_t>(1, (flat + c - 1) / c);
+  }
+  *nch = (int)n;
+  *chunk = (int)c;
+}
+
+struct RouteWs {
+  int* hist;
+  int* base;
+  int* offsets;
+};
+
+RouteWs carve_route(Carver& cv, int64_t flat, int active, int* nch, int* chunk) {
+  route_chunks(flat, active, nch, chunk);
+  RouteWs w;
+  w.hist = cv.take<int>((size_t)*nch * std::max(active, 1));
+  w.base = cv.take<int>((size_t)*nch * std::max(active, 1));
+  w.offsets = cv.take<int>((size_t)active + 1);
+  return w;
+}
+
+int quant_fmt(int quant_mode) { return quant_mode == MOE_QUANT_MXFP8_E4M3 ? 0 : 1; }
+
+bool valid_x_dtype(int d) { return d == MOE_DTYPE_FP32 || d == MOE_DTYPE_FP16 || d == MOE_DTYPE_BF16; }
+
+int token_tile_tt(int64_t rows, int64_t groups) {
+  const double avg = groups > 0 ? (double)rows / (double)groups : (double)rows;
+  if (avg <= 20.0) return 1;
+  if (avg <= 40.0) return 2;
+  return 4;
+}
+
+// ---- moe_init_routing ------------------------------------------------------------
+struct InitRoutingWs {
+  RouteWs r;
+  int32_t* scat;  // scatter index when the user asked for the gather type
+  int nch, chunk;
+};
+
+InitRoutingWs carve_init_routing(Carver& cv, int64_t flat, int active, bool need_scat) {
+  InitRoutingWs w;
+  w.r = carve_route(cv, flat, active, &w.nch, &w.chunk);
+  w.scat = need_scat ? cv.take<int32_t>((size_t)flat) : nullptr;
+  return w;
+}
+
+// ---- mega_moe --------------------------------------------------------------------
+struct MegaWs {
+  RouteWs r;
+  int nch, chunk;
+  int32_t* scat;
+  int32_t* gath;
+  int32_t* row_token;
+  float* row_weight;
+  int4* tiles;
+  int* tile_count;
+  int max_tiles, tt;
+  int4* sh_tiles;
+  int* sh_count;
+  int sh_max_tiles, sh_tt;
+  uint8_t* xq;
+  uint8_t* sx;
+  uint8_t* xq_tok;
+  uint8_t* sx_tok;
+  uint8_t* aq;
+  uint8_t* sa;
+  uint8_t* aq_sh;
+  uint8_t* sa_sh;
+  float* y_acc;
+};
+
+MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
+  MegaWs w{};
+  const int64_t n = a->num_tokens, h = a->hidden, i = a->inter, e = a->num_experts;
+  const int64_t flat = n * a->topk;
+  w.r = carve_route(cv, flat, (int)e, &w.nch, &w.chunk);
+  w.scat = cv.take<int32_t>(flat);
+  w.gath = a->sorted_row_idx ? nullptr : cv.take<int32_t>(flat);
+  w.row_token = cv.take<int32_t>(flat);
+  w.row_weight = cv.take<float>(flat);
+  w.tt = token_tile_tt(flat, e);
+  w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
+  w.tiles = cv.take<int4>(w.max_tiles);
+  w.tile_count = cv.take<int>(1);
+  w.xq = a->xq ? nullptr : cv.take<uint8_t>((size_t)flat * h);
+  w.sx = a->sx ? nullptr : cv.take<uint8_t>((size_t)flat * (h / 32));
+  w.aq = a->aq ? nullptr : cv.take<uint8_t>((size_t)flat * i);
+  w.sa = a->sa ? nullptr : cv.take<uint8_t>((size_t)flat * (i / 32));
+  if (a->num_shared > 0) {
+    w.sh_tt = n <= 16 ? 1 : (n <= 32 ? 2 : 4);
+    w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
+    w.sh_tiles = cv.take<int4>(w.sh_max_tiles);
+    w.sh_count = cv.take<int>(1);
+    w.xq_tok = cv.take<uint8_t>((size_t)n * h);
+    w.sx_tok = cv.take<uint8_t>((size_t)n * (h / 32));
+    w.aq_sh = cv.take<uint8_t>((size_t)n * i);
+    w.sa_sh = cv.take<uint8_t>((size_t)n * (i / 32));
+  }
+  w.y_acc = cv.take<float>((size_t)n * h);
+  return w;
+}
+
+moe_status check_mega(const moe_mega_args* a) {
+  if (!a) return fail(MOE_ERR_INVALID_ARG, "mega_moe: args is NULL");
+  if (a->num_tokens < 0) return fail(MOE_ERR_SHAPE, "mega_moe: num_tokens %lld < 0", (long long)a->num_tokens);
+  if (a->hidden < 128 || a->hidden % 128 != 0 || a->hidden > 65536)
+    return fail(MOE_ERR_SHAPE, "mega_moe: hidden %lld must be a positive multiple of 128 (<= 65536)",
+                (long long)a->hidden);
+  if (a->inter < 128 || a->inter % 128 != 0 || a->inter > 65536)
+    return fail(MOE_ERR_SHAPE, "mega_moe: inter %lld must be a positive multiple of 128 (<= 65536)",
+                (long long)a->inter);
+  if (a->topk < 1 || a->topk > 32) return fail(MOE_ERR_SHAPE, "mega_moe: topk %lld outside [1, 32]", (long long)a->topk);
+  if (a->num_experts < 1 || a->num_experts > 1024)
+    return fail(MOE_ERR_SHAPE, "mega_moe: num_experts %lld outside [1, 1024]", (long long)a->num_experts);
+  if (a->topk > a->num_experts)
+    return fail(MOE_ERR_SHAPE, "mega_moe: topk %lld > num_experts %lld (ids per token must be distinct)",
+                (long long)a->topk, (long long)a->num_experts);
+  if (a->num_tokens * a->topk >= MOE_MAX_FLAT_ROWS)
+    return fail(MOE_ERR_SHAPE, "mega_moe: num_tokens*topk must be < %d", MOE_MAX_FLAT_ROWS);
+  if (a->num_shared < 0 || a->num_shared > 4)
+    return fail(MOE_ERR_SHAPE, "mega_moe: num_shared %lld outside [0, 4]", (long long)a->num_shared);
+  if (a->quant_out_dtype != MOE_FP8_E5M2 && a->quant_out_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_DTYPE, "mega_moe: quant_out_dtype %d must be 23 (FLOAT8_E5M2) or 24 (FLOAT8_E4M3FN)",
+                a->quant_out_dtype);
+  if (a->activation != MOE_ACT_SWIGLU)
+    return fail(MOE_ERR_UNSUPPORTED, "mega_moe: activation %d not supported (only swiglu)", a->activation);
+  if (a->topk_weights_dtype != MOE_DTYPE_FP32 && a->topk_weights_dtype != MOE_DTYPE_BF16)
+    return fail(MOE_ERR_DTYPE, "mega_moe: topk_weights_dtype must be FP32 or BF16");
+  if (a->num_tokens > 0 && (!a->x || !a->topk_ids || !a->topk_weights || !a->y))
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: x, topk_ids, topk_weights and y must be non-NULL");
+  if (!a->w1 || !a->w1_scales || !a->w2 || !a->w2_scales)
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: w1, w1_scales, w2, w2_scales must be non-NULL");
+  if (a->num_shared > 0 && (!a->shared_w1 || !a->shared_w1_scales || !a->shared_w2 || !a->shared_w2_scales))
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: num_shared > 0 needs all four shared weight pointers");
+  return MOE_OK;
+}
+
+moe_status check_gmm_common(const char* who, int64_t rows, int64_t hidden, int64_t inter, int64_t groups,
+                            int quant_out_dtype) {
+  if (rows < 0) return fail(MOE_ERR_SHAPE, "%s: rows < 0", who);
+  if (hidden < 128 || hidden % 128 != 0 || hidden > 65536)
+    return fail(MOE_ERR_SHAPE, "%s: hidden %lld must be a positive multiple of 128", who, (long long)hidden);
+  if (inter < 128 || inter % 128 != 0 || inter > 65536)
+    return fail(MOE_ERR_SHAPE, "%s: inter %lld must be a positive multiple of 128", who, (long long)inter);
+  if (groups < 1 || groups > MOE_MAX_EXPERTS) return fail(MOE_ERR_SHAPE, "%s: num_groups outside [1, %d]", who, MOE_MAX_EXPERTS);
+  if (rows >= MOE_MAX_FLAT_ROWS) return fail(MOE_ERR_SHAPE, "%s: rows must be < %d", who, MOE_MAX_FLAT_ROWS);
+  if (quant_out_dtype != MOE_FP8_E5M2 && quant_out_dtype != MOE_FP8_E4M3)
+    return fail(MOE_ERR_DTYPE, "%s: quant_out_dtype must be 23 or 24", who);
+  return MOE_OK;
+}
+
+struct GmmWs {
+  int4* tiles;
+  int* count;
+  int max_tiles, tt;
+};
+
+GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups) {
+  GmmWs w;
+  w.tt = token_tile_tt(rows, groups);
+  w.max_tiles = (int)(rows / (16 * w.tt) + groups + 1);
+  w.tiles = cv.take<int4>(w.max_tiles);
+  w.count = cv.take<int>(1);
+  return w;
+}
+
+moe_status check_ws(const char* who, size_t need, void* ws, size_t have) {
+  if (have < need || (need > 0 && ws == nullptr))
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace of %zu bytes required, %zu given", who, need, ws ? have : 0);
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+    return fail(MOE_ERR_WORKSPACE, "%s: workspace must be 256-byte aligned", who);
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_last_error(void) { return g_error.c_str(); }
+
+int moe_version(void) { return 100; }
+
+int64_t moe_mx_scale_cols(int64_t cols) { return cols <= 0 ? 0 : scale_cols(cols); }
+
+int64_t moe_token_permute_out_rows(int64_t flat_rows, int64_t num_out_tokens) {
+  if (num_out_tokens == 0) return flat_rows;
+  if (num_out_tokens > 0) return std::min(num_out_tokens, flat_rows);
+  return std::max<int64_t>(flat_rows + num_out_tokens, 0);
+}
+
+moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int quant_mode, uint8_t* codes,
+                           uint8_t* scales, void* stream) {
+  if (rows < 0 || cols <= 0 || cols % 8 != 0)
+    return fail(MOE_ERR_SHAPE, "moe_mx_quantize: rows %lld >= 0 and cols %lld > 0 with cols %% 8 == 0 required",
+                (long long)rows, (long long)cols);
+  if (!valid_x_dtype(dtype)) return fail(MOE_ERR_DTYPE, "moe_mx_quantize: dtype %d not BF16/FP16/FP32", dtype);
+  if (quant_mode != MOE_QUANT_MXFP8_E4M3 && quant_mode != MOE_QUANT_MXFP8_E5M2)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_mx_quantize: quant_mode %d not 2 or 3", quant_mode);
+  if (rows == 0) return ok();
+  if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize: NULL buffer");
+  moe::PermuteParams p;
+  p.x = x; p.in_dtype = dtype; p.n = rows; p.hidden = cols; p.topk = 1; p.scat = nullptr; p.m_limit = rows;
+  p.quant = quant_fmt(quant_mode); p.out = codes; p.out_scales = scales; p.scale_cols = scale_cols(cols);
+  hipError_t e = moe::launch_permute(p, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_mx_quantize launch");
+  return ok();
+}
+
+moe_status moe_init_routing_workspace_size(int64_t num_rows, int64_t k, int64_t expert_num, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "moe_init_routing_workspace_size: bytes is NULL");
+  if (num_rows < 0 || k < 1 || expert_num < 1 || expert_num > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "moe_init_routing_workspace_size: bad sizes");
+  Carver cv(nullptr);
+  carve_init_routing(cv, num_rows * k, (int)expert_num, true);
+  *bytes = cv.off;
+  return ok();
+}
+
+moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_t hidden, const int32_t* expert_idx,
+                            int64_t k, int64_t expert_num, int64_t active_start, int64_t active_end, int quant_mode,
+                            int row_idx_type, int expert_tokens_num_type, void* expanded_x,
+                            int32_t* expanded_row_idx, int64_t* expert_tokens, uint8_t* expanded_scale,
+                            int64_t* available_idx_num, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "moe_init_routing";
+  if (num_rows < 0 || hidden < 1) return fail(MOE_ERR_SHAPE, "%s: num_rows >= 0 and hidden >= 1 required", who);
+  if (k < 1 || k > 64) return fail(MOE_ERR_SHAPE, "%s: k %lld outside [1, 64]", who, (long long)k);
+  if (expert_num < 1 || expert_num > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "%s: expert_num %lld outside [1, %d]", who, (long long)expert_num, MOE_MAX_EXPERTS);
+  if (active_start < 0 || active_start > active_end || active_end > expert_num)
+    return fail(MOE_ERR_SHAPE, "%s: active range [%lld, %lld) must satisfy 0 <= start <= end <= expert_num %lld", who,
+                (long long)active_start, (long long)active_end, (long long)expert_num);
+  const int64_t flat = num_rows * k;
+  if (flat >= MOE_MAX_FLAT_ROWS) return fail(MOE_ERR_SHAPE, "%s: num_rows*k must be < %d", who, MOE_MAX_FLAT_ROWS);
+  if (!valid_x_dtype(x_dtype)) return fail(MOE_ERR_DTYPE, "%s: x_dtype %d not FP32/FP16/BF16", who, x_dtype);
+  if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_MXFP8_E5M2 && quant_mode != MOE_QUANT_MXFP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3)", who, quant_mode);
+  const bool mx = quant_mode != MOE_QUANT_NONE;
+  if (mx && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: MX quantization needs hidden %% 32 == 0", who);
+  if (row_idx_type != MOE_ROW_IDX_GATHER && row_idx_type != MOE_ROW_IDX_SCATTER)
+    return fail(MOE_ERR_INVALID_ARG, "%s: row_idx_type %d not 0 or 1", who, row_idx_type);
+  if (expert_tokens_num_type == 2)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: expert_tokens_num_type 2 (key_value) not supported", who);
+  if (expert_tokens_num_type != MOE_TOKENS_CUMSUM && expert_tokens_num_type != MOE_TOKENS_COUNT)
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens_num_type %d not 0 or 1", who, expert_tokens_num_type);
+  if (flat > 0 && (!x || !expert_idx || !expanded_x || !expanded_row_idx))
+    return fail(MOE_ERR_INVALID_ARG, "%s: x, expert_idx, expanded_x, expanded_row_idx must be non-NULL", who);
+  if (!available_idx_num) return fail(MOE_ERR_INVALID_ARG, "%s: available_idx_num must be non-NULL", who);
+  if (active_end > active_start && !expert_tokens)
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens must be non-NULL", who);
+  if (mx && flat > 0 && !expanded_scale) return fail(MOE_ERR_INVALID_ARG, "%s: expanded_scale must be non-NULL in MX modes", who);
+  const int active = (int)(active_end - active_start);
+  const bool want_gather = row_idx_type == MOE_ROW_IDX_GATHER;
+  Carver cv(nullptr);
+  carve_init_routing(cv, flat, active, want_gather);
+  if (moe_status st = check_ws(who, cv.off, workspace, workspace_bytes)) return st;
+  Carver w(workspace);
+  InitRoutingWs ws = carve_init_routing(w, flat, active, want_gather);
+  hipStream_t st = (hipStream_t)stream;
+
+  moe::RouteParams rp;
+  rp.keys = expert_idx; rp.key_is64 = 0; rp.flat = flat; rp.topk = (int)k;
+  rp.s = (int)active_start; rp.e = (int)active_end; rp.nch = ws.nch; rp.chunk = ws.chunk;
+  rp.hist = ws.r.hist; rp.base = ws.r.base; rp.offsets = ws.r.offsets;
+  rp.avail64 = available_idx_num; rp.expert_tokens = expert_tokens; rp.tokens_type = expert_tokens_num_type;
+  if (want_gather) {
+    rp.scat = ws.scat; rp.gath = expanded_row_idx; rp.gath_fill = expanded_row_idx;
+  } else {
+    rp.scat = expanded_row_idx;
+  }
+  hipError_t e = moe::launch_routing(rp, st);
+  if (e != hipSuccess) return hip_fail(e, "moe_init_routing routing launch");
+  moe::PermuteParams pp;
+  pp.x = x; pp.in_dtype = x_dtype; pp.n = num_rows; pp.hidden = hidden; pp.topk = (int)k; pp.scat = rp.scat;
+  pp.m_limit = flat; pp.quant = mx ? quant_fmt(quant_mode) : -1; pp.out = expanded_x;
+  pp.out_scales = expanded_scale; pp.scale_cols = scale_cols(hidden);
+  e = moe::launch_permute(pp, st);
+  if (e != hipSuccess) return hip_fail(e, "moe_init_routing permute launch");
+  return ok();
+}
+
+moe_status moe_token_permute_workspace_size(int64_t flat_rows, int64_t num_experts, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "moe_token_permute_workspace_size: bytes is NULL");
+  if (flat_rows < 0 || num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "moe_token_permute_workspace_size: bad sizes");
+  Carver cv(nullptr);
+  int nch, chunk;
+  carve_route(cv, flat_rows, (int)num_experts, &nch, &chunk);
+  *bytes = cv.off;
+  return ok();
+}
+
+moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t hidden, const void* indices,
+                             int indices_dtype, int64_t topk, int64_t num_experts, int64_t num_out_tokens,
+                             int padded_mode, int quant_mode, void* permuted_tokens, int32_t* sorted_indices,
+                             uint8_t* expanded_scale, void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "moe_token_permute";
+  if (padded_mode != 0) return fail(MOE_ERR_UNSUPPORTED, "%s: padded_mode must be False", who);
+  if (n < 0 || hidden < 1) return fail(MOE_ERR_SHAPE, "%s: n >= 0 and hidden >= 1 required", who);
+  if (topk < 1 || topk > 64) return fail(MOE_ERR_SHAPE, "%s: topk %lld outside [1, 64]", who, (long long)topk);
+  if (num_experts < 1 || num_experts > MOE_MAX_EXPERTS)
+    return fail(MOE_ERR_SHAPE, "%s: num_experts %lld outside [1, %d]", who, (long long)num_experts, MOE_MAX_EXPERTS);
+  const int64_t flat = n * topk;
+  if (flat >= MOE_MAX_FLAT_ROWS) return fail(MOE_ERR_SHAPE, "%s: indices numel must be < %d", who, MOE_MAX_FLAT_ROWS);
+  if (indices_dtype != MOE_DTYPE_INT32 && indices_dtype != MOE_DTYPE_INT64)
+    return fail(MOE_ERR_DTYPE, "%s: indices dtype must be INT32 or INT64", who);
+  if (!valid_x_dtype(dtype)) return fail(MOE_ERR_DTYPE, "%s: tokens dtype %d not FP32/FP16/BF16", who, dtype);
+  if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_MXFP8_E5M2 && quant_mode != MOE_QUANT_MXFP8_E4M3)
+    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3)", who, quant_mode);
+  const bool mx = quant_mode != MOE_QUANT_NONE;
+  if (mx && dtype == MOE_DTYPE_FP32) return fail(MOE_ERR_DTYPE, "%s: MX quant modes take FP16/BF16 tokens", who);
+  if (mx && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: MX quantization needs hidden %% 32 == 0", who);
+  const int64_t m = moe_token_permute_out_rows(flat, num_out_tokens);
+  if (flat > 0 && (!tokens || !indices || !sorted_indices))
+    return fail(MOE_ERR_INVALID_ARG, "%s: tokens, indices, sorted_indices must be non-NULL", who);
+  if (m > 0 && (!permuted_tokens || (mx && !expanded_scale)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: permuted_tokens (and expanded_scale in MX modes) must be non-NULL", who);
+  Carver cv(nullptr);
+  int nch, chunk;
+  carve_route(cv, flat, (int)num_experts, &nch, &chunk);
+  if (moe_status st = check_ws(who, cv.off, workspace, workspace_bytes)) return st;
+  Carver w(workspace);
+  RouteWs rw = carve_route(w, flat, (int)num_experts, &nch, &chunk);
+  hipStream_t st = (hipStream_t)stream;
+  moe::RouteParams rp;
+  rp.keys = indices; rp.key_is64 = indices_dtype == MOE_DTYPE_INT64; rp.flat = flat; rp.topk = (int)topk;
+  rp.s = 0; rp.e = (int)num_experts; rp.nch = nch; rp.chunk = chunk;
+  rp.hist = rw.hist; rp.base = rw.base; rp.offsets = rw.offsets; rp.scat = sorted_indices;
+  hipError_t e = moe::launch_routing(rp, st);
+  if (e != hipSuccess) return hip_fail(e, "moe_token_permute routing launch");
+  moe::PermuteParams pp;
+  pp.x = tokens; pp.in_dtype = dtype; pp.n = n; pp.hidden = hidden; pp.topk = (int)topk; pp.scat = sorted_indices;
+  pp.m_limit = m; pp.quant = mx ? quant_fmt(quant_mode) : -1; pp.out = permuted_tokens;
+  pp.out_scales = expanded_scale; pp.scale_cols = scale_cols(hidden);
+  e = moe::launch_permute(pp, st);
+  if (e != hipSuccess) return hip_fail(e, "moe_token_permute permute launch");
+  return ok();
+}
+
+moe_status mega_moe_workspace_size(const moe_mega_args* args, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "mega_moe_workspace_size: bytes is NULL");
+  if (moe_status s = check_mega(args)) return s;
+  Carver cv(nullptr);
+  carve_mega(cv, args);
+  *bytes = cv.off;
+  return ok();
+}
+
+moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_bytes, void* stream) {
+  if (moe_status s = check_mega(a)) return s;
+  Carver cv(nullptr);
+  carve_mega(cv, a);
+  if (moe_status s = check_ws("mega_moe", cv.off, workspace, workspace_bytes)) return s;
+  Carver wc(workspace);
+  MegaWs w = carve_mega(wc, a);
+  hipStream_t st = (hipStream_t)stream;
+  auto mark = [&](int k) -> hipError_t {
+    return a->stage_events ? hipEventRecord((hipEvent_t)a->stage_events[k], st) : hipSuccess;
+  };
+  const int64_t n = a->num_tokens, h = a->hidden, inter = a->inter, ne = a->num_experts;
+  const int64_t flat = n * a->topk;
+  const int fmt = a->quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1;
+  uint8_t* xq = a->xq ? a->xq : w.xq;
+  uint8_t* sx = a->sx ? a->sx : w.sx;
+  uint8_t* aq = a->aq ? a->aq : w.aq;
+  uint8_t* sa = a->sa ? a->sa : w.sa;
+  int32_t* gath = a->sorted_row_idx ? a->sorted_row_idx : w.gath;
+
+  // stage 1a: routing (full expert range, scatter + gather forms, combine row maps)
+  moe::RouteParams rp;
+  rp.keys = a->topk_ids; rp.flat = flat; rp.topk = (int)a->topk; rp.s = 0; rp.e = (int)ne;
+  rp.nch = w.nch; rp.chunk = w.chunk; rp.hist = w.r.hist; rp.base = w.r.base; rp.offsets = w.r.offsets;
+  rp.token_nums32 = a->expert_token_nums; rp.scat = w.scat; rp.gath = gath;
+  rp.row_token = w.row_token; rp.row_weight = w.row_weight; rp.topk_w = a->topk_weights;
+  rp.topk_w_bf16 = a->topk_weights_dtype == MOE_DTYPE_BF16;
+  hipError_t e = mark(0);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe event record");
+  e = moe::launch_routing(rp, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe routing launch");
+  if (n == 0) return ok();
+  e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt, w.max_tiles, w.tiles, w.tile_count, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
+  if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // stage 1b: gather + MX quantization (plus the token-order copy for shared experts)
+  moe::PermuteParams pp;
+  pp.x = a->x; pp.in_dtype = MOE_DTYPE_BF16; pp.n = n; pp.hidden = h; pp.topk = (int)a->topk; pp.scat = w.scat;
+  pp.m_limit = flat; pp.quant = fmt; pp.out = xq; pp.out_scales = sx; pp.scale_cols = h / 32;
+  pp.tok_out = a->num_shared > 0 ? w.xq_tok : nullptr; pp.tok_scales = w.sx_tok;
+  e = moe::launch_permute(pp, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe permute launch");
+  if ((e = mark(2)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // stage 2: GMM1 + SwiGLU + MX requantization
+  moe::Gmm1Params g1{xq, sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
+                     (int)h, (int)inter, fmt, w.tt, aq, sa, a->h1};
+  e = moe::launch_gmm1(g1, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
+  if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // stages 3-4: GMM2 with the weighted combine into fp32 token rows
+  e = moe::launch_fill_zero(w.y_acc, n * h, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe zero-fill launch");
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  moe::Gmm2Params g2{aq, sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
+                     (int)h, (int)inter, fmt, w.tt, w.row_token, w.row_weight, w.y_acc, a->o};
+  e = moe::launch_gmm2(g2, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // shared experts: same FFN over all tokens in token order, added unweighted
+  if (a->num_shared > 0) {
+    e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
+    for (int64_t s = 0; s < a->num_shared; ++s) {
+      moe::Gmm1Params s1{w.xq_tok, w.sx_tok, a->shared_w1 + s * 2 * inter * h,
+                         a->shared_w1_scales + s * 2 * inter * (h / 32), w.sh_tiles, w.sh_count, w.sh_max_tiles,
+                         (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr};
+      e = moe::launch_gmm1(s1, st);
+      if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
+      moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter, a->shared_w2_scales + s * h * (inter / 32),
+                         w.sh_tiles, w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt,
+                         nullptr, nullptr, w.y_acc, nullptr};
+      e = moe::launch_gmm2(s2, st);
+      if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
+    }
+  }
+  if ((e = mark(6)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  e = moe::launch_finalize(w.y_acc, n * h, reinterpret_cast<uint16_t*>(a->y), st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe finalize launch");
+  if ((e = mark(7)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  return ok();
+}
+
+moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, size_t* bytes) {
+  if (!bytes) return fail(MOE_ERR_INVALID_ARG, "moe_gmm_workspace_size: bytes is NULL");
+  if (rows < 0 || num_groups < 1) return fail(MOE_ERR_SHAPE, "moe_gmm_workspace_size: bad sizes");
+  Carver cv(nullptr);
+  carve_gmm(cv, rows, num_groups);
+  *bytes = cv.off;
+  return ok();
+}
+
+moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t rows, int64_t hidden, int64_t inter,
+                                 const int32_t* group_offsets, int64_t num_groups, const uint8_t* w1,
+                                 const uint8_t* w1_scales, int quant_out_dtype, uint8_t* aq, uint8_t* sa, float* h1,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  const char* who = "moe_gmm1_swiglu_quant";
+  if (moe_status s = check_gmm_common(who, rows, hidden, inter, num_groups, quant_out_dtype)) return s;
+  if (!group_offsets || !w1 || !w1_scales || (rows > 0 && (!xq || !sx || !aq || !sa)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
+  Carver cv(nullptr);
+  carve_gmm(cv, rows, num_groups);
+  if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
+  if (rows == 0) return ok();
+  Carver wc(workspace);
+  GmmWs w = carve_gmm(wc, rows, num_groups);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
+  if (e != hipSuccess) return hip_fail(e, "tile list launch");
+  moe::Gmm1Params g{xq, sx, w1, w1_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, aq, sa, h1};
+  e = moe::launch_gmm1(g, st);
+  if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  return ok();
+}
+
+moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, int64_t inter, int64_t hidden,
+                            const int32_t* group_offsets, int64_t num_groups, const uint8_t* w2,
+                            const uint8_t* w2_scales, int quant_out_dtype, const int32_t* row_token,
+                            const float* row_weight, int64_t num_tokens, float* y_accum, float* o, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  const char* who = "moe_gmm2_combine";
+  if (moe_status s = check_gmm_common(who, rows, hidden, inter, num_groups, quant_out_dtype)) return s;
+  if (num_tokens < 1) return fail(MOE_ERR_SHAPE, "%s: num_tokens must be >= 1", who);
+  if (!group_offsets || !w2 || !w2_scales || (rows > 0 && (!aq || !sa || !row_token || !row_weight || !y_accum)))
+    return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
+  Carver cv(nullptr);
+  carve_gmm(cv, rows, num_groups);
+  if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
+  if (rows == 0) return ok();
+  Carver wc(workspace);
+  GmmWs w = carve_gmm(wc, rows, num_groups);
+  hipStream_t st = (hipStream_t)stream;
+  hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
+  if (e != hipSuccess) return hip_fail(e, "tile list launch");
+  moe::Gmm2Params g{aq, sa, w2, w2_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, row_token, row_weight, y_accum, o};
+  e = moe::launch_gmm2(g, st);
+  if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+  return ok();
+}
+
+moe_status moe_combine_finalize(const float* y_accum, int64_t num_tokens, int64_t hidden, void* y, void* stream) {
+  if (num_tokens < 0 || hidden < 1) return fail(MOE_ERR_SHAPE, "moe_combine_finalize: bad sizes");
+  if (num_tokens == 0) return ok();
+  if (!y_accum || !y) return fail(MOE_ERR_INVALID_ARG, "moe_combine_finalize: NULL buffer");
+  hipError_t e = moe::launch_finalize(y_accum, num_tokens * hidden, reinterpret_cast<uint16_t*>(y), (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "finalize launch");
+  return ok();
+}
+
+}  // extern "C"

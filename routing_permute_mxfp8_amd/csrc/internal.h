@@ -1,0 +1,90 @@
+// Launchers shared between the C-ABI layer (api.cpp) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// ---- routing (routing.hip) ----------------------------------------------------
+// Stable counting sort of F flat keys (expert ids) restricted to [s, e), split in
+// `nch` chunks of `chunk` keys (chunk % 64 == 0). Positions are relative to the
+// start of the active segment.
+struct RouteParams {
+  const void* keys = nullptr;   // int32 or int64 [flat]
+  int key_is64 = 0;
+  int64_t flat = 0;
+  int topk = 1;
+  int s = 0, e = 0;             // active experts [s, e); A = e - s buckets
+  int nch = 1, chunk = 64;
+  // workspace
+  int* hist = nullptr;          // [nch * A], chunk-major
+  int* base = nullptr;          // [nch * A], chunk-major: first position of (chunk, expert)
+  int* offsets = nullptr;       // [A + 1] exclusive prefix of the active counts
+  // outputs (nullable unless stated)
+  int64_t* avail64 = nullptr;   // availableIdxNum
+  int64_t* expert_tokens = nullptr;
+  int tokens_type = 1;          // 1 count, 0 inclusive cumsum
+  int32_t* token_nums32 = nullptr;
+  int32_t* scat = nullptr;      // [flat] position of each flat row, -1 outside [s, e) (required)
+  int32_t* gath = nullptr;      // [avail] flat row at each position
+  int32_t* gath_fill = nullptr; // if set (== gath), positions [avail, flat) are written -1
+  int32_t* row_token = nullptr; // [avail] flat row / topk at each position
+  float* row_weight = nullptr;  // [avail] gate weight at each position
+  const void* topk_w = nullptr; // fp32 or bf16 [flat]
+  int topk_w_bf16 = 0;
+};
+hipError_t launch_routing(const RouteParams& p, hipStream_t stream);
+
+// Token tiles of height `tm` over groups given by int32 offsets [groups + 1]
+// (clamped into [0, rows], non-decreasing): tiles[j] = {group, row0, nrows, 0},
+// *count = number of tiles (at most max_tiles are written).
+hipError_t launch_build_tiles(const int* offsets, int groups, int rows, int tm, int max_tiles, int4* tiles,
+                              int* count, hipStream_t stream);
+
+// ---- permute + MX quantization (permute_quant.hip) ------------------------------
+struct PermuteParams {
+  const void* x = nullptr;      // [n, hidden] of in_dtype
+  int in_dtype = 2;             // MOE_DTYPE_* (0 fp32, 1 fp16, 2 bf16)
+  int64_t n = 0, hidden = 0;
+  int topk = 1;
+  const int32_t* scat = nullptr;  // [n * topk] destination rows (-1 = none); nullptr = identity
+  int64_t m_limit = 0;          // only destinations < m_limit are written
+  int quant = -1;               // -1 copy, 0 E4M3FN, 1 E5M2
+  void* out = nullptr;          // [m_limit, hidden] codes or values
+  uint8_t* out_scales = nullptr;  // [m_limit, scale_cols]
+  int64_t scale_cols = 0;
+  uint8_t* tok_out = nullptr;   // optional token-order copy [n, hidden] (MX modes only)
+  uint8_t* tok_scales = nullptr;
+};
+hipError_t launch_permute(const PermuteParams& p, hipStream_t stream);
+
+// ---- grouped GEMMs (gmm.hip) -------------------------------------------------------
+struct Gmm1Params {
+  const uint8_t* xq; const uint8_t* sx;        // [rows, H], [rows, H/32]
+  const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
+  const int4* tiles; const int* tile_count; int max_tiles;
+  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per wave
+  uint8_t* aq; uint8_t* sa;                    // [rows, I], [rows, I/32]
+  float* h1;                                   // nullable [rows, 2I]
+};
+hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
+
+struct Gmm2Params {
+  const uint8_t* aq; const uint8_t* sa;        // [rows, I], [rows, I/32]
+  const uint8_t* w; const uint8_t* ws;         // [G, H, I], [G, H, I/32]
+  const int4* tiles; const int* tile_count; int max_tiles;
+  int hidden, inter, fmt, tt;
+  const int32_t* row_token;                    // nullptr: token = row, weight 1
+  const float* row_weight;
+  float* y_accum;                              // [tokens, H]
+  float* o;                                    // nullable [rows, H]
+};
+hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
+
+// Tiles of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), 0}.
+hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);
+hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t stream);
+hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t stream);
+
+}  // namespace moe

@@ -1,0 +1,225 @@
+// Routing on gfx950: stable counting sort of the flattened expert ids.
+//
+// MoeInitRoutingV3 README, 计算公式 1-3 and 6: keyValueSort(expertIdx, rowIdx), the
+// inverse scatter expandedRowIdx[sortedRowIdx[i]] = i, the per-expert histogram, and
+// availableIdxNum = number of ids inside the active expert range. moe_token_permute
+// article, 功能说明 / 确定性计算: the sort is stable, so ties keep ascending flat row.
+//
+// Expert ids are small integers (E <= 10240), so the sort is a three-pass counting
+// sort instead of a comparison sort:
+//   1. route_count   one workgroup per chunk of flat rows, LDS histogram over the
+//                    active experts, written chunk-major;
+//   2. route_scan    one workgroup, exclusive scan in expert-major, chunk-minor order:
+//                    base[c][a] = rows of experts < a + rows of expert a in chunks < c,
+//                    i.e. the first sorted position of (chunk c, expert a); also the
+//                    per-expert counts / cumsum and availableIdxNum;
+//   3. route_scatter one wave per chunk walks its rows in order, 64 at a time. The rank
+//                    of a row among the earlier lanes with the same expert comes from a
+//                    bit-sliced match: one ballot per bit of the expert id, AND-ed per
+//                    lane (bit set ? ballot : ~ballot), then mbcnt below the lane. An LDS
+//                    cursor per expert carries the running position across steps.
+// Positions are relative to the start of the active segment [s, e).
+
+#include <climits>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+template <typename KeyT>
+__global__ __launch_bounds__(256) void route_count(const KeyT* __restrict__ keys, int64_t flat, int s,
+                                                   int A, int chunk, int* __restrict__ hist) {
+  extern __shared__ int lds_hist[];
+  const int c = blockIdx.x;
+  for (int a = threadIdx.x; a < A; a += blockDim.x) lds_hist[a] = 0;
+  __syncthreads();
+  const int64_t lo = (int64_t)c * chunk;
+  const int64_t hi = min(flat, lo + chunk);
+  for (int64_t r = lo + threadIdx.x; r < hi; r += blockDim.x) {
+    const int64_t a = (int64_t)keys[r] - s;
+    if (a >= 0 && a < A) atomicAdd(&lds_hist[a], 1);
+  }
+  __syncthreads();
+  for (int a = threadIdx.x; a < A; a += blockDim.x) hist[(int64_t)c * A + a] = lds_hist[a];
+}
+
+// Inclusive scan (sum, or max when MAX) of one int per thread over a 1024-thread block
+// (LDS, Hillis-Steele). Leaves the block total in part[1023].
+template <bool MAX = false>
+__device__ int block_inclusive_scan_1024(int v, int* part) {
+  const int t = threadIdx.x;
+  part[t] = v;
+  __syncthreads();
+  for (int d = 1; d < 1024; d <<= 1) {
+    const int other = t >= d ? part[t - d] : (MAX ? INT_MIN : 0);
+    __syncthreads();
+    part[t] = MAX ? max(part[t], other) : part[t] + other;
+    __syncthreads();
+  }
+  return part[t];
+}
+
+__global__ __launch_bounds__(1024) void route_scan(const int* __restrict__ hist, int nch, int A,
+                                                   int* __restrict__ base, int* __restrict__ offsets,
+                                                   int64_t* avail64, int64_t* expert_tokens,
+                                                   int tokens_type, int32_t* token_nums32) {
+  __shared__ int part[1024];
+  extern __shared__ int lds_off[];  // A + 1
+  const int t = threadIdx.x;
+  const int64_t L = (int64_t)A * nch;
+  const int64_t P = (L + 1023) / 1024;
+  const int64_t j0 = min(L, t * P), j1 = min(L, j0 + P);
+  int sum = 0;
+  for (int64_t j = j0; j < j1; ++j) {
+    const int64_t a = j / nch, c = j - a * nch;
+    sum += hist[c * A + a];
+  }
+  const int incl = block_inclusive_scan_1024(sum, part);
+  int run = incl - sum;
+  for (int64_t j = j0; j < j1; ++j) {
+    const int64_t a = j / nch, c = j - a * nch;
+    base[c * A + a] = run;
+    if (c == 0) lds_off[a] = run;
+    run += hist[c * A + a];
+  }
+  const int total = part[1023];
+  if (t == 0) lds_off[A] = total;
+  __syncthreads();
+  for (int a = t; a <= A; a += 1024) offsets[a] = lds_off[a];
+  if (t == 0 && avail64) *avail64 = total;
+  for (int a = t; a < A; a += 1024) {
+    const int cnt = lds_off[a + 1] - lds_off[a];
+    if (expert_tokens) expert_tokens[a] = tokens_type == 1 ? (int64_t)cnt : (int64_t)lds_off[a + 1];
+    if (token_nums32) token_nums32[a] = cnt;
+  }
+}
+
+template <typename KeyT>
+__global__ __launch_bounds__(64) void route_scatter(
+    const KeyT* __restrict__ keys, int64_t flat, int topk, int s, int A, int nbits, int chunk,
+    const int* __restrict__ base, const int* __restrict__ offsets, int32_t* __restrict__ scat,
+    int32_t* __restrict__ gath, int32_t* __restrict__ gath_fill, int32_t* __restrict__ row_token,
+    float* __restrict__ row_weight, const void* __restrict__ topk_w, int topk_w_bf16) {
+  extern __shared__ int cursor[];  // A
+  const int c = blockIdx.x;
+  const int lane = threadIdx.x;
+  for (int a = lane; a < A; a += 64) cursor[a] = base[(int64_t)c * A + a];
+  __syncthreads();
+  const int64_t lo = (int64_t)c * chunk;
+  const int64_t hi = min(flat, lo + chunk);
+  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
+    const int64_t r = r0 + lane;
+    const bool valid = r < hi;
+    int a = A;  // sentinel for rows outside the active range (and past the end)
+    if (valid) {
+      const int64_t d = (int64_t)keys[r] - s;
+      if (d >= 0 && d < A) a = (int)d;
+    }
+    const bool act = a < A;
+    uint64_t match = __ballot(act);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (a >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      match &= bit ? bal : ~bal;
+    }
+    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
+                                               __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
+    const int total = __popcll(match);
+    int pos = -1;
+    if (act) pos = cursor[a] + rank;
+    // Within one wave LDS accesses complete in program order: every lane has read its
+    // cursor before the last lane of each expert advances it.
+    if (act && rank == total - 1) cursor[a] = pos + 1;
+    if (valid) scat[r] = pos;
+    if (act) {
+      if (gath) gath[pos] = (int32_t)r;
+      if (row_token) row_token[pos] = (int32_t)(r / topk);
+      if (row_weight) {
+        float w;
+        if (topk_w_bf16) w = bf16_to_f(reinterpret_cast<const uint16_t*>(topk_w)[r]);
+        else w = reinterpret_cast<const float*>(topk_w)[r];
+        row_weight[pos] = w;
+      }
+    }
+  }
+  if (gath_fill) {
+    const int avail = offsets[A];
+    for (int64_t p = avail + (int64_t)c * 64 + lane; p < flat; p += (int64_t)gridDim.x * 64) gath_fill[p] = -1;
+  }
+}
+
+// Offsets are clamped into [0, rows] and made non-decreasing, and at most max_tiles
+// tiles are written, so caller-given offsets can never send a GEMM out of bounds.
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict__ offsets, int G, int rows, int tm,
+                                                           int max_tiles, int4* __restrict__ tiles,
+                                                           int* __restrict__ count) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int P = (G + 1023) / 1024;
+  const int g0 = min(G, t * P), g1 = min(G, g0 + P);
+  auto off = [&](int g) { return min(max(offsets[g], 0), rows); };
+  // start of this thread's first group: max of the clamped offsets [0, g0]
+  int local = 0;
+  for (int g = g0; g < g1; ++g) local = max(local, off(g));
+  const int incl_max = block_inclusive_scan_1024<true>(local, part);
+  const int before = t > 0 ? part[t - 1] : 0;
+  __syncthreads();
+  (void)incl_max;
+  const int start = g0 < g1 ? max(before, off(g0)) : 0;
+  int sum = 0;
+  int prev = start;
+  for (int g = g0; g < g1; ++g) {
+    const int nxt = max(prev, off(g + 1));
+    sum += (nxt - prev + tm - 1) / tm;
+    prev = nxt;
+  }
+  const int incl = block_inclusive_scan_1024(sum, part);
+  int run = incl - sum;
+  prev = start;
+  for (int g = g0; g < g1; ++g) {
+    const int nxt = max(prev, off(g + 1));
+    const int cnt = nxt - prev;
+    for (int i = 0; i * tm < cnt; ++i) {
+      if (run < max_tiles) tiles[run] = make_int4(g, prev + i * tm, min(tm, cnt - i * tm), 0);
+      ++run;
+    }
+    prev = nxt;
+  }
+  if (t == 1023) *count = min(part[1023], max_tiles);
+}
+
+}  // namespace
+
+hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
+  const int A = p.e - p.s;
+  const size_t lds_a = sizeof(int) * (size_t)(A > 0 ? A : 1);
+  if (A > 0) {
+    if (p.key_is64)
+      route_count<int64_t><<<p.nch, 256, lds_a, stream>>>((const int64_t*)p.keys, p.flat, p.s, A, p.chunk, p.hist);
+    else
+      route_count<int32_t><<<p.nch, 256, lds_a, stream>>>((const int32_t*)p.keys, p.flat, p.s, A, p.chunk, p.hist);
+  }
+  route_scan<<<1, 1024, sizeof(int) * (size_t)(A + 1), stream>>>(p.hist, p.nch, A, p.base, p.offsets, p.avail64,
+                                                                 p.expert_tokens, p.tokens_type, p.token_nums32);
+  int nbits = 0;
+  while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
+  if (p.key_is64)
+    route_scatter<int64_t><<<p.nch, 64, lds_a, stream>>>(
+        (const int64_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
+        p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
+  else
+    route_scatter<int32_t><<<p.nch, 64, lds_a, stream>>>(
+        (const int32_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
+        p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_build_tiles(const int* offsets, int groups, int rows, int tm, int max_tiles, int4* tiles,
+                              int* count, hipStream_t stream) {
+  build_tiles_kernel<<<1, 1024, 0, stream>>>(offsets, groups, rows, tm, max_tiles, tiles, count);
+  return hipGetLastError();
+}
+
+}  // namespace moe

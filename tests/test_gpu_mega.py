@@ -1,0 +1,195 @@
+"""mega_moe on the GPU against the oracle (MegaMoE A8W8-FP stages 1-4, all experts local).
+
+Small layers are compared whole: routing and stage-1 operands bit for bit, h1
+within 2e-3 normwise, the requantized activations code by code, Y within
+max|dY| <= 2e-2 max|Y| and sum|dY| <= 5e-3 sum|Y|. The full-size decode,
+prefill and skewed layers run in the benchmark's configuration (weights made on
+the GPU and quantized by the library) and are checked on sampled tokens: the
+oracle requantizes the sampled experts' masters itself (and the library's weight
+bytes must equal its), then computes those tokens one (token, k) at a time."""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs
+import routing_permute_mxfp8_amd as rp
+from oracle import moe, mxfp, routing
+from gpu_support import (DEV, FP8, abs_gmm, check_gemm_elementwise, check_requant, library_weights, normwise_err,
+                         oracle_expert_from_gpu_masters, oracle_experts_parallel, oracle_weights, say, swiglu_delta,
+                         to_dev, y_errors)
+
+pytestmark = pytest.mark.gpu
+
+SMALL = [
+    dict(name="tiny"),
+    dict(name="tiny", shared=1, seed=41),
+    dict(name="tiny", tokens=333, hidden=512, inter=256, experts=16, topk=4, shared=2, seed=42),
+    dict(name="skewed", tokens=500, hidden=384, inter=384, experts=20, topk=5, seed=43),
+    dict(name="tiny", tokens=5, hidden=256, inter=128, experts=32, topk=8, seed=44),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['name']}-{c.get('tokens', '')}-{c.get('shared', 0)}")
+@pytest.mark.parametrize("wdtype", [torch.float32, torch.bfloat16])
+def test_small_layers(case, wdtype):
+    case = dict(case)
+    cfg = moe_inputs.config(case.pop("name"), **case)
+    say(f"mega_moe N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} S={cfg.shared} "
+        f"fmt={cfg.fmt} weights={wdtype}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    x = x_t.double().numpy()
+    w = moe_inputs.gate_weights(cfg)
+    w_t = torch.from_numpy(w).to(wdtype)
+    w_used = w_t.double().numpy()
+    weights = oracle_weights(cfg)
+    shared = None
+    shared_np = ()
+    if cfg.shared:
+        sh = oracle_weights(cfg, cfg.shared, shared=True)
+        shared_np = [tuple(a[s] for a in sh) for s in range(cfg.shared)]
+        shared = tuple(to_dev(a) for a in sh)
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), w_t.to(DEV),
+                              *[to_dev(a) for a in weights], shared=shared, quant_out_dtype=FP8[cfg.fmt], debug=True)
+    torch.cuda.synchronize()
+    ref = moe.mega_moe(x, ids, w_used, weights, cfg.fmt, cfg.experts, shared=shared_np)
+    assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
+    assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), ref["routing"]["sorted_row_idx"])
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    assert np.array_equal(dbg["sx"].cpu().numpy(), ref["sx"])
+    h1_got = dbg["h1"].cpu().numpy()
+    err = normwise_err(h1_got, ref["h1"])
+    assert err <= 2e-3, err
+    offs = ref["routing"]["offsets"]
+    h1_abs = np.zeros_like(ref["h1"])
+    for e in range(cfg.experts):
+        if offs[e + 1] > offs[e]:
+            h1_abs[offs[e]:offs[e + 1]] = abs_gmm(ref["xq"][offs[e]:offs[e + 1]], ref["sx"][offs[e]:offs[e + 1]],
+                                                  weights[0][e], weights[1][e], cfg.fmt)
+    check_gemm_elementwise(h1_got, ref["h1"], h1_abs, cfg.hidden)
+    delta = swiglu_delta(ref["h1"], h1_abs, cfg.hidden, cfg.inter)
+    codes, scales = check_requant(dbg["aq"].cpu().numpy(), dbg["sa"].cpu().numpy(), ref["a"], delta, cfg.fmt)
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  h1 err {err:.3g} requant codes differing {codes:.3g} scales {scales:.3g} Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
+@pytest.mark.parametrize("tokens,hidden,inter", [(64, 256, 128), (200, 512, 256), (40, 7168, 2048)])
+def test_shared_expert_alone(tokens, hidden, inter):
+    """All gate weights 0: Y is the shared expert's dense FFN over every token."""
+    cfg = moe_inputs.config("tiny", tokens=tokens, hidden=hidden, inter=inter, shared=1, seed=46)
+    say(f"mega_moe shared expert alone N={tokens} H={hidden} I={inter}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = np.zeros((cfg.tokens, cfg.topk), np.float32)
+    weights = oracle_weights(cfg, 1)
+    weights = tuple(np.repeat(a, cfg.experts, axis=0) for a in weights)
+    sh = oracle_weights(cfg, 1, shared=True)
+    y, _ = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *[to_dev(a) for a in weights],
+                       shared=tuple(to_dev(a) for a in sh), quant_out_dtype=FP8[cfg.fmt])
+    torch.cuda.synchronize()
+    x = x_t.double().numpy()
+    xq, sx = mxfp.quantize(x, cfg.fmt)
+    ref = mxfp.bf16_round(moe.expert_ffn(xq, sx, *[a[0] for a in sh], cfg.fmt)["o"])
+    mx, mean = y_errors(y.cpu().double().numpy(), ref)
+    say(f"  Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
+def test_repeated_calls_reuse_workspace():
+    cfg = moe_inputs.config("tiny", seed=45)
+    say("mega_moe repeated calls")
+    ids = to_dev(moe_inputs.expert_ids(cfg).astype(np.int32))
+    x = moe_inputs.activations(cfg).to(DEV)
+    w = to_dev(moe_inputs.gate_weights(cfg))
+    weights = [to_dev(a) for a in oracle_weights(cfg)]
+    y1, e1 = rp.mega_moe(x, ids, w, *weights)
+    y2, e2 = rp.mega_moe(x, ids, w, *weights)
+    torch.cuda.synchronize()
+    assert torch.equal(e1, e2)
+    d = (y1.float() - y2.float()).abs().max().item()
+    assert d <= 2e-2 * y1.float().abs().max().item()
+
+
+def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True):
+    cfg = moe_inputs.config(name)
+    say(f"mega_moe full size {name}: N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} "
+        f"S={cfg.shared} fmt={cfg.fmt}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    weights = library_weights(cfg)
+    shared = library_weights(cfg, cfg.shared, shared=True) if cfg.shared else None
+    say("  weights ready")
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *weights, shared=shared,
+                              quant_out_dtype=FP8[cfg.fmt], debug=True)
+    torch.cuda.synchronize()
+    say("  layer done")
+    r = routing.init_routing(ids, cfg.experts)
+    assert np.array_equal(etn.cpu().numpy(), r["counts"].astype(np.int32))
+    assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), r["sorted_row_idx"])
+    rng = np.random.default_rng(7)
+    tokens = rng.choice(cfg.tokens, size=n_tokens_sampled, replace=False)
+    busiest = int(np.argmax(r["counts"]))
+    needed = sorted(set(int(e) for e in ids[tokens].reshape(-1)) | {busiest})
+    cache = oracle_experts_parallel(cfg, needed)
+    for e in needed:   # the library's weight bytes equal the oracle's quantization of the same masters
+        for j in range(4):
+            assert np.array_equal(weights[j][e].cpu().numpy(), cache[e][j]), (e, j)
+
+    def expert(e):
+        return cache[e]
+
+    shared_np = [oracle_expert_from_gpu_masters(cfg, s, shared=True) for s in range(cfg.shared)]
+    say(f"  oracle weights ready ({len(needed)} experts)")
+    x = x_t.double().numpy()
+    ref = moe.per_token(x, ids, w, expert, cfg.fmt, tokens, shared=shared_np)
+    y_got = y[torch.from_numpy(tokens).to(DEV)].cpu().double().numpy()
+    mx, mean = y_errors(y_got, ref["y"])
+    inv = routing.inverse(r["sorted_row_idx"]).reshape(cfg.tokens, cfg.topk)
+    pos = inv[tokens].reshape(-1)
+    h1_got = dbg["h1"][torch.from_numpy(pos).to(DEV)].cpu().numpy()
+    err = normwise_err(h1_got, ref["h1"].reshape(len(pos), -1))
+    xq_ref, sx_ref = mxfp.quantize(x[tokens], cfg.fmt)
+    assert np.array_equal(dbg["xq"][torch.from_numpy(pos).to(DEV)].cpu().numpy(), np.repeat(xq_ref, cfg.topk, axis=0))
+    assert np.array_equal(dbg["sx"][torch.from_numpy(pos).to(DEV)].cpu().numpy(), np.repeat(sx_ref, cfg.topk, axis=0))
+    say(f"  sampled tokens {tokens.tolist()}: Y max {mx:.3g} mean {mean:.3g}, h1 err {err:.3g}")
+    assert err <= 2e-3
+    assert mx <= 2e-2 and mean <= 5e-3
+    if check_expert_rows:
+        # every row of the busiest expert: h1 of the whole group (largest tile count)
+        e = busiest
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        q = expert(e)
+        xq_rows = dbg["xq"][lo:hi].cpu().numpy()
+        sx_rows = dbg["sx"][lo:hi].cpu().numpy()
+        src = r["sorted_row_idx"][lo:hi] // cfg.topk
+        xq_o, sx_o = mxfp.quantize(x[src], cfg.fmt)
+        assert np.array_equal(xq_rows, xq_o) and np.array_equal(sx_rows, sx_o)
+        h1_ref = moe.gmm(xq_o, sx_o, q[0], q[1], cfg.fmt)
+        h1_abs = abs_gmm(xq_o, sx_o, q[0], q[1], cfg.fmt)
+        h1_got = dbg["h1"][lo:hi].cpu().numpy()
+        err_e = normwise_err(h1_got, h1_ref)
+        check_gemm_elementwise(h1_got, h1_ref, h1_abs, cfg.hidden)
+        a_ref = mxfp.fp32_round(moe.swiglu(h1_ref[:, :cfg.inter], h1_ref[:, cfg.inter:]))
+        delta = swiglu_delta(h1_ref, h1_abs, cfg.hidden, cfg.inter)
+        codes, scales = check_requant(dbg["aq"][lo:hi].cpu().numpy(), dbg["sa"][lo:hi].cpu().numpy(), a_ref, delta,
+                                      cfg.fmt)
+        say(f"  expert {e} ({hi - lo} rows): h1 err {err_e:.3g}, requant codes differing {codes:.3g} "
+            f"scales {scales:.3g}")
+        assert err_e <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_full_size_decode():
+    full_size_check("decode", n_tokens_sampled=4)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_skewed():
+    full_size_check("skewed", n_tokens_sampled=6)
+
+
+@pytest.mark.timeout(900)
+def test_full_size_prefill():
+    full_size_check("prefill", n_tokens_sampled=3)

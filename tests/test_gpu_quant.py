@@ -1,0 +1,60 @@
+"""MX quantization on the GPU against the oracle, bit for bit: every finite bf16 value,
+both FP8 formats, in two arrangements (random groups; groups of neighbouring
+magnitudes, which sweeps every scale byte, saturation, subnormal elements and
+subnormal amax). Plus fp16 / fp32 inputs and a ragged row count."""
+import numpy as np
+import pytest
+import torch
+
+import routing_permute_mxfp8_amd as rp
+from oracle import mxfp
+from gpu_support import DEV, QMODE, say
+
+pytestmark = pytest.mark.gpu
+
+
+def finite_bf16_bits():
+    bits = np.arange(65536, dtype=np.uint32)
+    v = (bits << 16).view(np.float32)
+    return bits[np.isfinite(v)].astype(np.uint16)
+
+
+def run(bits_2d, fmt):
+    x = torch.from_numpy(bits_2d.astype(np.int16)).view(torch.bfloat16).to(DEV)
+    codes, scales = rp.mx_quantize(x, QMODE[fmt])
+    torch.cuda.synchronize()
+    vals = mxfp.bf16_from_bits(bits_2d)
+    oc, os_ = mxfp.quantize(vals, fmt)
+    return codes.cpu().numpy(), scales.cpu().numpy(), oc, os_
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("arrangement", ["random", "sorted"])
+def test_all_bf16_values(fmt, arrangement):
+    say(f"mx_quantize all bf16 fmt={fmt} arrangement={arrangement}")
+    bits = finite_bf16_bits()
+    rng = np.random.default_rng(0)
+    if arrangement == "random":
+        bits = rng.permutation(bits)
+    else:
+        mag = np.abs(mxfp.bf16_from_bits(bits))
+        bits = bits[np.argsort(mag, kind="stable")]
+    pad = (-bits.size) % 256
+    bits = np.concatenate([bits, np.zeros(pad, np.uint16)]).reshape(-1, 256)
+    gc, gs, oc, os_ = run(bits, fmt)
+    assert np.array_equal(gs, os_)
+    assert np.array_equal(gc, oc)
+
+
+@pytest.mark.parametrize("dtype", [torch.float16, torch.float32])
+def test_other_input_dtypes(dtype):
+    say(f"mx_quantize dtype={dtype}")
+    rng = np.random.default_rng(1)
+    a = (rng.standard_normal((37, 96)) * np.exp(rng.uniform(-6, 6, (37, 1)))).astype(np.float32)
+    x = torch.from_numpy(a).to(dtype)
+    vals = x.double().numpy()
+    codes, scales = rp.mx_quantize(x.to(DEV), rp.QUANT_E4M3)
+    oc, os_ = mxfp.quantize(vals, "e4m3")
+    assert scales.shape == (37, 4)
+    assert np.array_equal(scales.cpu().numpy(), os_)
+    assert np.array_equal(codes.cpu().numpy(), oc)

@@ -10,8 +10,8 @@ MegaMoE page, "A8W8-FP quantization scenario":
 swiglu A = SiLU(G_c) * U_c, with c = +inf when no clamp is configured.
 "MXFP quantization scenario constraints": weight1 (E, 2I, H) and weight2
 (E, H, I), each output channel holding its K-contiguous inputs; G is the first
-I output channels of weight1 and U the last I ("first N/2 columns ... last N/2
-columns" of the logical H x 2I matrix).
+I output channels of weight1 and U the last I (the page splits the logical
+H x 2I matrix into its first and second halves of columns).
 
 Readings: accumulations are float64 on exact dequantized operands; the
 activation is evaluated in float64 and rounded once to fp32 before the MX

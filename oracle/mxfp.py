@@ -5,7 +5,7 @@ MegaMoE page, "A8W8-FP quantization scenario", stage 1: Q_MX takes groups of
 factor) and quantizes the group to FLOAT8_E4M3FN or FLOAT8_E5M2; DQ_MX is the
 inverse, done implicitly inside the matmul. The pages do not state the scale
 rule or the element rounding; the oracle takes the OCP Microscaling (MX) v1.0
-definitions, which is what "shared exponent" plus E8M0 denotes:
+definitions, the standard meaning of a per-group shared exponent stored as E8M0:
 
 * shared exponent  X = 2^(floor(log2(amax)) - emax_elem), emax_elem = 8 (E4M3)
   or 15 (E5M2), the exponent of the element format's largest normal;

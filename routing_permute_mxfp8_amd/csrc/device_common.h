@@ -21,8 +21,8 @@ template <> struct Fp8<1> {
   static constexpr float maxv = 57344.0f;
 };
 
-// E8M0 scale byte of an MX group (MegaMoE A8W8-FP stage 1: "the shared exponent is
-// extracted"; OCP MX rule): clamp(floor(log2(amax)) - emax + 127, 0, 254).
+// E8M0 scale byte of an MX group (MegaMoE A8W8-FP stage 1 takes one shared exponent
+// per 32 elements; the OCP MX rule gives it): clamp(floor(log2(amax)) - emax + 127, 0, 254).
 // amax >= 0 and finite. For a normal float the biased exponent field is
 // floor(log2) + 127, so the byte is field - emax; zero and subnormal amax give a
 // negative value, clamped to 0. The upper clamp is never reached (field <= 254).

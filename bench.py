@@ -127,16 +127,21 @@ def bench_mega(args, torch, rp, moe_inputs):
     log(f"[bench] {cfg.name}: generating weights on the GPU")
     weights = library_weights(torch, rp, moe_inputs, cfg, cfg.experts, shared=False)
     shared = library_weights(torch, rp, moe_inputs, cfg, cfg.shared, shared=True) if cfg.shared else None
+    wf = rp.WEIGHTS_PACKED if args.weights == "packed" else rp.WEIGHTS_ND
+    if wf == rp.WEIGHTS_PACKED:   # one-time conversion to the MFMA-native layout, untimed
+        weights = (*rp.pack_weights(weights[0], weights[1]), *rp.pack_weights(weights[2], weights[3]))
+        if shared is not None:
+            shared = (*rp.pack_weights(shared[0], shared[1]), *rp.pack_weights(shared[2], shared[3]))
     x = x_cpu.cuda()
     ids_d = torch.from_numpy(ids).cuda()
     w_d = torch.from_numpy(w).cuda()
     fmt = rp.FP8_E4M3 if cfg.fmt == "e4m3" else rp.FP8_E5M2
-    nbytes = rp.mega_moe_workspace_bytes(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt)
+    nbytes = rp.mega_moe_workspace_bytes(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, weight_format=wf)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws)
+        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, weight_format=wf)
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(rp.MEGA_STAGE_EVENTS)] for _ in range(args.steps)]
     for st in evs:
@@ -148,7 +153,8 @@ def bench_mega(args, torch, rp, moe_inputs):
     t0 = time.perf_counter()
     start.record()
     for k in range(args.steps):
-        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, stage_events=evs[k])
+        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, stage_events=evs[k],
+                    weight_format=wf)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -171,7 +177,8 @@ def bench_mega(args, torch, rp, moe_inputs):
                config=dict(workload=f"{cfg.name}: {cfg.tokens} tokens, hidden {cfg.hidden}, inter {cfg.inter}, "
                                     f"{cfg.experts} experts, topK {cfg.topk}, shared {cfg.shared}, {cfg.fmt}",
                            tokens=cfg.tokens, hidden=cfg.hidden, inter=cfg.inter, experts=cfg.experts,
-                           topk=cfg.topk, shared=cfg.shared, fmt=cfg.fmt, touched_experts=work["touched"]),
+                           topk=cfg.topk, shared=cfg.shared, fmt=cfg.fmt, touched_experts=work["touched"],
+                           weight_layout=args.weights),
                roofline=roofline,
                layer=dict(algorithmic_bytes=total_bytes, flops=total_flops,
                           hbm_frac=round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
@@ -233,6 +240,8 @@ def main():
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "routing"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU oracle sample")
+    ap.add_argument("--weights", default="packed", choices=["packed", "nd"],
+                    help="weight layout: the library's MFMA-native packed layout or the pages' ND layout")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "

@@ -102,6 +102,23 @@ moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
                            uint8_t* codes, uint8_t* scales, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Weight formats. MOE_WEIGHTS_ND is the pages' layout ([MM] "MXFP quantization */
+/* scenario constraints": codes [G, N, K], scales [G, N, K/32]). MOE_WEIGHTS_PACKED */
+/* is this library's MFMA-native layout (the analog of the pages' fractal weight  */
+/* formats): codes in 16-channel x 128-K tiles of 2048 bytes in MFMA lane order   */
+/* (tile (g, n/16, k/128), then half h, lane l: row 16*(n/16) + l%16, K bytes       */
+/* [128*(k/128) + 64*h + 16*(l/16), +16)), same total size; scales as one dword per */
+/* lane per 4 K steps: [G][N/16][CeilDiv(K, 512)][64][4] bytes.                     */
+/* moe_mx_pack_weights converts ND codes/scales to the packed layout on `stream`;   */
+/* moe_mx_packed_scale_bytes gives the packed scale size. N % 16 == 0 and           */
+/* K % 128 == 0 are required.                                                        */
+/* ------------------------------------------------------------------------ */
+enum { MOE_WEIGHTS_ND = 0, MOE_WEIGHTS_PACKED = 1 };
+int64_t moe_mx_packed_scale_bytes(int64_t groups, int64_t n, int64_t k);
+moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n,
+                               int64_t k, uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_init_routing  ([V3] 计算公式 1-6, dropless mode).                      */
 /*   x            device, [num_rows, hidden] of x_dtype (BF16, FP16; FP32 too  */
 /*                when quant_mode = -1)                                        */
@@ -180,6 +197,7 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /*                [num_experts, 2*inter, hidden/32] (= (.., CeilDiv(hidden,64), 2)) */
 /*   w2           fp8 [num_experts, hidden, inter];  w2_scales uint8              */
 /*                [num_experts, hidden, inter/32]                                 */
+/*                (or both in MOE_WEIGHTS_PACKED layout, see weight_format)       */
 /*   shared_*     the same for num_shared (0..4) shared experts, or NULL          */
 /*   y            out, bf16 [num_tokens, hidden]                                  */
 /*   expert_token_nums  out, int32 [num_experts] (nullable)                       */
@@ -219,6 +237,7 @@ typedef struct {
   const uint8_t* shared_w2_scales;
   int quant_out_dtype;            /* MOE_FP8_E5M2 or MOE_FP8_E4M3 (= the weights' FP8 type) */
   int activation;                 /* MOE_ACT_SWIGLU */
+  int weight_format;              /* MOE_WEIGHTS_ND or MOE_WEIGHTS_PACKED (routed and shared) */
   void* y;
   int32_t* expert_token_nums;
   /* optional parity outputs */
@@ -254,18 +273,19 @@ moe_status mega_moe(const moe_mega_args* args /* host */, void* workspace, size_
 /*                 weight * O[row] (accumulated atomically)                    */
 /*   o             device out, fp32 [rows, hidden] unweighted O, or NULL        */
 /* moe_combine_finalize: y (bf16 [num_tokens, hidden]) = RNE(y_accum).         */
-/* Limits as in mega_moe; fp8 = quant_out_dtype (23/24). Workspace:            */
+/* Limits as in mega_moe; fp8 = quant_out_dtype (23/24); weights in           */
+/* weight_format. Workspace:                                                    */
 /* moe_gmm_workspace_size.                                                     */
 /* ------------------------------------------------------------------------ */
 moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, size_t* bytes /* host out */);
 moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t rows, int64_t hidden,
                                  int64_t inter, const int32_t* group_offsets, int64_t num_groups,
-                                 const uint8_t* w1, const uint8_t* w1_scales, int quant_out_dtype,
+                                 const uint8_t* w1, const uint8_t* w1_scales, int weight_format, int quant_out_dtype,
                                  uint8_t* aq, uint8_t* sa, float* h1, void* workspace,
                                  size_t workspace_bytes, void* stream);
 moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, int64_t inter,
                             int64_t hidden, const int32_t* group_offsets, int64_t num_groups,
-                            const uint8_t* w2, const uint8_t* w2_scales, int quant_out_dtype,
+                            const uint8_t* w2, const uint8_t* w2_scales, int weight_format, int quant_out_dtype,
                             const int32_t* row_token, const float* row_weight, int64_t num_tokens,
                             float* y_accum, float* o, void* workspace, size_t workspace_bytes,
                             void* stream);

@@ -24,10 +24,12 @@ __all__ = [
     "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "FP8_E5M2", "FP8_E4M3",
     "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "token_permute",
     "mega_moe", "mega_moe_workspace_bytes", "gmm1_swiglu_quant", "gmm2_combine", "combine_finalize",
+    "pack_weights", "WEIGHTS_ND", "WEIGHTS_PACKED",
 ]
 
 QUANT_NONE, QUANT_E5M2, QUANT_E4M3 = -1, 2, 3
 FP8_E5M2, FP8_E4M3 = 23, 24
+WEIGHTS_ND, WEIGHTS_PACKED = 0, 1
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int32: 3, torch.int64: 4}
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP"}
 
@@ -49,7 +51,7 @@ class MegaArgs(ctypes.Structure):
         ("num_shared", ctypes.c_int64),
         ("shared_w1", ctypes.c_void_p), ("shared_w1_scales", ctypes.c_void_p),
         ("shared_w2", ctypes.c_void_p), ("shared_w2_scales", ctypes.c_void_p),
-        ("quant_out_dtype", ctypes.c_int), ("activation", ctypes.c_int),
+        ("quant_out_dtype", ctypes.c_int), ("activation", ctypes.c_int), ("weight_format", ctypes.c_int),
         ("y", ctypes.c_void_p), ("expert_token_nums", ctypes.c_void_p),
         ("xq", ctypes.c_void_p), ("sx", ctypes.c_void_p), ("h1", ctypes.c_void_p),
         ("aq", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("o", ctypes.c_void_p),
@@ -71,6 +73,8 @@ _SIGS = {
     "moe_mx_scale_cols": ([_I64], _I64),
     "moe_token_permute_out_rows": ([_I64, _I64], _I64),
     "moe_mx_quantize": ([_VP, _INT, _I64, _I64, _INT, _VP, _VP, _VP], _INT),
+    "moe_mx_packed_scale_bytes": ([_I64, _I64, _I64], _I64),
+    "moe_mx_pack_weights": ([_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP], _INT),
     "moe_init_routing_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_init_routing": ([_VP, _INT, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
                           _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
@@ -80,9 +84,9 @@ _SIGS = {
     "mega_moe_workspace_size": ([ctypes.POINTER(MegaArgs), ctypes.POINTER(_SZ)], _INT),
     "mega_moe": ([ctypes.POINTER(MegaArgs), _VP, _SZ, _VP], _INT),
     "moe_gmm_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
-    "moe_gmm1_swiglu_quant": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _VP, _VP, _VP,
+    "moe_gmm1_swiglu_quant": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _INT, _VP, _VP, _VP,
                                _VP, _SZ, _VP], _INT),
-    "moe_gmm2_combine": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _VP, _VP, _I64, _VP,
+    "moe_gmm2_combine": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _INT, _VP, _VP, _I64, _VP,
                           _VP, _VP, _SZ, _VP], _INT),
     "moe_combine_finalize": ([_VP, _I64, _I64, _VP, _VP], _INT),
 }
@@ -157,6 +161,19 @@ def mx_quantize(x: torch.Tensor, quant_mode: int = QUANT_E4M3):
     return codes, scales
 
 
+def pack_weights(codes, scales):
+    """MX weights [G, N, K] codes + [G, N, K/32] scales (the pages' layout) -> the library's
+    MFMA-native packed layout: (codes uint8 [G, N, K] in packed order, scales uint8 1-D)."""
+    lib = load()
+    codes, scales = _u8(codes), _u8(scales)
+    _need_gpu(codes, scales)
+    g, n, k = codes.shape
+    pc = torch.empty_like(codes)
+    ps = torch.empty((int(lib.moe_mx_packed_scale_bytes(g, n, k)),), dtype=torch.uint8, device=codes.device)
+    _check(lib.moe_mx_pack_weights(_ptr(codes), _ptr(scales), g, n, k, _ptr(pc), _ptr(ps), _stream(codes.device)))
+    return pc, ps
+
+
 def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: int = QUANT_NONE,
                  row_idx_type: int = 1, expert_tokens_num_type: int = 1):
     """MoeInitRoutingV3 (dropless). Returns (expanded_x, expanded_row_idx, expert_tokens,
@@ -211,7 +228,7 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
 
 
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
-                 debug):
+                 debug, weight_format=WEIGHTS_ND):
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -226,7 +243,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
         a.num_shared = sw1.shape[0]
         a.shared_w1, a.shared_w1_scales = _ptr(_u8(sw1)), _ptr(_u8(ss1))
         a.shared_w2, a.shared_w2_scales = _ptr(_u8(sw2)), _ptr(_u8(ss2))
-    a.quant_out_dtype, a.activation = quant_out_dtype, 0
+    a.quant_out_dtype, a.activation, a.weight_format = quant_out_dtype, 0, weight_format
     a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
     for name in ("xq", "sx", "h1", "aq", "sa", "o", "sorted_row_idx"):
         setattr(a, name, _ptr(debug.get(name)) if debug else None)
@@ -234,12 +251,15 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
 
 
 def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
-             quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None):
+             quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None,
+             weight_format: int = WEIGHTS_ND):
     """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
     debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
 
     shared: None or (shared_w1, shared_w1_scales, shared_w2, shared_w2_scales) stacked
     over the shared experts. workspace: optional preallocated uint8 device tensor.
+    weight_format: WEIGHTS_ND (the pages' layout) or WEIGHTS_PACKED (w1/w2 and the
+    shared weights as returned by pack_weights; the code tensors keep their [E, N, K] shape).
     stage_events: optional list of MEGA_STAGE_EVENTS torch.cuda.Event(enable_timing=True),
     recorded by the library on the stream at the boundaries of MEGA_STAGES."""
     lib = load()
@@ -261,7 +281,8 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
                    sa=torch.empty((f, inter // 32), dtype=torch.uint8, device=dev),
                    o=torch.empty((f, h), dtype=torch.float32, device=dev),
                    sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
-    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg)
+    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg,
+                     weight_format)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} events")
@@ -279,15 +300,17 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
 
 
 def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
-                             quant_out_dtype: int = FP8_E4M3) -> int:
+                             quant_out_dtype: int = FP8_E4M3, weight_format: int = WEIGHTS_ND) -> int:
     lib = load()
-    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None)
+    a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None,
+                     weight_format)
     nbytes = ctypes.c_size_t()
     _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     return nbytes.value
 
 
-def gmm1_swiglu_quant(xq, sx, group_offsets, w1, w1_scales, quant_out_dtype: int = FP8_E4M3, want_h1: bool = False):
+def gmm1_swiglu_quant(xq, sx, group_offsets, w1, w1_scales, quant_out_dtype: int = FP8_E4M3, want_h1: bool = False,
+                      weight_format: int = WEIGHTS_ND):
     """Stage 2 on given operands: (aq uint8 [rows, I], sa uint8 [rows, I/32], h1 fp32 [rows, 2I] or None)."""
     lib = load()
     xq, sx, w1, w1_scales = _u8(xq), _u8(sx), _u8(w1), _u8(w1_scales)
@@ -303,13 +326,13 @@ def gmm1_swiglu_quant(xq, sx, group_offsets, w1, w1_scales, quant_out_dtype: int
     _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
     _check(lib.moe_gmm1_swiglu_quant(_ptr(xq), _ptr(sx), rows, h, inter, _ptr(group_offsets), g, _ptr(w1),
-                                     _ptr(w1_scales), quant_out_dtype, _ptr(aq), _ptr(sa), _ptr(h1), _ptr(ws),
-                                     ws.numel(), _stream(dev)))
+                                     _ptr(w1_scales), weight_format, quant_out_dtype, _ptr(aq), _ptr(sa), _ptr(h1),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
     return aq, sa, h1
 
 
 def gmm2_combine(aq, sa, group_offsets, w2, w2_scales, row_token, row_weight, y_accum,
-                 quant_out_dtype: int = FP8_E4M3, want_o: bool = False):
+                 quant_out_dtype: int = FP8_E4M3, want_o: bool = False, weight_format: int = WEIGHTS_ND):
     """Stages 3-4 on given operands: y_accum[row_token[r]] += row_weight[r] * O[r]; returns O (fp32) or None."""
     lib = load()
     aq, sa, w2, w2_scales = _u8(aq), _u8(sa), _u8(w2), _u8(w2_scales)
@@ -322,7 +345,7 @@ def gmm2_combine(aq, sa, group_offsets, w2, w2_scales, row_token, row_weight, y_
     _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
     _check(lib.moe_gmm2_combine(_ptr(aq), _ptr(sa), rows, inter, h, _ptr(group_offsets), g, _ptr(w2),
-                                _ptr(w2_scales), quant_out_dtype, _ptr(row_token), _ptr(row_weight),
+                                _ptr(w2_scales), weight_format, quant_out_dtype, _ptr(row_token), _ptr(row_weight),
                                 y_accum.shape[0], _ptr(y_accum), _ptr(o), _ptr(ws), ws.numel(), _stream(dev)))
     return o
 

@@ -88,11 +88,12 @@ int quant_fmt(int quant_mode) { return quant_mode == MOE_QUANT_MXFP8_E4M3 ? 0 : 
 
 bool valid_x_dtype(int d) { return d == MOE_DTYPE_FP32 || d == MOE_DTYPE_FP16 || d == MOE_DTYPE_BF16; }
 
-int token_tile_tt(int64_t rows, int64_t groups) {
-  const double avg = groups > 0 ? (double)rows / (double)groups : (double)rows;
-  if (avg <= 20.0) return 1;
-  if (avg <= 40.0) return 2;
-  return 4;
+int token_tile_tt(int64_t rows, int64_t groups) { return moe::gmm_token_tiles(rows, groups); }
+
+// Scale bytes of one weight group (N output channels, K inputs) in a weight format.
+int64_t group_scale_bytes(int64_t n, int64_t k, int format) {
+  if (format == MOE_WEIGHTS_PACKED) return (n / 16) * (((k / 128) + 3) / 4) * 256;
+  return n * (k / 32);
 }
 
 // ---- moe_init_routing ------------------------------------------------------------
@@ -152,7 +153,7 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.aq = a->aq ? nullptr : cv.take<uint8_t>((size_t)flat * i);
   w.sa = a->sa ? nullptr : cv.take<uint8_t>((size_t)flat * (i / 32));
   if (a->num_shared > 0) {
-    w.sh_tt = n <= 16 ? 1 : (n <= 32 ? 2 : 4);
+    w.sh_tt = token_tile_tt(n, 1);
     w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
     w.sh_tiles = cv.take<int4>(w.sh_max_tiles);
     w.sh_count = cv.take<int>(1);
@@ -191,6 +192,8 @@ moe_status check_mega(const moe_mega_args* a) {
     return fail(MOE_ERR_UNSUPPORTED, "mega_moe: activation %d not supported (only swiglu)", a->activation);
   if (a->topk_weights_dtype != MOE_DTYPE_FP32 && a->topk_weights_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_DTYPE, "mega_moe: topk_weights_dtype must be FP32 or BF16");
+  if (a->weight_format != MOE_WEIGHTS_ND && a->weight_format != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: weight_format %d not 0 (ND) or 1 (packed)", a->weight_format);
   if (a->num_tokens > 0 && (!a->x || !a->topk_ids || !a->topk_weights || !a->y))
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: x, topk_ids, topk_weights and y must be non-NULL");
   if (!a->w1 || !a->w1_scales || !a->w2 || !a->w2_scales)
@@ -268,6 +271,23 @@ moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
   p.quant = quant_fmt(quant_mode); p.out = codes; p.out_scales = scales; p.scale_cols = scale_cols(cols);
   hipError_t e = moe::launch_permute(p, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_mx_quantize launch");
+  return ok();
+}
+
+int64_t moe_mx_packed_scale_bytes(int64_t groups, int64_t n, int64_t k) {
+  if (groups < 0 || n <= 0 || k <= 0) return 0;
+  return groups * group_scale_bytes(n, k, MOE_WEIGHTS_PACKED);
+}
+
+moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                               uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  if (groups < 0 || n <= 0 || k <= 0 || n % 16 != 0 || k % 128 != 0)
+    return fail(MOE_ERR_SHAPE, "moe_mx_pack_weights: groups >= 0, n %% 16 == 0 and k %% 128 == 0 required");
+  if (groups == 0) return ok();
+  if (!codes || !scales || !packed_codes || !packed_scales)
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx_pack_weights: NULL buffer");
+  hipError_t e = moe::launch_pack_weights(codes, scales, groups, n, k, packed_codes, packed_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_mx_pack_weights launch");
   return ok();
 }
 
@@ -454,8 +474,9 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if (e != hipSuccess) return hip_fail(e, "mega_moe permute launch");
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 2: GMM1 + SwiGLU + MX requantization
+  const int packed = a->weight_format == MOE_WEIGHTS_PACKED;
   moe::Gmm1Params g1{xq, sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, aq, sa, a->h1};
+                     (int)h, (int)inter, fmt, w.tt, aq, sa, a->h1, packed};
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
@@ -464,7 +485,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if (e != hipSuccess) return hip_fail(e, "mega_moe zero-fill launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   moe::Gmm2Params g2{aq, sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, w.row_token, w.row_weight, w.y_acc, a->o};
+                     (int)h, (int)inter, fmt, w.tt, w.row_token, w.row_weight, w.y_acc, a->o, packed};
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
@@ -474,13 +495,15 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
     for (int64_t s = 0; s < a->num_shared; ++s) {
       moe::Gmm1Params s1{w.xq_tok, w.sx_tok, a->shared_w1 + s * 2 * inter * h,
-                         a->shared_w1_scales + s * 2 * inter * (h / 32), w.sh_tiles, w.sh_count, w.sh_max_tiles,
-                         (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr};
+                         a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
+                         w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr,
+                         packed};
       e = moe::launch_gmm1(s1, st);
       if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
-      moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter, a->shared_w2_scales + s * h * (inter / 32),
-                         w.sh_tiles, w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt,
-                         nullptr, nullptr, w.y_acc, nullptr};
+      moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter,
+                         a->shared_w2_scales + s * group_scale_bytes(h, inter, a->weight_format), w.sh_tiles,
+                         w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, nullptr, nullptr, w.y_acc,
+                         nullptr, packed};
       e = moe::launch_gmm2(s2, st);
       if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
     }
@@ -503,10 +526,12 @@ moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, size_t* byte
 
 moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t rows, int64_t hidden, int64_t inter,
                                  const int32_t* group_offsets, int64_t num_groups, const uint8_t* w1,
-                                 const uint8_t* w1_scales, int quant_out_dtype, uint8_t* aq, uint8_t* sa, float* h1,
-                                 void* workspace, size_t workspace_bytes, void* stream) {
+                                 const uint8_t* w1_scales, int weight_format, int quant_out_dtype, uint8_t* aq,
+                                 uint8_t* sa, float* h1, void* workspace, size_t workspace_bytes, void* stream) {
   const char* who = "moe_gmm1_swiglu_quant";
   if (moe_status s = check_gmm_common(who, rows, hidden, inter, num_groups, quant_out_dtype)) return s;
+  if (weight_format != MOE_WEIGHTS_ND && weight_format != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "%s: weight_format %d not 0 or 1", who, weight_format);
   if (!group_offsets || !w1 || !w1_scales || (rows > 0 && (!xq || !sx || !aq || !sa)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
   Carver cv(nullptr);
@@ -519,7 +544,7 @@ moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t r
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
   moe::Gmm1Params g{xq, sx, w1, w1_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
-                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, aq, sa, h1};
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, aq, sa, h1, weight_format};
   e = moe::launch_gmm1(g, st);
   if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
   return ok();
@@ -527,11 +552,13 @@ moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t r
 
 moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, int64_t inter, int64_t hidden,
                             const int32_t* group_offsets, int64_t num_groups, const uint8_t* w2,
-                            const uint8_t* w2_scales, int quant_out_dtype, const int32_t* row_token,
-                            const float* row_weight, int64_t num_tokens, float* y_accum, float* o, void* workspace,
-                            size_t workspace_bytes, void* stream) {
+                            const uint8_t* w2_scales, int weight_format, int quant_out_dtype,
+                            const int32_t* row_token, const float* row_weight, int64_t num_tokens, float* y_accum,
+                            float* o, void* workspace, size_t workspace_bytes, void* stream) {
   const char* who = "moe_gmm2_combine";
   if (moe_status s = check_gmm_common(who, rows, hidden, inter, num_groups, quant_out_dtype)) return s;
+  if (weight_format != MOE_WEIGHTS_ND && weight_format != MOE_WEIGHTS_PACKED)
+    return fail(MOE_ERR_INVALID_ARG, "%s: weight_format %d not 0 or 1", who, weight_format);
   if (num_tokens < 1) return fail(MOE_ERR_SHAPE, "%s: num_tokens must be >= 1", who);
   if (!group_offsets || !w2 || !w2_scales || (rows > 0 && (!aq || !sa || !row_token || !row_weight || !y_accum)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
@@ -545,7 +572,8 @@ moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, 
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
   moe::Gmm2Params g{aq, sa, w2, w2_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
-                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, row_token, row_weight, y_accum, o};
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, row_token, row_weight, y_accum, o,
+                    weight_format};
   e = moe::launch_gmm2(g, st);
   if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
   return ok();

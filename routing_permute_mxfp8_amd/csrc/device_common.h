@@ -8,6 +8,9 @@ namespace moe {
 
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef float v4f __attribute__((ext_vector_type(4)));
+// Native 16-byte vector (HIP's uint4 is a class with a union inside and is kept in
+// scratch memory by the optimizer when held in arrays across branches).
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // FP8 element formats, indexed by the MFMA operand-type code (cbsz / blgp):
 // 0 = FLOAT8_E4M3FN, 1 = FLOAT8_E5M2.
@@ -88,13 +91,17 @@ __device__ __forceinline__ v4f mfma_mx16(const v8i& a, const v8i& b, v4f c, int 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
 }
 
-__device__ __forceinline__ v8i load_mx_operand(const uint8_t* row_k0, int g) {
-  const uint4 lo = *reinterpret_cast<const uint4*>(row_k0 + 16 * g);
-  const uint4 hi = *reinterpret_cast<const uint4*>(row_k0 + 64 + 16 * g);
+__device__ __forceinline__ v8i join_operand(u32x4 lo, u32x4 hi) {
   v8i r;
-  r[0] = (int)lo.x; r[1] = (int)lo.y; r[2] = (int)lo.z; r[3] = (int)lo.w;
-  r[4] = (int)hi.x; r[5] = (int)hi.y; r[6] = (int)hi.z; r[7] = (int)hi.w;
+  r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];
+  r[4] = (int)hi[0]; r[5] = (int)hi[1]; r[6] = (int)hi[2]; r[7] = (int)hi[3];
   return r;
+}
+
+__device__ __forceinline__ v8i load_mx_operand(const uint8_t* row_k0, int g) {
+  const u32x4 lo = *reinterpret_cast<const u32x4*>(row_k0 + 16 * g);
+  const u32x4 hi = *reinterpret_cast<const u32x4*>(row_k0 + 64 + 16 * g);
+  return join_operand(lo, hi);
 }
 
 }  // namespace moe

@@ -2,29 +2,40 @@
 //
 // MegaMoE README, "A8W8-FP quantization scenario":
 //   stage 2  G_e = DQ(X^_e).DQ(W1_e^(G)), U_e = DQ(X^_e).DQ(W1_e^(U)), A_e = SiLU(G_e)*U_e
-//            ("Activation function formulas", swiglu without clamp), then
-//            A^_e, S_A,e = Q_MX(A_e) in the same FP8 type as stage 1;
+//            (swiglu of the activation formulas, no clamp), then A^_e, S_A,e = Q_MX(A_e)
+//            with the FP8 type of stage 1;
 //   stage 3  O_e = DQ(A^_e).DQ(W2_e);
-//   stage 4  Y[i] = sum_k W[i,k] O[pi(i,k)] (+ shared expert outputs).
-// Weight layout ("MXFP quantization scenario constraints"): weight1 (E, 2I, H),
-// weight2 (E, H, I), every output channel a K-contiguous row; W1's first I
-// channels are the gate branch, the last I the up branch; E8M0 scales per 32 along K.
+//   stage 4  Y[i] = sum_k W[i,k] O[pi(i,k)] (+ the shared experts' outputs).
+// Weight layout (MXFP quantization scenario constraints): weight1 (E, 2I, H), weight2
+// (E, H, I), every output channel a K-contiguous row with one E8M0 scale per 32; the
+// first I channels of weight1 are the gate branch, the last I the up branch.
 //
-// Both GEMMs are computed transposed, C[channel][token] = sum_k W[channel][k] X[token][k],
-// with V_MFMA_SCALE_F32_16X16X128_F8F6F4: the weight rows are the MFMA A operand
-// (16 channels) and the token rows the B operand (16 tokens). A small expert (decode:
-// ~4 rows) then pads only to 16 tokens while the weights stream through the matrix
-// core once, straight from HBM into VGPRs; each K step (128) issues the next step's
-// 16-byte loads before the current MFMAs (register double buffering).
-//
-// Work items are (token tile, channel block) pairs over a device-built tile list
-// (tiles of 16*TT rows of one group), so no host readback of the expert counts.
-// GMM1 wave: 32 gate + 32 up channels x 16*TT tokens. The matching gate and up
-// accumulators sit in the same lane, so SwiGLU is lane-local; the 32-channel MX
-// group of the requantization is the lane's 8 values plus the 3 other lanes with
-// the same token (xor 16 / xor 32), and each lane stores 4 consecutive FP8 codes.
-// GMM2 wave: 64 channels x 16*TT tokens; the epilogue scales by the row's gate
-// weight and accumulates into the fp32 token rows with hardware float atomics.
+// Design (one kernel per GEMM, persistent):
+// * Work item = (token chunk of one expert, channel block). A chunk holds up to 16*NT
+//   rows of one expert (device-built tile list, no host readback of the counts).
+// * Each wave owns 64 output channels (GMM1: 32 gate + the matching 32 up channels)
+//   and streams their weights from HBM straight into VGPRs exactly once per chunk, with
+//   a two-step register prefetch. The chunk's token rows are staged per K step into LDS
+//   (double-buffered, laid out exactly as the MFMA operand so every ds_read_b128 is
+//   conflict-free) and shared by the block's waves.
+// * V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the E8M0 scales applied by the matrix core.
+//   GMM1 puts the weights in the A slot (output rows = channels): a lane then holds the
+//   gate and up values of the same channels, so SwiGLU is lane-local and the 32-channel
+//   MX group of the requantization is the lane's 8 values plus 3 lanes (xor 16 / 32).
+//   GMM2 puts the tokens in the A slot (output rows = tokens): a lane group then holds
+//   16 consecutive channels of one token, so the weighted combine issues fp32 atomics on
+//   64 contiguous bytes per token row.
+// * Blocks are persistent and XCD-aware: block b runs on XCD b % 8 and takes items from
+//   that XCD's contiguous share of the item list, so the channel blocks of one expert run
+//   together on one XCD and share its L2 for the token rows.
+// * Weights are read either in the pages' layout (ND) or in an MFMA-native packed layout
+//   (built once by moe_mx_pack_weights, the analog of the pages' fractal weight formats):
+//   16-channel x 128-K blocks of 2 KB in lane order, so each load instruction of a wave
+//   reads 1 KB of contiguous memory, with the scales of 4 K steps in one dword per lane.
+
+#include <algorithm>
+#include <map>
+#include <mutex>
 
 #include "device_common.h"
 #include "internal.h"
@@ -32,211 +43,384 @@
 namespace moe {
 namespace {
 
-__device__ __forceinline__ int scale_arg(const uint8_t* srow, int step, int g) {
-  return (int)(*reinterpret_cast<const uint32_t*>(srow + 4 * step) >> (8 * g));
+constexpr int kXcds = 8;
+constexpr int kTileBytes = 2048;   // one 16-row x 128-K MX operand tile
+constexpr int kTileScaleBytes = 256;
+
+// ---- weight operand loads --------------------------------------------------------
+// ND: row pointer of channel (tile*16 + r) and its scale row.
+// PACKED: tile base (group, 16-channel tile, K step 0) and its scale base + lane*4.
+template <bool PACKED>
+struct WPtr {
+  const uint8_t* d;
+  const uint8_t* s;
+};
+
+template <bool PACKED>
+__device__ __forceinline__ WPtr<PACKED> weight_tile(const uint8_t* w, const uint8_t* ws, int64_t tile_index, int K,
+                                                    int lane) {
+  // tile_index = group * (N / 16) + channel_tile
+  WPtr<PACKED> p;
+  const int ks = K >> 7;
+  if constexpr (PACKED) {
+    const int kq = (ks + 3) >> 2;
+    p.d = w + tile_index * ks * kTileBytes;
+    p.s = ws + tile_index * kq * kTileScaleBytes + lane * 4;
+  } else {
+    const int64_t row = tile_index * 16 + (lane & 15);
+    p.d = w + row * K;
+    p.s = ws + row * (K >> 5);
+  }
+  return p;
 }
 
-template <int FMT, int TT>
-__global__ __launch_bounds__(256) void gmm1_swiglu_kernel(
+// Loads one K step of a weight tile: the operand bytes and the raw scale dword. The
+// byte of the dword this lane needs is selected only where the MFMA uses it
+// (weight_scale), so no ALU work waits on a load before its data is due.
+template <bool PACKED>
+__device__ __forceinline__ void load_weight(const WPtr<PACKED>& p, int step, int lane, v8i& v, int& sc_raw) {
+  const int g = lane >> 4;
+  if constexpr (PACKED) {
+    const uint8_t* t = p.d + (int64_t)step * kTileBytes;
+    v = join_operand(*reinterpret_cast<const u32x4*>(t + lane * 16), *reinterpret_cast<const u32x4*>(t + 1024 + lane * 16));
+    sc_raw = (int)*reinterpret_cast<const uint32_t*>(p.s + (step >> 2) * kTileScaleBytes);
+  } else {
+    v = load_mx_operand(p.d + 128 * step, g);
+    sc_raw = (int)*reinterpret_cast<const uint32_t*>(p.s + 4 * step);
+  }
+}
+
+template <bool PACKED>
+__device__ __forceinline__ int weight_scale(int sc_raw, int step, int lane) {
+  if constexpr (PACKED)
+    return (int)((uint32_t)sc_raw >> (8 * (step & 3)));
+  else
+    return (int)((uint32_t)sc_raw >> (8 * (lane >> 4)));
+}
+
+// ---- token staging ------------------------------------------------------------------
+// LDS per buffer: NT tiles x {2 KB operand bytes (lo halves of the 64 lanes, then hi
+// halves), 256 B scale words (one per lane)}.
+template <int NT>
+struct Stage {
+  static constexpr int kBufBytes = NT * (kTileBytes + kTileScaleBytes);
+  static constexpr int kPerWave = (NT + 3) / 4;   // tiles loaded by each of 4 waves
+  u32x4 lo[kPerWave], hi[kPerWave];
+  int sc[kPerWave];
+};
+
+template <int NT>
+__device__ __forceinline__ void stage_load(Stage<NT>& st, const uint8_t* tok, const uint8_t* toks, int K, int row0,
+                                           int nrows, int ntt, int step, int wave, int lane) {
+  const int g = lane >> 4, r = lane & 15;
+  // Loads are unconditional (tile index clamped to the last valid tile, padding lanes
+  // re-read the last valid row), so the compiler can count them exactly and never has
+  // to drain the load queue at a branch join.
+#pragma unroll
+  for (int i = 0; i < Stage<NT>::kPerWave; ++i) {
+    const int t = min(wave + 4 * i, ntt - 1);
+    const int rr = min(16 * t + r, nrows - 1);
+    const uint8_t* row = tok + (int64_t)(row0 + rr) * K + 128 * step;
+    st.lo[i] = *reinterpret_cast<const u32x4*>(row + 16 * g);
+    st.hi[i] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * g);
+    st.sc[i] = (int)*reinterpret_cast<const uint32_t*>(toks + (int64_t)(row0 + rr) * (K >> 5) + 4 * step);
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_store(const Stage<NT>& st, uint8_t* buf, int ntt, int wave, int lane) {
+  // Slots are clamped like the loads: waves whose tile is past the chunk rewrite the
+  // last valid slot with the same bytes another wave stores there.
+#pragma unroll
+  for (int i = 0; i < Stage<NT>::kPerWave; ++i) {
+    const int t = min(wave + 4 * i, ntt - 1);
+    uint8_t* tile = buf + t * kTileBytes;
+    reinterpret_cast<u32x4*>(tile)[lane] = st.lo[i];
+    reinterpret_cast<u32x4*>(tile + 1024)[lane] = st.hi[i];
+    reinterpret_cast<int*>(buf + NT * kTileBytes + t * kTileScaleBytes)[lane] =
+        (int)((uint32_t)st.sc[i] >> (8 * (lane >> 4)));
+  }
+}
+
+template <int NT>
+__device__ __forceinline__ void stage_read(const uint8_t* buf, int t, int lane, v8i& v, int& sc) {
+  const uint8_t* tile = buf + t * kTileBytes;
+  v = join_operand(reinterpret_cast<const u32x4*>(tile)[lane], reinterpret_cast<const u32x4*>(tile + 1024)[lane]);
+  sc = reinterpret_cast<const int*>(buf + NT * kTileBytes + t * kTileScaleBytes)[lane];
+}
+
+// Persistent, XCD-aware item range of this block: [*lo, *hi) stepping by *stride.
+__device__ __forceinline__ void block_items(int total, int* first, int* stride, int* last) {
+  const int nb = gridDim.x;
+  const int xcd = blockIdx.x % kXcds;
+  const int per = nb / kXcds;
+  const int lo = (int)(((int64_t)total * xcd) / kXcds);
+  const int hi = (int)(((int64_t)total * (xcd + 1)) / kXcds);
+  *first = lo + blockIdx.x / kXcds;
+  *stride = per;
+  *last = hi;
+}
+
+// ---- the K loop shared by both GEMMs ---------------------------------------------
+// One K step: issue the global loads of the next token stage and of the weights two
+// steps ahead, run the MFMAs of this step from the registers and the LDS stage, then
+// store the next stage into the other LDS buffer and meet the barrier.
+// WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int PF>
+__device__ __forceinline__ void k_step(int s, int ks, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], Stage<NT>& st,
+                                       const v8i (&acur)[4], const int (&scur)[4], v8i (&aload)[4], int (&sload)[4],
+                                       const uint8_t* tok, const uint8_t* toks, int K, int row0, int nrows, int ntt,
+                                       uint8_t* lds, int wave, int lane) {
+  // Next stage and the weights PF steps ahead; past the last step the last step is
+  // re-read (in bounds, unused) so that every K step issues the same loads.
+  stage_load<NT>(st, tok, toks, K, row0, nrows, ntt, min(s + 1, ks - 1), wave, lane);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(s + PF, ks - 1), lane, aload[q], sload[q]);
+  const uint8_t* buf = lds + (s & 1) * Stage<NT>::kBufBytes;
+  int sw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) sw[q] = weight_scale<PACKED>(scur[q], s, lane);
+  auto tile_mfmas = [&](int t) {
+    v8i b;
+    int sb;
+    stage_read<NT>(buf, t, lane, b, sb);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (WEIGHTS_A)
+        acc[q][t] = mfma_mx16<FMT>(acur[q], b, acc[q][t], sw[q], sb);
+      else
+        acc[q][t] = mfma_mx16<FMT>(b, acur[q], acc[q][t], sb, sw[q]);
+    }
+  };
+#pragma unroll
+  for (int t = 0; t < NT; ++t)
+    if (t < ntt) tile_mfmas(t);
+  stage_store<NT>(st, lds + ((s + 1) & 1) * Stage<NT>::kBufBytes, ntt, wave, lane);
+  __syncthreads();
+}
+
+// Weight prefetch depth: two K steps ahead for small chunks (few MFMAs per step, the
+// loads need the lead), one step for large chunks (64 MFMAs per step already cover the
+// latency, and the third register buffer would not fit beside 256 accumulators).
+template <int NT> struct Prefetch { static constexpr int value = NT <= 4 ? 2 : 1; };
+
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+__device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+                                       const uint8_t* toks, int K, int row0, int nrows, int ntt, uint8_t* lds,
+                                       int wave, int lane) {
+  constexpr int PF = Prefetch<NT>::value;
+  const int ks = K >> 7;
+  Stage<NT> st;
+  v8i a0[4], a1[4], a2[4];
+  int s0[4], s1[4], s2[4];
+  stage_load<NT>(st, tok, toks, K, row0, nrows, ntt, 0, wave, lane);
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], 0, lane, a0[q], s0[q]);
+  if (PF == 2) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(1, ks - 1), lane, a1[q], s1[q]);
+  }
+  stage_store<NT>(st, lds, ntt, wave, lane);
+  __syncthreads();
+  if constexpr (PF == 2) {
+    for (int s = 0; s < ks; s += 3) {   // three register buffers rotate with the K step
+      k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt, lds,
+                                            wave, lane);
+      if (s + 1 < ks)
+        k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows, ntt,
+                                              lds, wave, lane);
+      if (s + 2 < ks)
+        k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s + 2, ks, acc, wp, st, a2, s2, a1, s1, tok, toks, K, row0, nrows, ntt,
+                                              lds, wave, lane);
+    }
+  } else {
+    for (int s = 0; s < ks; s += 2) {   // two register buffers alternate
+      k_step<FMT, NT, PACKED, WEIGHTS_A, 1>(s, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt, lds,
+                                            wave, lane);
+      if (s + 1 < ks)
+        k_step<FMT, NT, PACKED, WEIGHTS_A, 1>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows, ntt,
+                                              lds, wave, lane);
+    }
+  }
+  (void)a2; (void)s2;
+}
+
+// Occupancy targets: small token chunks (decode) want several waves per SIMD to keep
+// many weight loads in flight; 256-row chunks need the whole register file for 256
+// accumulators.
+template <int NT> struct WavesPerEU { static constexpr int value = NT <= 2 ? 2 : 1; };
+
+// ---- GMM1 + SwiGLU + MX requantization ------------------------------------------
+template <int FMT, int NT, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
+void gmm1_swiglu_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ sx, const uint8_t* __restrict__ w,
-    const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count,
-    int hidden, int inter, uint8_t* __restrict__ aq, uint8_t* __restrict__ sa, float* __restrict__ h1) {
+    const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
+    int inter, uint8_t* __restrict__ aq, uint8_t* __restrict__ sa, float* __restrict__ h1) {
+  extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int ncb = inter >> 7;
-  const int j = blockIdx.x / ncb, cb = blockIdx.x - j * ncb;
-  if (j >= *tile_count) return;
-  const int4 tile = tiles[j];
-  const int e = tile.x, row0 = tile.y, nrows = tile.z;
-  const int n0 = cb * 128 + wave * 32;
-  const int ks = hidden >> 7, hs = hidden >> 5;
-
-  const uint8_t* wrow[4];
-  const uint8_t* wsrow[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int ch = (q < 2 ? n0 + 16 * q : inter + n0 + 16 * (q - 2)) + r;
-    const int64_t wr = (int64_t)e * 2 * inter + ch;
-    wrow[q] = w + wr * hidden;
-    wsrow[q] = ws + wr * hs;
-  }
-  const uint8_t* xrow[TT];
-  const uint8_t* xsrow[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int rr = 16 * t + r;
-    const int64_t row = row0 + (rr < nrows ? rr : 0);  // padding lanes re-read a valid row
-    xrow[t] = xq + row * hidden;
-    xsrow[t] = sx + row * hs;
-  }
-
-  v4f acc[4][TT];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  v8i a_cur[4], b_cur[TT];
-  int sa_cur[4], sb_cur[TT];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { a_cur[q] = load_mx_operand(wrow[q], g); sa_cur[q] = scale_arg(wsrow[q], 0, g); }
-#pragma unroll
-  for (int t = 0; t < TT; ++t) { b_cur[t] = load_mx_operand(xrow[t], g); sb_cur[t] = scale_arg(xsrow[t], 0, g); }
-
-  for (int s = 0; s < ks; ++s) {
-    v8i a_nxt[4], b_nxt[TT];
-    int sa_nxt[4], sb_nxt[TT];
-    const int sn = s + 1 < ks ? s + 1 : s;
+  const int ncb = inter >> 7;                 // 128 gate channels per block
+  const int n16 = (2 * inter) >> 4;            // 16-channel tiles per expert
+  int it, stride, last;
+  block_items(*tile_count * ncb, &it, &stride, &last);
+  for (; it < last; it += stride) {
+    const int j = it / ncb, cb = it - j * ncb;
+    const int4 tile = tiles[j];
+    const int e = tile.x, row0 = tile.y, nrows = tile.z;
+    const int ntt = (nrows + 15) >> 4;
+    const int n0 = cb * 128 + wave * 32;       // first gate channel of this wave
+    WPtr<PACKED> wp[4];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      a_nxt[q] = load_mx_operand(wrow[q] + 128 * sn, g);
-      sa_nxt[q] = scale_arg(wsrow[q], sn, g);
+      const int ct = (q < 2 ? n0 : inter + n0 - 32) / 16 + q;   // q = 0,1 gate; 2,3 up
+      wp[q] = weight_tile<PACKED>(w, ws, (int64_t)e * n16 + ct, hidden, lane);
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      b_nxt[t] = load_mx_operand(xrow[t] + 128 * sn, g);
-      sb_nxt[t] = scale_arg(xsrow[t], sn, g);
-    }
+    v4f acc[4][NT];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < TT; ++t) acc[q][t] = mfma_mx16<FMT>(a_cur[q], b_cur[t], acc[q][t], sa_cur[q], sb_cur[t]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { a_cur[q] = a_nxt[q]; sa_cur[q] = sa_nxt[q]; }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) { b_cur[t] = b_nxt[t]; sb_cur[t] = sb_nxt[t]; }
-  }
+      for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    k_loop<FMT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, nrows, ntt, lds, wave, lane);
 
-  const int is = inter >> 5;
+    const int is = inter >> 5;
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int rr = 16 * t + r;
-    const bool valid = rr < nrows;
-    const int64_t row = row0 + rr;
-    float act[2][4];
-    int m = 0;
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntt) continue;                   // uniform per wave
+      const int rr = 16 * t + r;
+      const bool valid = rr < nrows;
+      const int64_t row = row0 + rr;
+      float act[2][4];
+      int m = 0;
 #pragma unroll
-    for (int jj = 0; jj < 2; ++jj)
+      for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float gv = acc[jj][t][i], uv = acc[2 + jj][t][i];
-        const float a = gv / (1.0f + expf(-gv)) * uv;
-        act[jj][i] = a;
-        m = max(m, __float_as_int(fabsf(a)));
-      }
-    m = max(m, __shfl_xor(m, 16));
-    m = max(m, __shfl_xor(m, 32));
-    const int b = mx_scale_byte<FMT>(__int_as_float(m));
-    const float inv = mx_inv_scale(b);
-    if (valid) {
+        for (int i = 0; i < 4; ++i) {
+          const float gv = acc[jj][t][i], uv = acc[2 + jj][t][i];
+          const float a = gv / (1.0f + expf(-gv)) * uv;
+          act[jj][i] = a;
+          m = max(m, __float_as_int(fabsf(a)));
+        }
+      m = max(m, __shfl_xor(m, 16));
+      m = max(m, __shfl_xor(m, 32));
+      const int b = mx_scale_byte<FMT>(__int_as_float(m));
+      const float inv = mx_inv_scale(b);
+      if (valid) {
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const uint32_t codes = pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
-        *reinterpret_cast<uint32_t*>(aq + row * inter + n0 + 16 * jj + 4 * g) = codes;
-      }
-      if (g == 0) sa[row * is + (n0 >> 5)] = (uint8_t)b;
-      if (h1) {
+        for (int jj = 0; jj < 2; ++jj) {
+          const uint32_t codes =
+              pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
+          *reinterpret_cast<uint32_t*>(aq + row * inter + n0 + 16 * jj + 4 * g) = codes;
+        }
+        if (g == 0) sa[row * is + (n0 >> 5)] = (uint8_t)b;
+        if (h1) {
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj)
+          for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ch = n0 + 16 * jj + 4 * g + i;
-            h1[row * 2 * inter + ch] = acc[jj][t][i];
-            h1[row * 2 * inter + inter + ch] = acc[2 + jj][t][i];
-          }
+            for (int i = 0; i < 4; ++i) {
+              const int ch = n0 + 16 * jj + 4 * g + i;
+              h1[row * 2 * inter + ch] = acc[jj][t][i];
+              h1[row * 2 * inter + inter + ch] = acc[2 + jj][t][i];
+            }
+        }
       }
     }
   }
 }
 
-template <int FMT, int TT>
-__global__ __launch_bounds__(256) void gmm2_combine_kernel(
+// ---- GMM2 + weighted combine -------------------------------------------------------
+template <int FMT, int NT, bool PACKED>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
+void gmm2_combine_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
-    const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count,
-    int hidden, int inter, const int32_t* __restrict__ row_token, const float* __restrict__ row_weight,
+    const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
+    int inter, const int32_t* __restrict__ row_token, const float* __restrict__ row_weight,
     float* __restrict__ y_accum, float* __restrict__ o) {
+  extern __shared__ __align__(16) uint8_t lds[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int nwaves = blockDim.x >> 6;
   const int g = lane >> 4, r = lane & 15;
-  const int ncb = hidden / (64 * nwaves);
-  const int j = blockIdx.x / ncb, cb = blockIdx.x - j * ncb;
-  if (j >= *tile_count) return;
-  const int4 tile = tiles[j];
-  const int e = tile.x, row0 = tile.y, nrows = tile.z;
-  const int c0 = (cb * nwaves + wave) * 64;
-  const int ks = inter >> 7, is = inter >> 5;
-
-  const uint8_t* wrow[4];
-  const uint8_t* wsrow[4];
+  const int ncb = (hidden + 255) >> 8;        // 256 channels per block (64 per wave)
+  const int n16 = hidden >> 4;
+  int it, stride, last;
+  block_items(*tile_count * ncb, &it, &stride, &last);
+  for (; it < last; it += stride) {
+    const int j = it / ncb, cb = it - j * ncb;
+    const int4 tile = tiles[j];
+    const int e = tile.x, row0 = tile.y, nrows = tile.z;
+    const int ntt = (nrows + 15) >> 4;
+    const int c0 = cb * 256 + wave * 64;
+    // hidden % 256 == 128: the last block's upper waves have no channels; they still
+    // stage tokens and meet the barriers, reading a valid tile, and skip the epilogue.
+    const bool wave_on = c0 < hidden;
+    const int c0w = wave_on ? c0 : 0;
+    WPtr<PACKED> wp[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t wr = (int64_t)e * hidden + c0 + 16 * q + r;
-    wrow[q] = w + wr * inter;
-    wsrow[q] = ws + wr * is;
-  }
-  const uint8_t* arow[TT];
-  const uint8_t* asrow[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int rr = 16 * t + r;
-    const int64_t row = row0 + (rr < nrows ? rr : 0);
-    arow[t] = aq + row * inter;
-    asrow[t] = sa + row * is;
-  }
-
-  v4f acc[4][TT];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int t = 0; t < TT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-
-  v8i a_cur[4], b_cur[TT];
-  int sa_cur[4], sb_cur[TT];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) { a_cur[q] = load_mx_operand(wrow[q], g); sa_cur[q] = scale_arg(wsrow[q], 0, g); }
-#pragma unroll
-  for (int t = 0; t < TT; ++t) { b_cur[t] = load_mx_operand(arow[t], g); sb_cur[t] = scale_arg(asrow[t], 0, g); }
-
-  for (int s = 0; s < ks; ++s) {
-    v8i a_nxt[4], b_nxt[TT];
-    int sa_nxt[4], sb_nxt[TT];
-    const int sn = s + 1 < ks ? s + 1 : s;
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      a_nxt[q] = load_mx_operand(wrow[q] + 128 * sn, g);
-      sa_nxt[q] = scale_arg(wsrow[q], sn, g);
-    }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      b_nxt[t] = load_mx_operand(arow[t] + 128 * sn, g);
-      sb_nxt[t] = scale_arg(asrow[t], sn, g);
-    }
+    for (int q = 0; q < 4; ++q) wp[q] = weight_tile<PACKED>(w, ws, (int64_t)e * n16 + (c0w >> 4) + q, inter, lane);
+    v4f acc[4][NT];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
-      for (int t = 0; t < TT; ++t) acc[q][t] = mfma_mx16<FMT>(a_cur[q], b_cur[t], acc[q][t], sa_cur[q], sb_cur[t]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) { a_cur[q] = a_nxt[q]; sa_cur[q] = sa_nxt[q]; }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) { b_cur[t] = b_nxt[t]; sb_cur[t] = sb_nxt[t]; }
-  }
+      for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
+    k_loop<FMT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, nrows, ntt, lds, wave, lane);
 
+    // acc[q][t][i] = O[token row 16t + 4g + i][channel c0 + 16q + r]
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const int rr = 16 * t + r;
-    if (rr >= nrows) continue;
-    const int64_t row = row0 + rr;
-    const int64_t tok = row_token ? (int64_t)row_token[row] : row;
-    const float wgt = row_token ? row_weight[row] : 1.0f;
-    float* yrow = y_accum + tok * hidden;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int t = 0; t < NT; ++t) {
+      if (t >= ntt || !wave_on) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int ch = c0 + 16 * q + 4 * g + i;
-        unsafeAtomicAdd(yrow + ch, wgt * acc[q][t][i]);
-        if (o) o[row * hidden + ch] = acc[q][t][i];
+        const int rr = 16 * t + 4 * g + i;
+        if (rr >= nrows) continue;
+        const int64_t row = row0 + rr;
+        const int64_t tok = row_token ? (int64_t)row_token[row] : row;
+        const float wgt = row_token ? row_weight[row] : 1.0f;
+        float* yrow = y_accum + tok * hidden + c0 + r;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          unsafeAtomicAdd(yrow + 16 * q, wgt * acc[q][t][i]);
+          if (o) o[row * hidden + c0 + 16 * q + r] = acc[q][t][i];
+        }
       }
+    }
+  }
+}
+
+// ---- packing of weights into the MFMA-native layout -----------------------------
+// codes [G, N, K] -> packed [G][N/16][K/128][2][64][16 B]: tile (g, n16, s), half h, lane l
+// holds row n16*16 + l%16, K bytes [128 s + 64 h + 16 (l/16), +16).
+// scales [G, N, K/32] -> packed [G][N/16][ceil(K/512)][64][4 B]: byte j of lane l = the
+// scale of row n16*16 + l%16, K block 4 (4 q + j) + l/16 (0 beyond the last K step).
+__global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, uint8_t* __restrict__ packed, int64_t pieces,
+                                  int N, int K) {
+  const int ks = K >> 7;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(p & 63);
+    const int h = (int)((p >> 6) & 1);
+    const int64_t blk = p >> 7;                 // (g * N/16 + n16) * ks + s
+    const int s = (int)(blk % ks);
+    const int64_t tile = blk / ks;              // g * N/16 + n16
+    const int64_t row = tile * 16 + (l & 15);   // flat row over [G * N]
+    const u32x4 v = *reinterpret_cast<const u32x4*>(codes + row * K + 128 * s + 64 * h + 16 * (l >> 4));
+    reinterpret_cast<u32x4*>(packed)[p] = v;
+  }
+}
+
+__global__ void pack_scales_kernel(const uint8_t* __restrict__ scales, uint32_t* __restrict__ packed, int64_t words,
+                                   int N, int K) {
+  const int ks = K >> 7, kq = (ks + 3) >> 2, kb = K >> 5;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < words; p += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(p & 63);
+    const int64_t blk = p >> 6;                 // (g * N/16 + n16) * kq + q
+    const int q = (int)(blk % kq);
+    const int64_t tile = blk / kq;
+    const int64_t row = tile * 16 + (l & 15);
+    uint32_t word = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int s = 4 * q + j;
+      if (s < ks) word |= (uint32_t)scales[row * kb + 4 * s + (l >> 4)] << (8 * j);
+    }
+    packed[p] = word;
   }
 }
 
@@ -268,41 +452,114 @@ __global__ void finalize_kernel(const float* __restrict__ acc, int64_t n, uint16
     y[i] = f_to_bf16(acc[i]);
 }
 
-template <int FMT, int TT>
-void gmm1_go(const Gmm1Params& p, hipStream_t st) {
-  const unsigned grid = (unsigned)p.max_tiles * (unsigned)(p.inter >> 7);
-  gmm1_swiglu_kernel<FMT, TT><<<grid, 256, 0, st>>>(p.xq, p.sx, p.w, p.ws, p.tiles, p.tile_count, p.hidden,
-                                                    p.inter, p.aq, p.sa, p.h1);
+// ---- launch helpers: persistent grid = CUs x resident blocks per CU (multiple of 8) --
+struct LaunchShape {
+  int grid = 0;
+  size_t lds = 0;
+};
+
+template <typename K>
+hipError_t persistent_shape(K kernel, size_t lds, LaunchShape* out) {
+  static std::mutex mu;
+  static std::map<const void*, int> cache;
+  std::lock_guard<std::mutex> lock(mu);
+  const void* key = reinterpret_cast<const void*>(kernel);
+  auto itc = cache.find(key);
+  int grid;
+  if (itc == cache.end()) {
+    hipError_t e = hipFuncSetAttribute(key, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    int dev = 0, cus = 0, per_cu = 0;
+    if ((e = hipGetDevice(&dev)) != hipSuccess) return e;
+    if ((e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev)) != hipSuccess) return e;
+    if ((e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, 256, lds)) != hipSuccess) return e;
+    if (per_cu < 1) per_cu = 1;
+    grid = cus * per_cu;
+    grid = ((grid + kXcds - 1) / kXcds) * kXcds;
+    cache[key] = grid;
+  } else {
+    grid = itc->second;
+  }
+  out->grid = grid;
+  out->lds = lds;
+  return hipSuccess;
 }
 
-template <int FMT, int TT>
-void gmm2_go(const Gmm2Params& p, hipStream_t st) {
-  const int nwaves = (p.hidden % 256 == 0) ? 4 : 2;
-  const unsigned grid = (unsigned)p.max_tiles * (unsigned)(p.hidden / (64 * nwaves));
-  gmm2_combine_kernel<FMT, TT><<<grid, 64 * nwaves, 0, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count,
-                                                             p.hidden, p.inter, p.row_token, p.row_weight,
-                                                             p.y_accum, p.o);
+template <int FMT, int NT, bool PACKED>
+hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
+  auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED>;
+  LaunchShape ls;
+  hipError_t e = persistent_shape(kern, 2 * Stage<NT>::kBufBytes, &ls);
+  if (e != hipSuccess) return e;
+  kern<<<ls.grid, 256, ls.lds, st>>>(p.xq, p.sx, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.aq, p.sa,
+                                     p.h1);
+  return hipGetLastError();
+}
+
+template <int FMT, int NT, bool PACKED>
+hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
+  auto kern = gmm2_combine_kernel<FMT, NT, PACKED>;
+  LaunchShape ls;
+  hipError_t e = persistent_shape(kern, 2 * Stage<NT>::kBufBytes, &ls);
+  if (e != hipSuccess) return e;
+  kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.row_token,
+                                     p.row_weight, p.y_accum, p.o);
+  return hipGetLastError();
+}
+
+template <int FMT, bool PACKED>
+hipError_t gmm1_nt(const Gmm1Params& p, hipStream_t st) {
+  switch (p.tt) {
+    case 1: return gmm1_go<FMT, 1, PACKED>(p, st);
+    case 2: return gmm1_go<FMT, 2, PACKED>(p, st);
+    case 4: return gmm1_go<FMT, 4, PACKED>(p, st);
+    case 8: return gmm1_go<FMT, 8, PACKED>(p, st);
+    default: return gmm1_go<FMT, 16, PACKED>(p, st);
+  }
+}
+
+template <int FMT, bool PACKED>
+hipError_t gmm2_nt(const Gmm2Params& p, hipStream_t st) {
+  switch (p.tt) {
+    case 1: return gmm2_go<FMT, 1, PACKED>(p, st);
+    case 2: return gmm2_go<FMT, 2, PACKED>(p, st);
+    case 4: return gmm2_go<FMT, 4, PACKED>(p, st);
+    case 8: return gmm2_go<FMT, 8, PACKED>(p, st);
+    default: return gmm2_go<FMT, 16, PACKED>(p, st);
+  }
 }
 
 }  // namespace
 
+int gmm_token_tiles(int64_t rows, int64_t groups) {
+  const double avg = groups > 0 ? (double)rows / (double)groups : (double)rows;
+  if (avg <= 16.0) return 1;
+  if (avg <= 32.0) return 2;
+  if (avg <= 64.0) return 4;
+  if (avg <= 128.0) return 8;
+  return 16;
+}
+
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t st) {
-  if (p.max_tiles <= 0) return hipSuccess;
-  if (p.fmt == 0) {
-    if (p.tt == 1) gmm1_go<0, 1>(p, st); else if (p.tt == 2) gmm1_go<0, 2>(p, st); else gmm1_go<0, 4>(p, st);
-  } else {
-    if (p.tt == 1) gmm1_go<1, 1>(p, st); else if (p.tt == 2) gmm1_go<1, 2>(p, st); else gmm1_go<1, 4>(p, st);
-  }
-  return hipGetLastError();
+  if (p.fmt == 0) return p.packed ? gmm1_nt<0, true>(p, st) : gmm1_nt<0, false>(p, st);
+  return p.packed ? gmm1_nt<1, true>(p, st) : gmm1_nt<1, false>(p, st);
 }
 
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t st) {
-  if (p.max_tiles <= 0) return hipSuccess;
-  if (p.fmt == 0) {
-    if (p.tt == 1) gmm2_go<0, 1>(p, st); else if (p.tt == 2) gmm2_go<0, 2>(p, st); else gmm2_go<0, 4>(p, st);
-  } else {
-    if (p.tt == 1) gmm2_go<1, 1>(p, st); else if (p.tt == 2) gmm2_go<1, 2>(p, st); else gmm2_go<1, 4>(p, st);
-  }
+  if (p.fmt == 0) return p.packed ? gmm2_nt<0, true>(p, st) : gmm2_nt<0, false>(p, st);
+  return p.packed ? gmm2_nt<1, true>(p, st) : gmm2_nt<1, false>(p, st);
+}
+
+hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                               uint8_t* packed, uint8_t* packed_scales, hipStream_t st) {
+  const int64_t pieces = groups * n * k / 16;
+  const int64_t words = groups * (n / 16) * (((k >> 7) + 3) >> 2) * 64;
+  int64_t b1 = std::min<int64_t>((pieces + 255) / 256, 65536), b2 = std::min<int64_t>((words + 255) / 256, 65536);
+  if (b1 < 1) b1 = 1;
+  if (b2 < 1) b2 = 1;
+  pack_codes_kernel<<<(unsigned)b1, 256, 0, st>>>(codes, packed, pieces, (int)n, (int)k);
+  pack_scales_kernel<<<(unsigned)b2, 256, 0, st>>>(scales, reinterpret_cast<uint32_t*>(packed_scales), words, (int)n,
+                                                   (int)k);
   return hipGetLastError();
 }
 

@@ -64,9 +64,10 @@ struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // [rows, H], [rows, H/32]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
   const int4* tiles; const int* tile_count; int max_tiles;
-  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per wave
+  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16)
   uint8_t* aq; uint8_t* sa;                    // [rows, I], [rows, I/32]
   float* h1;                                   // nullable [rows, 2I]
+  int packed;                                  // weights in the MFMA-native packed layout
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 
@@ -79,8 +80,17 @@ struct Gmm2Params {
   const float* row_weight;
   float* y_accum;                              // [tokens, H]
   float* o;                                    // nullable [rows, H]
+  int packed;
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
+
+// Token tiles (16 rows each) per chunk for `rows` rows over `groups` groups.
+int gmm_token_tiles(int64_t rows, int64_t groups);
+
+// codes [G, N, K] + scales [G, N, K/32] -> MFMA-native packed codes (same size) and
+// packed scales [G, N/16, ceil(K/512), 64, 4].
+hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                               uint8_t* packed, uint8_t* packed_scales, hipStream_t stream);
 
 // Tiles of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), 0}.
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);

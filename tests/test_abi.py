@@ -133,6 +133,7 @@ def test_mega_moe_validation(lib):
     assert status(num_shared=5) == 2
     assert status(num_shared=1) == 1   # shared weights missing
     assert status(w2=None) == 1
+    assert status(weight_format=2) == 1
     a = args()
     assert lib.mega_moe(ctypes.byref(a), FAKE, 16, None) == 5
     assert "bytes required" in lib.moe_last_error().decode()

@@ -37,15 +37,28 @@ CASES = [
 ]
 
 
+def device_weights(wq, ws, wf):
+    """Oracle-quantized ND weights on the GPU, packed by the library when wf is PACKED."""
+    q, s = to_dev(wq), to_dev(ws)
+    if wf == rp.WEIGHTS_PACKED:
+        return rp.pack_weights(q, s)
+    return q, s
+
+
+WF = [rp.WEIGHTS_ND, rp.WEIGHTS_PACKED]
+
+
+@pytest.mark.parametrize("wf", WF, ids=["nd", "packed"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c['name']}-{c.get('tokens', '')}")
-def test_gmm1_swiglu_quant(case):
+def test_gmm1_swiglu_quant(case, wf):
     case = dict(case)
     cfg = moe_inputs.config(case.pop("name"), **case)
     say(f"gmm1 N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} fmt={cfg.fmt}")
     ids, x, r, xq, sx = grouped_operands(cfg)
     w1q, w1s, w2q, w2s = oracle_weights(cfg)
     offs = to_dev(r["offsets"].astype(np.int32))
-    aq, sa, h1 = rp.gmm1_swiglu_quant(to_dev(xq), to_dev(sx), offs, to_dev(w1q), to_dev(w1s), FP8[cfg.fmt], True)
+    dw, dws = device_weights(w1q, w1s, wf)
+    aq, sa, h1 = rp.gmm1_swiglu_quant(to_dev(xq), to_dev(sx), offs, dw, dws, FP8[cfg.fmt], True, weight_format=wf)
     torch.cuda.synchronize()
     h1_ref = np.zeros((xq.shape[0], 2 * cfg.inter))
     h1_abs = np.zeros_like(h1_ref)
@@ -65,8 +78,9 @@ def test_gmm1_swiglu_quant(case):
     say(f"  requant: codes differing from the oracle {codes:.3g}, scales {scales:.3g}")
 
 
+@pytest.mark.parametrize("wf", WF, ids=["nd", "packed"])
 @pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
-def test_gmm1_requant_exact_regime(fmt):
+def test_gmm1_requant_exact_regime(fmt, wf):
     """Integer-valued operands: every fp32 sum is exact whatever its order, G >= 256 so
     1 + exp(-G) rounds to 1 and A = G*U exactly on both sides -> bit-exact requant."""
     say(f"gmm1 exact regime fmt={fmt}")
@@ -80,7 +94,8 @@ def test_gmm1_requant_exact_regime(fmt):
     w1q[:, inter:] = rng.choice([0, one, two, one | 0x80, two | 0x80, 0, 0, 0], size=(groups, inter, h))
     w1s = np.full((groups, 2 * inter, h // 32), 127, np.uint8)
     offs = np.array([0, 10, 10, 41, 90, 93], np.int32)
-    aq, sa, h1 = rp.gmm1_swiglu_quant(to_dev(xq), to_dev(sx), to_dev(offs), to_dev(w1q), to_dev(w1s), FP8[fmt], True)
+    dw, dws = device_weights(w1q, w1s, wf)
+    aq, sa, h1 = rp.gmm1_swiglu_quant(to_dev(xq), to_dev(sx), to_dev(offs), dw, dws, FP8[fmt], True, weight_format=wf)
     torch.cuda.synchronize()
     h1_ref = np.zeros((rows, 2 * inter))
     for e in range(groups):
@@ -96,8 +111,9 @@ def test_gmm1_requant_exact_regime(fmt):
     assert np.array_equal(aq.cpu().numpy(), aq_o)
 
 
+@pytest.mark.parametrize("wf", WF, ids=["nd", "packed"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"{c['name']}-{c.get('tokens', '')}")
-def test_gmm2_combine(case):
+def test_gmm2_combine(case, wf):
     case = dict(case)
     cfg = moe_inputs.config(case.pop("name"), **case)
     say(f"gmm2 N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} fmt={cfg.fmt}")
@@ -110,8 +126,9 @@ def test_gmm2_combine(case):
     row_token = (srt // cfg.topk).astype(np.int32)
     row_weight = w.reshape(-1)[srt].astype(np.float32)
     y_acc = torch.zeros((cfg.tokens, cfg.hidden), dtype=torch.float32, device=DEV)
-    o = rp.gmm2_combine(to_dev(aq_o), to_dev(sa_o), to_dev(r["offsets"].astype(np.int32)), to_dev(weights[2]),
-                        to_dev(weights[3]), to_dev(row_token), to_dev(row_weight), y_acc, FP8[cfg.fmt], True)
+    dw, dws = device_weights(weights[2], weights[3], wf)
+    o = rp.gmm2_combine(to_dev(aq_o), to_dev(sa_o), to_dev(r["offsets"].astype(np.int32)), dw, dws,
+                        to_dev(row_token), to_dev(row_weight), y_acc, FP8[cfg.fmt], True, weight_format=wf)
     y = rp.combine_finalize(y_acc)
     torch.cuda.synchronize()
     o_got = o.cpu().numpy()
@@ -127,3 +144,30 @@ def test_gmm2_combine(case):
     mx, mean = y_errors(y.cpu().double().numpy(), full["y"])
     say(f"  Y max err {mx:.3g} mean rel {mean:.3g}")
     assert mx <= 2e-2 and mean <= 5e-3
+
+
+def packed_reference(codes, scales):
+    """The packed layout of include/moe_mx.h re-stated with numpy index arithmetic."""
+    g, n, k = codes.shape
+    ks, kq = k // 128, (k // 128 + 3) // 4
+    c = codes.reshape(g, n // 16, 16, ks, 2, 4, 16)          # (g, tile, r, s, h, lanegroup, byte)
+    pc = c.transpose(0, 1, 3, 4, 5, 2, 6).reshape(-1)         # (g, tile, s, h, lanegroup, r, byte)
+    sc = np.zeros((g, n // 16, kq, 4, 16, 4), np.uint8)       # (g, tile, q, lanegroup, r, j)
+    sv = scales.reshape(g, n // 16, 16, ks, 4)                # (g, tile, r, s, block g)
+    for s_ in range(ks):
+        sc[:, :, s_ // 4, :, :, s_ % 4] = sv[:, :, :, s_, :].transpose(0, 1, 3, 2)
+    return pc, sc.reshape(-1)
+
+
+@pytest.mark.parametrize("shape", [(2, 32, 256), (3, 48, 640), (1, 16, 128)])
+def test_pack_weights_layout(shape):
+    say(f"pack_weights {shape}")
+    rng = np.random.default_rng(sum(shape))
+    g, n, k = shape
+    codes = rng.integers(0, 256, size=shape).astype(np.uint8)
+    scales = rng.integers(0, 255, size=(g, n, k // 32)).astype(np.uint8)
+    pc, ps = rp.pack_weights(to_dev(codes), to_dev(scales))
+    torch.cuda.synchronize()
+    rc, rs = packed_reference(codes, scales)
+    assert np.array_equal(pc.cpu().numpy().reshape(-1), rc)
+    assert np.array_equal(ps.cpu().numpy(), rs)

@@ -29,9 +29,17 @@ SMALL = [
 ]
 
 
+def device_weights(arrays, wf):
+    d = [to_dev(a) for a in arrays]
+    if wf == rp.WEIGHTS_PACKED:
+        return [*rp.pack_weights(d[0], d[1]), *rp.pack_weights(d[2], d[3])]
+    return d
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['name']}-{c.get('tokens', '')}-{c.get('shared', 0)}")
-@pytest.mark.parametrize("wdtype", [torch.float32, torch.bfloat16])
-def test_small_layers(case, wdtype):
+@pytest.mark.parametrize("wdtype,wf", [(torch.float32, rp.WEIGHTS_ND), (torch.bfloat16, rp.WEIGHTS_PACKED),
+                                       (torch.float32, rp.WEIGHTS_PACKED)], ids=["fp32-nd", "bf16-packed", "fp32-packed"])
+def test_small_layers(case, wdtype, wf):
     case = dict(case)
     cfg = moe_inputs.config(case.pop("name"), **case)
     say(f"mega_moe N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} S={cfg.shared} "
@@ -48,9 +56,10 @@ def test_small_layers(case, wdtype):
     if cfg.shared:
         sh = oracle_weights(cfg, cfg.shared, shared=True)
         shared_np = [tuple(a[s] for a in sh) for s in range(cfg.shared)]
-        shared = tuple(to_dev(a) for a in sh)
+        shared = tuple(device_weights(sh, wf))
     y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), w_t.to(DEV),
-                              *[to_dev(a) for a in weights], shared=shared, quant_out_dtype=FP8[cfg.fmt], debug=True)
+                              *device_weights(weights, wf), shared=shared, quant_out_dtype=FP8[cfg.fmt], debug=True,
+                              weight_format=wf)
     torch.cuda.synchronize()
     ref = moe.mega_moe(x, ids, w_used, weights, cfg.fmt, cfg.experts, shared=shared_np)
     assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
@@ -111,7 +120,7 @@ def test_repeated_calls_reuse_workspace():
     assert d <= 2e-2 * y1.float().abs().max().item()
 
 
-def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True):
+def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True, wf=rp.WEIGHTS_ND):
     cfg = moe_inputs.config(name)
     say(f"mega_moe full size {name}: N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} "
         f"S={cfg.shared} fmt={cfg.fmt}")
@@ -121,8 +130,14 @@ def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True):
     weights = library_weights(cfg)
     shared = library_weights(cfg, cfg.shared, shared=True) if cfg.shared else None
     say("  weights ready")
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *weights, shared=shared,
-                              quant_out_dtype=FP8[cfg.fmt], debug=True)
+    dev_w = list(weights)
+    dev_sh = shared
+    if wf == rp.WEIGHTS_PACKED:
+        dev_w = [*rp.pack_weights(weights[0], weights[1]), *rp.pack_weights(weights[2], weights[3])]
+        if shared is not None:
+            dev_sh = (*rp.pack_weights(shared[0], shared[1]), *rp.pack_weights(shared[2], shared[3]))
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w, shared=dev_sh,
+                              quant_out_dtype=FP8[cfg.fmt], debug=True, weight_format=wf)
     torch.cuda.synchronize()
     say("  layer done")
     r = routing.init_routing(ids, cfg.experts)
@@ -182,7 +197,7 @@ def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True):
 
 @pytest.mark.timeout(900)
 def test_full_size_decode():
-    full_size_check("decode", n_tokens_sampled=4)
+    full_size_check("decode", n_tokens_sampled=4, wf=rp.WEIGHTS_PACKED)
 
 
 @pytest.mark.timeout(900)
@@ -192,4 +207,4 @@ def test_full_size_skewed():
 
 @pytest.mark.timeout(900)
 def test_full_size_prefill():
-    full_size_check("prefill", n_tokens_sampled=3)
+    full_size_check("prefill", n_tokens_sampled=3, wf=rp.WEIGHTS_PACKED)

@@ -274,10 +274,14 @@ moe_status mega_moe(const moe_mega_args* args /* host */, void* workspace, size_
 /*   o             device out, fp32 [rows, hidden] unweighted O, or NULL        */
 /* moe_combine_finalize: y (bf16 [num_tokens, hidden]) = RNE(y_accum).         */
 /* Limits as in mega_moe; fp8 = quant_out_dtype (23/24); weights in           */
-/* weight_format. Workspace:                                                    */
-/* moe_gmm_workspace_size.                                                     */
+/* weight_format. Workspace: moe_gmm_workspace_size (the same for both, given  */
+/* rows, num_groups, hidden and inter; it holds the chunk list and the token   */
+/* operands restaged into the kernels' tiled layout, each group padded to 16  */
+/* rows: (rows + 15 * min(rows, num_groups)) * (max(hidden, inter) + inter)   */
+/* bytes of codes plus 1/32 of that for scales, roughly).                      */
 /* ------------------------------------------------------------------------ */
-moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, size_t* bytes /* host out */);
+moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, int64_t hidden, int64_t inter,
+                                  size_t* bytes /* host out */);
 moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t rows, int64_t hidden,
                                  int64_t inter, const int32_t* group_offsets, int64_t num_groups,
                                  const uint8_t* w1, const uint8_t* w1_scales, int weight_format, int quant_out_dtype,

@@ -83,7 +83,7 @@ _SIGS = {
                            _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
     "mega_moe_workspace_size": ([ctypes.POINTER(MegaArgs), ctypes.POINTER(_SZ)], _INT),
     "mega_moe": ([ctypes.POINTER(MegaArgs), _VP, _SZ, _VP], _INT),
-    "moe_gmm_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
+    "moe_gmm_workspace_size": ([_I64, _I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_gmm1_swiglu_quant": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _INT, _VP, _VP, _VP,
                                _VP, _SZ, _VP], _INT),
     "moe_gmm2_combine": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _INT, _VP, _VP, _I64, _VP,
@@ -323,7 +323,7 @@ def gmm1_swiglu_quant(xq, sx, group_offsets, w1, w1_scales, quant_out_dtype: int
     sa = torch.empty((rows, inter // 32), dtype=torch.uint8, device=dev)
     h1 = torch.empty((rows, two_i), dtype=torch.float32, device=dev) if want_h1 else None
     nbytes = ctypes.c_size_t()
-    _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
+    _check(lib.moe_gmm_workspace_size(rows, g, h, inter, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
     _check(lib.moe_gmm1_swiglu_quant(_ptr(xq), _ptr(sx), rows, h, inter, _ptr(group_offsets), g, _ptr(w1),
                                      _ptr(w1_scales), weight_format, quant_out_dtype, _ptr(aq), _ptr(sa), _ptr(h1),
@@ -342,7 +342,7 @@ def gmm2_combine(aq, sa, group_offsets, w2, w2_scales, row_token, row_weight, y_
     dev = aq.device
     o = torch.empty((rows, h), dtype=torch.float32, device=dev) if want_o else None
     nbytes = ctypes.c_size_t()
-    _check(lib.moe_gmm_workspace_size(rows, g, ctypes.byref(nbytes)))
+    _check(lib.moe_gmm_workspace_size(rows, g, h, inter, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
     _check(lib.moe_gmm2_combine(_ptr(aq), _ptr(sa), rows, inter, h, _ptr(group_offsets), g, _ptr(w2),
                                 _ptr(w2_scales), weight_format, quant_out_dtype, _ptr(row_token), _ptr(row_weight),

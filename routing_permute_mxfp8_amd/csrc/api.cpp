@@ -11,7 +11,7 @@
 #include <cstdio>
 #include <string>
 
-#include "../../include/moe_mx.h"
+#include "moe_mx.h"
 #include "internal.h"
 
 namespace {
@@ -124,12 +124,14 @@ struct MegaWs {
   int4* sh_tiles;
   int* sh_count;
   int sh_max_tiles, sh_tt;
+  // token operands in the tiled layout: routed rows (padded per expert) and the
+  // token-order rows of the shared experts
   uint8_t* xq;
   uint8_t* sx;
-  uint8_t* xq_tok;
-  uint8_t* sx_tok;
   uint8_t* aq;
   uint8_t* sa;
+  uint8_t* xq_sh;
+  uint8_t* sx_sh;
   uint8_t* aq_sh;
   uint8_t* sa_sh;
   float* y_acc;
@@ -148,19 +150,21 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.tile_count = cv.take<int>(1);
-  w.xq = a->xq ? nullptr : cv.take<uint8_t>((size_t)flat * h);
-  w.sx = a->sx ? nullptr : cv.take<uint8_t>((size_t)flat * (h / 32));
-  w.aq = a->aq ? nullptr : cv.take<uint8_t>((size_t)flat * i);
-  w.sa = a->sa ? nullptr : cv.take<uint8_t>((size_t)flat * (i / 32));
+  const int64_t padded = moe::t16_padded_rows(flat, e);
+  w.xq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, h));
+  w.sx = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, h));
+  w.aq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, i));
+  w.sa = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, i));
   if (a->num_shared > 0) {
     w.sh_tt = token_tile_tt(n, 1);
     w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
     w.sh_tiles = cv.take<int4>(w.sh_max_tiles);
     w.sh_count = cv.take<int>(1);
-    w.xq_tok = cv.take<uint8_t>((size_t)n * h);
-    w.sx_tok = cv.take<uint8_t>((size_t)n * (h / 32));
-    w.aq_sh = cv.take<uint8_t>((size_t)n * i);
-    w.sa_sh = cv.take<uint8_t>((size_t)n * (i / 32));
+    const int64_t padded_sh = moe::t16_padded_rows(n, 1);
+    w.xq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, h));
+    w.sx_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, h));
+    w.aq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, i));
+    w.sa_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, i));
   }
   w.y_acc = cv.take<float>((size_t)n * h);
   return w;
@@ -217,18 +221,30 @@ moe_status check_gmm_common(const char* who, int64_t rows, int64_t hidden, int64
   return MOE_OK;
 }
 
+// The stage entry points take row-major token operands (the pages' layout) and stage
+// them through the tiled layout of the kernels: in_* holds the packed input (K up to
+// max(hidden, inter)), out_* GMM1's requantized output before it is unpacked.
 struct GmmWs {
   int4* tiles;
   int* count;
   int max_tiles, tt;
+  uint8_t* in_codes;
+  uint8_t* in_scales;
+  uint8_t* out_codes;
+  uint8_t* out_scales;
 };
 
-GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups) {
+GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_t inter) {
   GmmWs w;
   w.tt = token_tile_tt(rows, groups);
   w.max_tiles = (int)(rows / (16 * w.tt) + groups + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.count = cv.take<int>(1);
+  const int64_t padded = moe::t16_padded_rows(rows, groups), kin = std::max(hidden, inter);
+  w.in_codes = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, kin));
+  w.in_scales = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, kin));
+  w.out_codes = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, inter));
+  w.out_scales = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, inter));
   return w;
 }
 
@@ -444,10 +460,6 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   const int64_t n = a->num_tokens, h = a->hidden, inter = a->inter, ne = a->num_experts;
   const int64_t flat = n * a->topk;
   const int fmt = a->quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1;
-  uint8_t* xq = a->xq ? a->xq : w.xq;
-  uint8_t* sx = a->sx ? a->sx : w.sx;
-  uint8_t* aq = a->aq ? a->aq : w.aq;
-  uint8_t* sa = a->sa ? a->sa : w.sa;
   int32_t* gath = a->sorted_row_idx ? a->sorted_row_idx : w.gath;
 
   // stage 1a: routing (full expert range, scatter + gather forms, combine row maps)
@@ -465,48 +477,63 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt, w.max_tiles, w.tiles, w.tile_count, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  // stage 1b: gather + MX quantization (plus the token-order copy for shared experts)
-  moe::PermuteParams pp;
-  pp.x = a->x; pp.in_dtype = MOE_DTYPE_BF16; pp.n = n; pp.hidden = h; pp.topk = (int)a->topk; pp.scat = w.scat;
-  pp.m_limit = flat; pp.quant = fmt; pp.out = xq; pp.out_scales = sx; pp.scale_cols = h / 32;
-  pp.tok_out = a->num_shared > 0 ? w.xq_tok : nullptr; pp.tok_scales = w.sx_tok;
-  e = moe::launch_permute(pp, st);
+  // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
+  // of the shared experts)
+  moe::PermuteTilesParams pt;
+  pt.x = a->x; pt.in_dtype = MOE_DTYPE_BF16; pt.hidden = (int)h; pt.row_token = w.row_token;
+  pt.chunks = w.tiles; pt.chunk_count = w.tile_count; pt.max_chunks = w.max_tiles; pt.tt = w.tt; pt.fmt = fmt;
+  pt.out = w.xq; pt.out_scales = w.sx;
+  e = moe::launch_permute_tiles(pt, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe permute launch");
+  if (a->num_shared > 0) {
+    e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
+    moe::PermuteTilesParams ps = pt;
+    ps.row_token = nullptr; ps.chunks = w.sh_tiles; ps.chunk_count = w.sh_count; ps.max_chunks = w.sh_max_tiles;
+    ps.tt = w.sh_tt; ps.out = w.xq_sh; ps.out_scales = w.sx_sh;
+    e = moe::launch_permute_tiles(ps, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared permute launch");
+  }
+  if (a->xq || a->sx) {
+    e = moe::launch_unpack_tokens(w.xq, w.sx, (int)h, w.tiles, w.tile_count, w.max_tiles, w.tt, a->xq, a->sx, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe unpack launch");
+  }
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 2: GMM1 + SwiGLU + MX requantization
   const int packed = a->weight_format == MOE_WEIGHTS_PACKED;
-  moe::Gmm1Params g1{xq, sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, aq, sa, a->h1, packed};
+  moe::Gmm1Params g1{w.xq, w.sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
+                     (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed};
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
+  if (a->aq || a->sa) {
+    e = moe::launch_unpack_tokens(w.aq, w.sa, (int)inter, w.tiles, w.tile_count, w.max_tiles, w.tt, a->aq, a->sa,
+                                  st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe unpack launch");
+  }
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stages 3-4: GMM2 with the weighted combine into fp32 token rows
   e = moe::launch_fill_zero(w.y_acc, n * h, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe zero-fill launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  moe::Gmm2Params g2{aq, sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
+  moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
                      (int)h, (int)inter, fmt, w.tt, w.row_token, w.row_weight, w.y_acc, a->o, packed};
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // shared experts: same FFN over all tokens in token order, added unweighted
-  if (a->num_shared > 0) {
-    e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
-    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
-    for (int64_t s = 0; s < a->num_shared; ++s) {
-      moe::Gmm1Params s1{w.xq_tok, w.sx_tok, a->shared_w1 + s * 2 * inter * h,
-                         a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
-                         w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr,
-                         packed};
-      e = moe::launch_gmm1(s1, st);
-      if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
-      moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter,
-                         a->shared_w2_scales + s * group_scale_bytes(h, inter, a->weight_format), w.sh_tiles,
-                         w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, nullptr, nullptr, w.y_acc,
-                         nullptr, packed};
-      e = moe::launch_gmm2(s2, st);
-      if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
-    }
+  for (int64_t s = 0; s < a->num_shared; ++s) {
+    moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + s * 2 * inter * h,
+                       a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr,
+                       packed};
+    e = moe::launch_gmm1(s1, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
+    moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter,
+                       a->shared_w2_scales + s * group_scale_bytes(h, inter, a->weight_format), w.sh_tiles,
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, nullptr, nullptr, w.y_acc,
+                       nullptr, packed};
+    e = moe::launch_gmm2(s2, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
   }
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   e = moe::launch_finalize(w.y_acc, n * h, reinterpret_cast<uint16_t*>(a->y), st);
@@ -515,11 +542,12 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   return ok();
 }
 
-moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, size_t* bytes) {
+moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, int64_t hidden, int64_t inter, size_t* bytes) {
   if (!bytes) return fail(MOE_ERR_INVALID_ARG, "moe_gmm_workspace_size: bytes is NULL");
-  if (rows < 0 || num_groups < 1) return fail(MOE_ERR_SHAPE, "moe_gmm_workspace_size: bad sizes");
+  if (moe_status s = check_gmm_common("moe_gmm_workspace_size", rows, hidden, inter, num_groups, MOE_FP8_E4M3))
+    return s;
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   *bytes = cv.off;
   return ok();
 }
@@ -535,18 +563,22 @@ moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t r
   if (!group_offsets || !w1 || !w1_scales || (rows > 0 && (!xq || !sx || !aq || !sa)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
   if (rows == 0) return ok();
   Carver wc(workspace);
-  GmmWs w = carve_gmm(wc, rows, num_groups);
+  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
-  moe::Gmm1Params g{xq, sx, w1, w1_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
-                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, aq, sa, h1, weight_format};
+  e = moe::launch_pack_tokens(xq, sx, (int)hidden, w.tiles, w.count, w.max_tiles, w.tt, w.in_codes, w.in_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "token pack launch");
+  moe::Gmm1Params g{w.in_codes, w.in_scales, w1, w1_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, w.out_codes, w.out_scales, h1, weight_format};
   e = moe::launch_gmm1(g, st);
   if (e != hipSuccess) return hip_fail(e, "gmm1 launch");
+  e = moe::launch_unpack_tokens(w.out_codes, w.out_scales, (int)inter, w.tiles, w.count, w.max_tiles, w.tt, aq, sa, st);
+  if (e != hipSuccess) return hip_fail(e, "token unpack launch");
   return ok();
 }
 
@@ -563,15 +595,17 @@ moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, 
   if (!group_offsets || !w2 || !w2_scales || (rows > 0 && (!aq || !sa || !row_token || !row_weight || !y_accum)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
   if (rows == 0) return ok();
   Carver wc(workspace);
-  GmmWs w = carve_gmm(wc, rows, num_groups);
+  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
-  moe::Gmm2Params g{aq, sa, w2, w2_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
+  e = moe::launch_pack_tokens(aq, sa, (int)inter, w.tiles, w.count, w.max_tiles, w.tt, w.in_codes, w.in_scales, st);
+  if (e != hipSuccess) return hip_fail(e, "token pack launch");
+  moe::Gmm2Params g{w.in_codes, w.in_scales, w2, w2_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
                     quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, row_token, row_weight, y_accum, o,
                     weight_format};
   e = moe::launch_gmm2(g, st);

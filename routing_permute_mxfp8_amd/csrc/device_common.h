@@ -104,4 +104,17 @@ __device__ __forceinline__ v8i load_mx_operand(const uint8_t* row_k0, int g) {
   return join_operand(lo, hi);
 }
 
+// ---- tiled token layout ------------------------------------------------------------
+// An FP8 matrix of R rows (R a multiple of 16) and K columns (K a multiple of 128) in
+// the operand order of the MFMA above: 16-row x 128-K tiles of 2 KB,
+//   codes  [R/16][K/128][2 halves][64 lanes][16 B]: lane l = (g, r) of half h holds
+//          row 16T + r, K bytes [128 s + 64 h + 16 g, +16),
+//   scales [R/16][ceil(K/512)][64 lanes][4 B]: byte j of lane (g, r) in quad q is the
+//          E8M0 scale of row 16T + r, K-block g of step 4q + j (0 past the last step).
+// Rows of one expert start at a multiple of 16 (each expert is padded to whole tiles).
+__device__ __forceinline__ int64_t t16_codes(int64_t tile, int ks, int step) {
+  return ((tile * ks + step) * 2) * 1024;
+}
+__device__ __forceinline__ int64_t t16_scales(int64_t tile, int kq, int quad) { return (tile * kq + quad) * 256; }
+
 }  // namespace moe

@@ -102,43 +102,50 @@ __device__ __forceinline__ int weight_scale(int sc_raw, int step, int lane) {
 // LDS per buffer: NT tiles x {2 KB operand bytes (lo halves of the 64 lanes, then hi
 // halves), 256 B scale words (one per lane)}.
 template <int NT>
-struct Stage {
+struct StageLayout {
   static constexpr int kBufBytes = NT * (kTileBytes + kTileScaleBytes);
-  static constexpr int kPerWave = (NT + 3) / 4;   // tiles loaded by each of 4 waves
+};
+
+template <int NTT>
+struct Stage {
+  static constexpr int kPerWave = (NTT + 3) / 4;   // tiles loaded by each of 4 waves
   u32x4 lo[kPerWave], hi[kPerWave];
   int sc[kPerWave];
 };
 
-template <int NT>
-__device__ __forceinline__ void stage_load(Stage<NT>& st, const uint8_t* tok, const uint8_t* toks, int K, int row0,
-                                           int nrows, int ntt, int step, int wave, int lane) {
-  const int g = lane >> 4, r = lane & 15;
-  // Loads are unconditional (tile index clamped to the last valid tile, padding lanes
-  // re-read the last valid row), so the compiler can count them exactly and never has
-  // to drain the load queue at a branch join.
+// Token operands are in the tiled layout (device_common.h): the chunk's padded row0 is a
+// multiple of 16, so its tile t is tile row0/16 + t and one K step of it is two 1 KB
+// loads per wave plus one scale dword per lane (shared by 4 consecutive K steps).
+template <int NTT>
+__device__ __forceinline__ void stage_load(Stage<NTT>& st, const uint8_t* tok, const uint8_t* toks, int K, int row0,
+                                           int ntt, int step, int wave, int lane) {
+  const int ks = K >> 7, kq = (ks + 3) >> 2;
+  // Loads are unconditional (tile index clamped to the last tile of the chunk), so the
+  // compiler can count them exactly and never has to drain the load queue at a branch
+  // join.
 #pragma unroll
-  for (int i = 0; i < Stage<NT>::kPerWave; ++i) {
-    const int t = min(wave + 4 * i, ntt - 1);
-    const int rr = min(16 * t + r, nrows - 1);
-    const uint8_t* row = tok + (int64_t)(row0 + rr) * K + 128 * step;
-    st.lo[i] = *reinterpret_cast<const u32x4*>(row + 16 * g);
-    st.hi[i] = *reinterpret_cast<const u32x4*>(row + 64 + 16 * g);
-    st.sc[i] = (int)*reinterpret_cast<const uint32_t*>(toks + (int64_t)(row0 + rr) * (K >> 5) + 4 * step);
+  for (int i = 0; i < Stage<NTT>::kPerWave; ++i) {
+    const int64_t tile = (int64_t)(row0 >> 4) + min(wave + 4 * i, ntt - 1);
+    const uint8_t* tb = tok + t16_codes(tile, ks, step);
+    st.lo[i] = reinterpret_cast<const u32x4*>(tb)[lane];
+    st.hi[i] = reinterpret_cast<const u32x4*>(tb + 1024)[lane];
+    st.sc[i] = reinterpret_cast<const int*>(toks + t16_scales(tile, kq, step >> 2))[lane];
   }
 }
 
-template <int NT>
-__device__ __forceinline__ void stage_store(const Stage<NT>& st, uint8_t* buf, int ntt, int wave, int lane) {
+template <int NT, int NTT>
+__device__ __forceinline__ void stage_store(const Stage<NTT>& st, uint8_t* buf, int ntt, int step, int wave,
+                                            int lane) {
   // Slots are clamped like the loads: waves whose tile is past the chunk rewrite the
   // last valid slot with the same bytes another wave stores there.
 #pragma unroll
-  for (int i = 0; i < Stage<NT>::kPerWave; ++i) {
+  for (int i = 0; i < Stage<NTT>::kPerWave; ++i) {
     const int t = min(wave + 4 * i, ntt - 1);
     uint8_t* tile = buf + t * kTileBytes;
     reinterpret_cast<u32x4*>(tile)[lane] = st.lo[i];
     reinterpret_cast<u32x4*>(tile + 1024)[lane] = st.hi[i];
     reinterpret_cast<int*>(buf + NT * kTileBytes + t * kTileScaleBytes)[lane] =
-        (int)((uint32_t)st.sc[i] >> (8 * (lane >> 4)));
+        (int)((uint32_t)st.sc[i] >> (8 * (step & 3)));
   }
 }
 
@@ -162,40 +169,46 @@ __device__ __forceinline__ void block_items(int total, int* first, int* stride, 
 }
 
 // ---- the K loop shared by both GEMMs ---------------------------------------------
-// One K step: issue the global loads of the next token stage and of the weights two
+// One K step: issue the global loads of the next token stage and of the weights PF
 // steps ahead, run the MFMAs of this step from the registers and the LDS stage, then
 // store the next stage into the other LDS buffer and meet the barrier.
+// All NTT token tiles are multiplied whatever the chunk's tile count ntt: the MFMA
+// sequence is straight-line code in which the LDS reads of tile t+1 are issued before the
+// MFMAs of tile t (a branch per tile would drain the LDS queue before every tile's MFMAs).
+// Tiles in [ntt, NTT) hold stale LDS bytes; their accumulators are never stored. The
+// idle tiles of a partial chunk cost MFMA time only, and less of it than the chunk's
+// weight stream takes.
 // WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int PF>
-__device__ __forceinline__ void k_step(int s, int ks, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], Stage<NT>& st,
-                                       const v8i (&acur)[4], const int (&scur)[4], v8i (&aload)[4], int (&sload)[4],
-                                       const uint8_t* tok, const uint8_t* toks, int K, int row0, int nrows, int ntt,
-                                       uint8_t* lds, int wave, int lane) {
+template <int FMT, int NT, int NTT, bool PACKED, bool WEIGHTS_A, int PF>
+__device__ __forceinline__ void k_step(int s, int ks, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4],
+                                       Stage<NTT>& st, const v8i (&acur)[4], const int (&scur)[4],
+                                       v8i (&aload)[4], int (&sload)[4], const uint8_t* tok, const uint8_t* toks,
+                                       int K, int row0, int nrows, int ntt, uint8_t* lds, int wave, int lane) {
   // Next stage and the weights PF steps ahead; past the last step the last step is
   // re-read (in bounds, unused) so that every K step issues the same loads.
-  stage_load<NT>(st, tok, toks, K, row0, nrows, ntt, min(s + 1, ks - 1), wave, lane);
+  const int next = min(s + 1, ks - 1);
+  stage_load<NTT>(st, tok, toks, K, row0, ntt, next, wave, lane);
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(s + PF, ks - 1), lane, aload[q], sload[q]);
-  const uint8_t* buf = lds + (s & 1) * Stage<NT>::kBufBytes;
+  const uint8_t* buf = lds + (s & 1) * StageLayout<NT>::kBufBytes;
   int sw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) sw[q] = weight_scale<PACKED>(scur[q], s, lane);
-  auto tile_mfmas = [&](int t) {
-    v8i b;
-    int sb;
-    stage_read<NT>(buf, t, lane, b, sb);
+  v8i b[2];
+  int sb[2];
+  stage_read<NT>(buf, 0, lane, b[0], sb[0]);
+#pragma unroll
+  for (int t = 0; t < NTT; ++t) {
+    if (t + 1 < NTT) stage_read<NT>(buf, t + 1, lane, b[(t + 1) & 1], sb[(t + 1) & 1]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (WEIGHTS_A)
-        acc[q][t] = mfma_mx16<FMT>(acur[q], b, acc[q][t], sw[q], sb);
+        acc[q][t] = mfma_mx16<FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
       else
-        acc[q][t] = mfma_mx16<FMT>(b, acur[q], acc[q][t], sb, sw[q]);
+        acc[q][t] = mfma_mx16<FMT>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
     }
-  };
-#pragma unroll
-  for (int t = 0; t < NT; ++t)
-    if (t < ntt) tile_mfmas(t);
-  stage_store<NT>(st, lds + ((s + 1) & 1) * Stage<NT>::kBufBytes, ntt, wave, lane);
+  }
+  stage_store<NT, NTT>(st, lds + ((s + 1) & 1) * StageLayout<NT>::kBufBytes, ntt, next, wave, lane);
   __syncthreads();
 }
 
@@ -204,42 +217,68 @@ __device__ __forceinline__ void k_step(int s, int ks, v4f (&acc)[4][NT], const W
 // latency, and the third register buffer would not fit beside 256 accumulators).
 template <int NT> struct Prefetch { static constexpr int value = NT <= 4 ? 2 : 1; };
 
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+template <int FMT, int NT, int NTT, bool PACKED, bool WEIGHTS_A>
 __device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int nrows, int ntt, uint8_t* lds,
                                        int wave, int lane) {
   constexpr int PF = Prefetch<NT>::value;
   const int ks = K >> 7;
-  Stage<NT> st;
+  Stage<NTT> st;
   v8i a0[4], a1[4], a2[4];
   int s0[4], s1[4], s2[4];
-  stage_load<NT>(st, tok, toks, K, row0, nrows, ntt, 0, wave, lane);
+  stage_load<NTT>(st, tok, toks, K, row0, ntt, 0, wave, lane);
 #pragma unroll
   for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], 0, lane, a0[q], s0[q]);
   if (PF == 2) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(1, ks - 1), lane, a1[q], s1[q]);
   }
-  stage_store<NT>(st, lds, ntt, wave, lane);
+  stage_store<NT, NTT>(st, lds, ntt, 0, wave, lane);
   __syncthreads();
   if constexpr (PF == 2) {
-    for (int s = 0; s < ks; s += 3) {   // three register buffers rotate with the K step
-      k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt, lds,
-                                            wave, lane);
-      if (s + 1 < ks)
-        k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows, ntt,
-                                              lds, wave, lane);
-      if (s + 2 < ks)
-        k_step<FMT, NT, PACKED, WEIGHTS_A, 2>(s + 2, ks, acc, wp, st, a2, s2, a1, s1, tok, toks, K, row0, nrows, ntt,
-                                              lds, wave, lane);
+    // Three register buffers rotate with the K step. The ks % 3 leading steps run one
+    // at a time (rotating the buffers by copies); the loop body then holds three whole
+    // steps with no branch between them.
+    int s = 0;
+    for (const int lead = ks % 3; s < lead; ++s) {
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt,
+                                                 lds, wave, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = a1[q];
+        s0[q] = s1[q];
+        a1[q] = a2[q];
+        s1[q] = s2[q];
+      }
+    }
+    for (; s < ks; s += 3) {
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt,
+                                                 lds, wave, lane);
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows,
+                                                 ntt, lds, wave, lane);
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s + 2, ks, acc, wp, st, a2, s2, a1, s1, tok, toks, K, row0, nrows,
+                                                 ntt, lds, wave, lane);
     }
   } else {
-    for (int s = 0; s < ks; s += 2) {   // two register buffers alternate
-      k_step<FMT, NT, PACKED, WEIGHTS_A, 1>(s, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt, lds,
-                                            wave, lane);
-      if (s + 1 < ks)
-        k_step<FMT, NT, PACKED, WEIGHTS_A, 1>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows, ntt,
-                                              lds, wave, lane);
+    // Two register buffers alternate; the loop body holds two whole K steps with no
+    // branch between them (an odd step count runs its first step alone, with the
+    // buffers swapped afterwards), so every accumulator is updated in place.
+    int s = 0;
+    if (ks & 1) {
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(0, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt,
+                                                 lds, wave, lane);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        a0[q] = a1[q];
+        s0[q] = s1[q];
+      }
+      s = 1;
+    }
+    for (; s < ks; s += 2) {
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(s, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt,
+                                                 lds, wave, lane);
+      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows,
+                                                 ntt, lds, wave, lane);
     }
   }
   (void)a2; (void)s2;
@@ -267,7 +306,7 @@ void gmm1_swiglu_kernel(
   for (; it < last; it += stride) {
     const int j = it / ncb, cb = it - j * ncb;
     const int4 tile = tiles[j];
-    const int e = tile.x, row0 = tile.y, nrows = tile.z;
+    const int e = tile.x, row0 = tile.y, nrows = tile.z, srow0 = tile.w;
     const int ntt = (nrows + 15) >> 4;
     const int n0 = cb * 128 + wave * 32;       // first gate channel of this wave
     WPtr<PACKED> wp[4];
@@ -281,15 +320,17 @@ void gmm1_swiglu_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, nrows, ntt, lds, wave, lane);
+    k_loop<FMT, NT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, nrows, ntt, lds, wave, lane);
 
-    const int is = inter >> 5;
+    // A^ goes out in the tiled layout with K = inter, where this block's 128 gate
+    // channels are exactly K step cb: the wave's 32 channels are half wave/2 of it,
+    // lane groups 2 (wave % 2) + jj, byte 4g + i, and its MX group is K-block `wave`.
+    const int ks2 = inter >> 7, kq2 = (ks2 + 3) >> 2;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= ntt) continue;                   // uniform per wave
       const int rr = 16 * t + r;
-      const bool valid = rr < nrows;
-      const int64_t row = row0 + rr;
+      const int64_t tl = (int64_t)(row0 >> 4) + t;
       float act[2][4];
       int m = 0;
 #pragma unroll
@@ -305,24 +346,25 @@ void gmm1_swiglu_kernel(
       m = max(m, __shfl_xor(m, 32));
       const int b = mx_scale_byte<FMT>(__int_as_float(m));
       const float inv = mx_inv_scale(b);
-      if (valid) {
+      // Every row of the tile is written: rows past the chunk are zero tokens (the
+      // tiled X holds zeros there), so they requantize to code 0 and scale 0.
+      uint8_t* tb = aq + t16_codes(tl, ks2, cb) + (wave >> 1) * 1024;
 #pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-          const uint32_t codes =
-              pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
-          *reinterpret_cast<uint32_t*>(aq + row * inter + n0 + 16 * jj + 4 * g) = codes;
-        }
-        if (g == 0) sa[row * is + (n0 >> 5)] = (uint8_t)b;
-        if (h1) {
+      for (int jj = 0; jj < 2; ++jj) {
+        const uint32_t codes = pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
+        *reinterpret_cast<uint32_t*>(tb + ((2 * (wave & 1) + jj) * 16 + r) * 16 + 4 * g) = codes;
+      }
+      if (g == 0) sa[t16_scales(tl, kq2, cb >> 2) + (wave * 16 + r) * 4 + (cb & 3)] = (uint8_t)b;
+      if (h1 && rr < nrows) {
+        const int64_t row = srow0 + rr;
 #pragma unroll
-          for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int ch = n0 + 16 * jj + 4 * g + i;
-              h1[row * 2 * inter + ch] = acc[jj][t][i];
-              h1[row * 2 * inter + inter + ch] = acc[2 + jj][t][i];
-            }
-        }
+          for (int i = 0; i < 4; ++i) {
+            const int ch = n0 + 16 * jj + 4 * g + i;
+            h1[row * 2 * inter + ch] = acc[jj][t][i];
+            h1[row * 2 * inter + inter + ch] = acc[2 + jj][t][i];
+          }
       }
     }
   }
@@ -346,7 +388,7 @@ void gmm2_combine_kernel(
   for (; it < last; it += stride) {
     const int j = it / ncb, cb = it - j * ncb;
     const int4 tile = tiles[j];
-    const int e = tile.x, row0 = tile.y, nrows = tile.z;
+    const int e = tile.x, row0 = tile.y, nrows = tile.z, srow0 = tile.w;
     const int ntt = (nrows + 15) >> 4;
     const int c0 = cb * 256 + wave * 64;
     // hidden % 256 == 128: the last block's upper waves have no channels; they still
@@ -361,7 +403,7 @@ void gmm2_combine_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, nrows, ntt, lds, wave, lane);
+    k_loop<FMT, NT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, nrows, ntt, lds, wave, lane);
 
     // acc[q][t][i] = O[token row 16t + 4g + i][channel c0 + 16q + r]
 #pragma unroll
@@ -371,7 +413,7 @@ void gmm2_combine_kernel(
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * t + 4 * g + i;
         if (rr >= nrows) continue;
-        const int64_t row = row0 + rr;
+        const int64_t row = srow0 + rr;
         const int64_t tok = row_token ? (int64_t)row_token[row] : row;
         const float wgt = row_token ? row_weight[row] : 1.0f;
         float* yrow = y_accum + tok * hidden + c0 + r;
@@ -427,7 +469,7 @@ __global__ void pack_scales_kernel(const uint8_t* __restrict__ scales, uint32_t*
 __global__ void single_group_tiles_kernel(int rows, int tm, int4* __restrict__ tiles, int* __restrict__ count) {
   const int nt = (rows + tm - 1) / tm;
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nt; i += gridDim.x * blockDim.x)
-    tiles[i] = make_int4(0, i * tm, min(tm, rows - i * tm), 0);
+    tiles[i] = make_int4(0, i * tm, min(tm, rows - i * tm), i * tm);
   if (blockIdx.x == 0 && threadIdx.x == 0) *count = nt;
 }
 
@@ -489,7 +531,7 @@ template <int FMT, int NT, bool PACKED>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED>;
   LaunchShape ls;
-  hipError_t e = persistent_shape(kern, 2 * Stage<NT>::kBufBytes, &ls);
+  hipError_t e = persistent_shape(kern, 2 * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
   kern<<<ls.grid, 256, ls.lds, st>>>(p.xq, p.sx, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.aq, p.sa,
                                      p.h1);
@@ -500,7 +542,7 @@ template <int FMT, int NT, bool PACKED>
 hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
   auto kern = gmm2_combine_kernel<FMT, NT, PACKED>;
   LaunchShape ls;
-  hipError_t e = persistent_shape(kern, 2 * Stage<NT>::kBufBytes, &ls);
+  hipError_t e = persistent_shape(kern, 2 * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
   kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.row_token,
                                      p.row_weight, p.y_accum, p.o);

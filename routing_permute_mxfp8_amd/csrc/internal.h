@@ -36,11 +36,45 @@ struct RouteParams {
 };
 hipError_t launch_routing(const RouteParams& p, hipStream_t stream);
 
-// Token tiles of height `tm` over groups given by int32 offsets [groups + 1]
-// (clamped into [0, rows], non-decreasing): tiles[j] = {group, row0, nrows, 0},
-// *count = number of tiles (at most max_tiles are written).
+// Chunks of up to `tm` rows (tm a multiple of 16) over groups given by int32 offsets
+// [groups + 1] (clamped into [0, rows], non-decreasing):
+//   tiles[j] = {group, padded row0, nrows, sorted row0},
+// where the padded row space gives every group a whole number of 16-row tiles (see
+// t16_padded_rows). *count = number of chunks (at most max_tiles are written).
 hipError_t launch_build_tiles(const int* offsets, int groups, int rows, int tm, int max_tiles, int4* tiles,
                               int* count, hipStream_t stream);
+
+// ---- tiled token layout (tiles.hip; layout in device_common.h) --------------------
+// Upper bound of the padded row count of `rows` rows split into `groups` groups.
+inline int64_t t16_padded_rows(int64_t rows, int64_t groups) {
+  const int64_t p = rows + 15 * (rows < groups ? rows : groups);
+  return (p + 15) / 16 * 16;
+}
+inline int64_t t16_code_bytes(int64_t padded_rows, int64_t k) { return padded_rows * k; }
+inline int64_t t16_scale_bytes(int64_t padded_rows, int64_t k) { return padded_rows / 16 * ((k / 128 + 3) / 4) * 256; }
+
+// Gather of the rows of each chunk (source token = row_token[sorted row], or the sorted
+// row itself when row_token is null) with MX quantization, into the tiled layout.
+struct PermuteTilesParams {
+  const void* x = nullptr;       // [tokens, hidden] of in_dtype
+  int in_dtype = 2;              // MOE_DTYPE_* (0 fp32, 1 fp16, 2 bf16)
+  int hidden = 0;                // multiple of 128
+  const int32_t* row_token = nullptr;
+  const int4* chunks = nullptr;
+  const int* chunk_count = nullptr;
+  int max_chunks = 0, tt = 1;    // tt = 16-row tiles per chunk
+  int fmt = 0;                   // 0 E4M3FN, 1 E5M2
+  uint8_t* out = nullptr;        // tiled codes
+  uint8_t* out_scales = nullptr; // tiled scales
+};
+hipError_t launch_permute_tiles(const PermuteTilesParams& p, hipStream_t stream);
+// Row-major codes [rows, K] / scales [rows, K/32] (sorted rows) <-> tiled layout.
+hipError_t launch_pack_tokens(const uint8_t* codes, const uint8_t* scales, int K, const int4* chunks,
+                              const int* chunk_count, int max_chunks, int tt, uint8_t* out, uint8_t* out_scales,
+                              hipStream_t stream);
+hipError_t launch_unpack_tokens(const uint8_t* in, const uint8_t* in_scales, int K, const int4* chunks,
+                                const int* chunk_count, int max_chunks, int tt, uint8_t* codes, uint8_t* scales,
+                                hipStream_t stream);
 
 // ---- permute + MX quantization (permute_quant.hip) ------------------------------
 struct PermuteParams {
@@ -60,19 +94,21 @@ struct PermuteParams {
 hipError_t launch_permute(const PermuteParams& p, hipStream_t stream);
 
 // ---- grouped GEMMs (gmm.hip) -------------------------------------------------------
+// Token operands and GMM1's requantized output are in the tiled layout, indexed by the
+// chunks' padded rows; h1, o, row_token and row_weight are indexed by sorted rows.
 struct Gmm1Params {
-  const uint8_t* xq; const uint8_t* sx;        // [rows, H], [rows, H/32]
+  const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
   const int4* tiles; const int* tile_count; int max_tiles;
   int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16)
-  uint8_t* aq; uint8_t* sa;                    // [rows, I], [rows, I/32]
+  uint8_t* aq; uint8_t* sa;                    // tiled [padded rows, I]
   float* h1;                                   // nullable [rows, 2I]
   int packed;                                  // weights in the MFMA-native packed layout
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 
 struct Gmm2Params {
-  const uint8_t* aq; const uint8_t* sa;        // [rows, I], [rows, I/32]
+  const uint8_t* aq; const uint8_t* sa;        // tiled [padded rows, I]
   const uint8_t* w; const uint8_t* ws;         // [G, H, I], [G, H, I/32]
   const int4* tiles; const int* tile_count; int max_tiles;
   int hidden, inter, fmt, tt;
@@ -92,7 +128,7 @@ int gmm_token_tiles(int64_t rows, int64_t groups);
 hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
                                uint8_t* packed, uint8_t* packed_scales, hipStream_t stream);
 
-// Tiles of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), 0}.
+// Chunks of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), i*tm}.
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);
 hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t stream);
 hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t stream);

@@ -152,6 +152,8 @@ __global__ __launch_bounds__(64) void route_scatter(
 
 // Offsets are clamped into [0, rows] and made non-decreasing, and at most max_tiles
 // tiles are written, so caller-given offsets can never send a GEMM out of bounds.
+// Each group is padded to whole 16-row tiles in the tiled token layout: its padded
+// start is the sum of the padded sizes of the groups before it.
 __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict__ offsets, int G, int rows, int tm,
                                                            int max_tiles, int4* __restrict__ tiles,
                                                            int* __restrict__ count) {
@@ -163,31 +165,36 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
   // start of this thread's first group: max of the clamped offsets [0, g0]
   int local = 0;
   for (int g = g0; g < g1; ++g) local = max(local, off(g));
-  const int incl_max = block_inclusive_scan_1024<true>(local, part);
+  block_inclusive_scan_1024<true>(local, part);
   const int before = t > 0 ? part[t - 1] : 0;
   __syncthreads();
-  (void)incl_max;
   const int start = g0 < g1 ? max(before, off(g0)) : 0;
-  int sum = 0;
+  int ntiles = 0, npad = 0;
   int prev = start;
   for (int g = g0; g < g1; ++g) {
     const int nxt = max(prev, off(g + 1));
-    sum += (nxt - prev + tm - 1) / tm;
+    ntiles += (nxt - prev + tm - 1) / tm;
+    npad += (nxt - prev + 15) & ~15;
     prev = nxt;
   }
-  const int incl = block_inclusive_scan_1024(sum, part);
-  int run = incl - sum;
+  const int tiles_incl = block_inclusive_scan_1024(ntiles, part);
+  const int total = part[1023];
+  __syncthreads();
+  const int pad_incl = block_inclusive_scan_1024(npad, part);
+  int run = tiles_incl - ntiles;
+  int pad = pad_incl - npad;
   prev = start;
   for (int g = g0; g < g1; ++g) {
     const int nxt = max(prev, off(g + 1));
     const int cnt = nxt - prev;
     for (int i = 0; i * tm < cnt; ++i) {
-      if (run < max_tiles) tiles[run] = make_int4(g, prev + i * tm, min(tm, cnt - i * tm), 0);
+      if (run < max_tiles) tiles[run] = make_int4(g, pad + i * tm, min(tm, cnt - i * tm), prev + i * tm);
       ++run;
     }
+    pad += (cnt + 15) & ~15;
     prev = nxt;
   }
-  if (t == 1023) *count = min(part[1023], max_tiles);
+  if (t == 0) *count = min(total, max_tiles);
 }
 
 }  // namespace

@@ -58,8 +58,11 @@ def test_workspace_queries(lib):
     assert st == 0 and b > 0
     st, _ = ws_size(lib.moe_init_routing_workspace_size, 10, 2, 0)
     assert st == 2
-    st, _ = ws_size(lib.moe_gmm_workspace_size, 100, 4)
-    assert st == 0
+    # rows restaged in the tiled layout, each of the 4 groups padded to 16 rows
+    st, c = ws_size(lib.moe_gmm_workspace_size, 100, 4, 256, 128)
+    assert st == 0 and c >= (100 + 15 * 4) * (256 + 128)
+    st, _ = ws_size(lib.moe_gmm_workspace_size, 100, 4, 200, 128)
+    assert st == 2
 
 
 FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: every call below fails validation

@@ -30,7 +30,7 @@ def build(verbose: bool = False) -> str:
     out = lib_path()
     tmp = out + ".tmp"
     cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-shared",
+        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
         # keep fp32 denormals: MX quantization of subnormal bf16 inputs depends on them
         "-fno-gpu-flush-denormals-to-zero",
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

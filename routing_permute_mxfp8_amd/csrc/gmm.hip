@@ -36,6 +36,7 @@
 #include <algorithm>
 #include <map>
 #include <mutex>
+#include <utility>
 
 #include "device_common.h"
 #include "internal.h"
@@ -74,22 +75,9 @@ __device__ __forceinline__ WPtr<PACKED> weight_tile(const uint8_t* w, const uint
   return p;
 }
 
-// Loads one K step of a weight tile: the operand bytes and the raw scale dword. The
-// byte of the dword this lane needs is selected only where the MFMA uses it
-// (weight_scale), so no ALU work waits on a load before its data is due.
-template <bool PACKED>
-__device__ __forceinline__ void load_weight(const WPtr<PACKED>& p, int step, int lane, v8i& v, int& sc_raw) {
-  const int g = lane >> 4;
-  if constexpr (PACKED) {
-    const uint8_t* t = p.d + (int64_t)step * kTileBytes;
-    v = join_operand(*reinterpret_cast<const u32x4*>(t + lane * 16), *reinterpret_cast<const u32x4*>(t + 1024 + lane * 16));
-    sc_raw = (int)*reinterpret_cast<const uint32_t*>(p.s + (step >> 2) * kTileScaleBytes);
-  } else {
-    v = load_mx_operand(p.d + 128 * step, g);
-    sc_raw = (int)*reinterpret_cast<const uint32_t*>(p.s + 4 * step);
-  }
-}
-
+// The byte of a raw weight scale dword that the MFMA uses in K step `step` (the shift
+// is done where the MFMA needs it, so no ALU work waits on a load before its data is
+// due).
 template <bool PACKED>
 __device__ __forceinline__ int weight_scale(int sc_raw, int step, int lane) {
   if constexpr (PACKED)
@@ -99,61 +87,41 @@ __device__ __forceinline__ int weight_scale(int sc_raw, int step, int lane) {
 }
 
 // ---- token staging ------------------------------------------------------------------
-// LDS per buffer: NT tiles x {2 KB operand bytes (lo halves of the 64 lanes, then hi
-// halves), 256 B scale words (one per lane)}.
+// The token rows of a chunk go straight from HBM/L2 to LDS (global_load_lds: lane l of
+// a wave writes LDS base + 16 l, so a 1 KB half tile of the tiled layout lands as is)
+// into a ring of 3 slots, two K steps ahead of their use. A slot holds NT tiles x
+// {2 KB operand bytes, 256 B scale dwords (the raw dwords of the tiled layout: byte
+// step % 4 of lane l is the lane's E8M0 scale of that step)}.
 template <int NT>
 struct StageLayout {
   static constexpr int kBufBytes = NT * (kTileBytes + kTileScaleBytes);
+  static constexpr int kPerWave = (NT + 3) / 4;   // tiles loaded by each of 4 waves
 };
+constexpr int kRing = 3;
 
-template <int NTT>
-struct Stage {
-  static constexpr int kPerWave = (NTT + 3) / 4;   // tiles loaded by each of 4 waves
-  u32x4 lo[kPerWave], hi[kPerWave];
-  int sc[kPerWave];
-};
+typedef __attribute__((address_space(3))) void* lds_void_ptr;
 
-// Token operands are in the tiled layout (device_common.h): the chunk's padded row0 is a
-// multiple of 16, so its tile t is tile row0/16 + t and one K step of it is two 1 KB
-// loads per wave plus one scale dword per lane (shared by 4 consecutive K steps).
-template <int NTT>
-__device__ __forceinline__ void stage_load(Stage<NTT>& st, const uint8_t* tok, const uint8_t* toks, int K, int row0,
-                                           int ntt, int step, int wave, int lane) {
-  const int ks = K >> 7, kq = (ks + 3) >> 2;
-  // Loads are unconditional (tile index clamped to the last tile of the chunk), so the
-  // compiler can count them exactly and never has to drain the load queue at a branch
-  // join.
-#pragma unroll
-  for (int i = 0; i < Stage<NTT>::kPerWave; ++i) {
-    const int64_t tile = (int64_t)(row0 >> 4) + min(wave + 4 * i, ntt - 1);
-    const uint8_t* tb = tok + t16_codes(tile, ks, step);
-    st.lo[i] = reinterpret_cast<const u32x4*>(tb)[lane];
-    st.hi[i] = reinterpret_cast<const u32x4*>(tb + 1024)[lane];
-    st.sc[i] = reinterpret_cast<const int*>(toks + t16_scales(tile, kq, step >> 2))[lane];
-  }
+__device__ __forceinline__ void lds_dma16(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void_ptr)dst, 4, 0, 0);
 }
 
-template <int NT, int NTT>
-__device__ __forceinline__ void stage_store(const Stage<NTT>& st, uint8_t* buf, int ntt, int step, int wave,
-                                            int lane) {
-  // Slots are clamped like the loads: waves whose tile is past the chunk rewrite the
-  // last valid slot with the same bytes another wave stores there.
-#pragma unroll
-  for (int i = 0; i < Stage<NTT>::kPerWave; ++i) {
-    const int t = min(wave + 4 * i, ntt - 1);
-    uint8_t* tile = buf + t * kTileBytes;
-    reinterpret_cast<u32x4*>(tile)[lane] = st.lo[i];
-    reinterpret_cast<u32x4*>(tile + 1024)[lane] = st.hi[i];
-    reinterpret_cast<int*>(buf + NT * kTileBytes + t * kTileScaleBytes)[lane] =
-        (int)((uint32_t)st.sc[i] >> (8 * (step & 3)));
-  }
-}
-
+// Operand and scale byte of token tile t of a slot for K step `step`.
 template <int NT>
-__device__ __forceinline__ void stage_read(const uint8_t* buf, int t, int lane, v8i& v, int& sc) {
+__device__ __forceinline__ void stage_read(const uint8_t* buf, int t, int step, int lane, v8i& v, int& sc) {
   const uint8_t* tile = buf + t * kTileBytes;
   v = join_operand(reinterpret_cast<const u32x4*>(tile)[lane], reinterpret_cast<const u32x4*>(tile + 1024)[lane]);
-  sc = reinterpret_cast<const int*>(buf + NT * kTileBytes + t * kTileScaleBytes)[lane];
+  sc = buf[NT * kTileBytes + t * kTileScaleBytes + 4 * lane + (step & 3)];
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
 // Persistent, XCD-aware item range of this block: [*lo, *hi) stepping by *stride.
@@ -169,119 +137,228 @@ __device__ __forceinline__ void block_items(int total, int* first, int* stride, 
 }
 
 // ---- the K loop shared by both GEMMs ---------------------------------------------
-// One K step: issue the global loads of the next token stage and of the weights PF
-// steps ahead, run the MFMAs of this step from the registers and the LDS stage, then
-// store the next stage into the other LDS buffer and meet the barrier.
-// All NTT token tiles are multiplied whatever the chunk's tile count ntt: the MFMA
-// sequence is straight-line code in which the LDS reads of tile t+1 are issued before the
-// MFMAs of tile t (a branch per tile would drain the LDS queue before every tile's MFMAs).
-// Tiles in [ntt, NTT) hold stale LDS bytes; their accumulators are never stored. The
-// idle tiles of a partial chunk cost MFMA time only, and less of it than the chunk's
-// weight stream takes.
-// WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
-template <int FMT, int NT, int NTT, bool PACKED, bool WEIGHTS_A, int PF>
-__device__ __forceinline__ void k_step(int s, int ks, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4],
-                                       Stage<NTT>& st, const v8i (&acur)[4], const int (&scur)[4],
-                                       v8i (&aload)[4], int (&sload)[4], const uint8_t* tok, const uint8_t* toks,
-                                       int K, int row0, int nrows, int ntt, uint8_t* lds, int wave, int lane) {
-  // Next stage and the weights PF steps ahead; past the last step the last step is
-  // re-read (in bounds, unused) so that every K step issues the same loads.
-  const int next = min(s + 1, ks - 1);
-  stage_load<NTT>(st, tok, toks, K, row0, ntt, next, wave, lane);
+// Loads issued in K step s, numbered: first the weights of step s + WPF (per weight
+// tile: operand lo half, hi half, scale dword; from HBM into the VGPR buffer that step
+// uses), then the token tiles of step s + 2 (per tile this wave stages: lo half, hi
+// half, scale dword; from L2 into ring slot (s + 2) % 3). WPF (weight prefetch
+// distance) is 2 where three weight buffers fit in the registers beside the
+// accumulators, else 1. At the top of step s the weights and token tiles of step s
+// must have landed; with WPF = 2 the newest batch (step s + 1's) may be in flight,
+// with WPF = 1 the token tiles issued after step s's weights may: one fixed vmcnt.
+template <int NT> struct WeightPrefetch { static constexpr int value = NT >= 16 ? 1 : 2; };
+
+template <int NT>
+struct Batch {
+  static constexpr int kWeights = 12;
+  static constexpr int kTokens = 3 * StageLayout<NT>::kPerWave;
+  static constexpr int kLoads = kWeights + kTokens;
+  static constexpr int kInFlight = WeightPrefetch<NT>::value == 2 ? kLoads : kTokens;
+};
+
+template <int NT, bool PACKED, int K_SLOT>
+__device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], const WPtr<PACKED> (&wp)[4], int wstep,
+                                          const uint8_t* tok, const uint8_t* toks, int ks, int row0, int ntt,
+                                          int tstep, uint8_t* slot, int wave, int lane) {
+  constexpr int kW = Batch<NT>::kWeights;
+  if constexpr (K_SLOT < kW) {
+    constexpr int q = K_SLOT / 3, part = K_SLOT % 3;
+    const int g = lane >> 4;
+    if constexpr (part == 2) {
+      if constexpr (PACKED)
+        sload[q] = (int)*reinterpret_cast<const uint32_t*>(wp[q].s + (wstep >> 2) * kTileScaleBytes);
+      else
+        sload[q] = (int)*reinterpret_cast<const uint32_t*>(wp[q].s + 4 * wstep);
+    } else {
+      const uint8_t* src;
+      if constexpr (PACKED)
+        src = wp[q].d + (int64_t)wstep * kTileBytes + part * 1024 + lane * 16;
+      else
+        src = wp[q].d + 128 * wstep + part * 64 + 16 * g;
+      const u32x4 v = *reinterpret_cast<const u32x4*>(src);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(s + PF, ks - 1), lane, aload[q], sload[q]);
-  const uint8_t* buf = lds + (s & 1) * StageLayout<NT>::kBufBytes;
+      for (int j = 0; j < 4; ++j) aload[q][4 * part + j] = (int)v[j];
+    }
+  } else {
+    // Tile wave + 4 i of the chunk (clamped to its last tile: a wave past the end
+    // re-stages that tile, writing the same bytes another wave writes).
+    constexpr int i = (K_SLOT - kW) / 3, part = (K_SLOT - kW) % 3;
+    const int t = min(wave + 4 * i, ntt - 1);
+    const int64_t tile = (int64_t)(row0 >> 4) + t;
+    if constexpr (part == 2)
+      lds_dma4(toks + t16_scales(tile, (ks + 3) >> 2, tstep >> 2) + 4 * lane, slot + NT * kTileBytes + t * kTileScaleBytes);
+    else
+      lds_dma16(tok + t16_codes(tile, ks, tstep) + part * 1024 + 16 * lane, slot + t * kTileBytes + part * 1024);
+  }
+}
+
+template <int NT, bool PACKED, int K0, int... I>
+__device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i (&aload)[4], int (&sload)[4],
+                                           const WPtr<PACKED> (&wp)[4], int wstep, const uint8_t* tok,
+                                           const uint8_t* toks, int ks, int row0, int ntt, int tstep, uint8_t* slot,
+                                           int wave, int lane) {
+  (load_slot<NT, PACKED, K0 + I>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane), ...);
+}
+
+// One K step s, with its weights in (acur, scur) and its token tiles in ring slot
+// s % 3 (`cur`):
+//  1. wait until the loads of step s have landed and meet the barrier: every wave's
+//     token tiles of step s are then in LDS, and every wave is done with slot
+//     (s + 2) % 3, read in step s - 1;
+//  2. issue the weights of step s + WPF into (aload, sload) and the token tiles of step
+//     s + 2 into slot (s + 2) % 3 (past the last step the last one is re-read: in
+//     bounds, unused);
+//  3. the MFMAs of step s.
+// All NT token tiles are multiplied whatever the chunk's tile count ntt: the MFMA
+// sequence is straight-line code in which the LDS reads of tile t+1 are issued before
+// the MFMAs of tile t. Tiles in [ntt, NT) hold stale LDS bytes; their accumulators are
+// never stored (idle tiles of a partial chunk cost MFMA time only).
+// Load placement: with one wave per SIMD the MFMA pipe idles whenever the wave's
+// in-order issue waits, and a burst of loads waits for the CU's vector memory unit. So
+// for chunks of 4 or more tiles the loads are spread one after each MFMA (scheduling
+// fences keep them there); loads that do not fit, and all loads of small chunks, go
+// first.
+// WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+__device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4],
+                                       const v8i (&acur)[4], const int (&scur)[4], v8i (&aload)[4],
+                                       int (&sload)[4], const uint8_t* tok, const uint8_t* toks, int row0, int ntt,
+                                       uint8_t* lds, int wave, int lane) {
+  constexpr int kLoads = Batch<NT>::kLoads;
+  constexpr int kTop = NT < 4 ? kLoads : (kLoads > 4 * NT ? kLoads - 4 * NT : 0);
+  constexpr int kBuf = StageLayout<NT>::kBufBytes;
+  wait_vmcnt<Batch<NT>::kInFlight>();
+  __syncthreads();
+  const int wstep = min(s + WeightPrefetch<NT>::value, ks - 1), tstep = min(s + 2, ks - 1);
+  uint8_t* slot = lds + (cur == 0 ? 2 : cur - 1) * kBuf;   // (cur + 2) % 3
+  const uint8_t* buf = lds + cur * kBuf;
+  load_slots<NT, PACKED, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
+                            ntt, tstep, slot, wave, lane);
   int sw[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) sw[q] = weight_scale<PACKED>(scur[q], s, lane);
   v8i b[2];
   int sb[2];
-  stage_read<NT>(buf, 0, lane, b[0], sb[0]);
-#pragma unroll
-  for (int t = 0; t < NTT; ++t) {
-    if (t + 1 < NTT) stage_read<NT>(buf, t + 1, lane, b[(t + 1) & 1], sb[(t + 1) & 1]);
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (WEIGHTS_A)
-        acc[q][t] = mfma_mx16<FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
-      else
-        acc[q][t] = mfma_mx16<FMT>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
-    }
+  stage_read<NT>(buf, 0, s, lane, b[0], sb[0]);
+  [&]<int... T>(std::integer_sequence<int, T...>) {
+    ([&] {
+      constexpr int t = T;
+      if constexpr (t + 1 < NT) stage_read<NT>(buf, t + 1, s, lane, b[(t + 1) & 1], sb[(t + 1) & 1]);
+      [&]<int... Q>(std::integer_sequence<int, Q...>) {
+        ([&] {
+          constexpr int q = Q;
+          if constexpr (WEIGHTS_A)
+            acc[q][t] = mfma_mx16<FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
+          else
+            acc[q][t] = mfma_mx16<FMT>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
+          constexpr int k = kTop + 4 * t + q;
+          if constexpr (k < kLoads) {
+            load_slot<NT, PACKED, k>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        }(), ...);
+      }(std::make_integer_sequence<int, 4>{});
+    }(), ...);
+  }(std::make_integer_sequence<int, NT>{});
+}
+
+// The K loop of one chunk with WPF = 2. Three weight register buffers rotate with the step (roles
+// fixed in the unrolled three-step body: step s uses a0 and loads into a2, s + 1 uses a1
+// and loads into a0, s + 2 uses a2 and loads into a1); the ring slot is a runtime
+// index. The r = ks % 3 leftover steps run first, and batches 0 and 1 go into the
+// buffers that make the rotation line up when the loop starts at step r (no buffer is
+// copied: a copy would wait for its load). (With the leftover steps after the loop the
+// register allocator permutes the accumulators across the loop body instead.) At the
+// end every load has landed and every wave is past its last LDS read, so the next
+// chunk may reuse the ring.
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+__device__ __forceinline__ void k_loop_pf2(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+                                       const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
+                                       int lane) {
+  constexpr int kL = Batch<NT>::kLoads;
+  constexpr int kBuf = StageLayout<NT>::kBufBytes;
+  const int ks = K >> 7, r = ks % 3, s1 = min(1, ks - 1);
+  v8i a0[4], a1[4], a2[4];
+  int c0[4], c1[4], c2[4];
+  auto seq = std::make_integer_sequence<int, kL>{};
+  if (r == 0) {
+    load_slots<NT, PACKED, 0>(seq, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, 0>(seq, a1, c1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+  } else if (r == 1) {
+    load_slots<NT, PACKED, 0>(seq, a2, c2, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, 0>(seq, a0, c0, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+  } else {
+    load_slots<NT, PACKED, 0>(seq, a1, c1, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, 0>(seq, a2, c2, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   }
-  stage_store<NT, NTT>(st, lds + ((s + 1) & 1) * StageLayout<NT>::kBufBytes, ntt, next, wave, lane);
+  int s = 0, cur = 0;
+  if (r == 1) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    s = 1;
+    cur = 1;
+  } else if (r == 2) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    s = 2;
+    cur = 2;
+  }
+  for (; s < ks; s += 3) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(s, ks, cur, acc, wp, a0, c0, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  wait_vmcnt<0>();
   __syncthreads();
 }
 
-// Weight prefetch depth: two K steps ahead for small chunks (few MFMAs per step, the
-// loads need the lead), one step for large chunks (64 MFMAs per step already cover the
-// latency, and the third register buffer would not fit beside 256 accumulators).
-template <int NT> struct Prefetch { static constexpr int value = NT <= 4 ? 2 : 1; };
-
-template <int FMT, int NT, int NTT, bool PACKED, bool WEIGHTS_A>
-__device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
-                                       const uint8_t* toks, int K, int row0, int nrows, int ntt, uint8_t* lds,
-                                       int wave, int lane) {
-  constexpr int PF = Prefetch<NT>::value;
+// The K loop of one chunk with WPF = 1: weights of step 0 and token tiles of steps 0 and
+// 1 first; if ks is odd, step 0 alone (its weight buffers then swap by copies); then
+// the steps two at a time (the two weight buffers alternate, roles fixed in the
+// unrolled body). Then as above.
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+__device__ __forceinline__ void k_loop_pf1(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+                                           const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
+                                           int lane) {
+  constexpr int kW = Batch<NT>::kWeights, kT = Batch<NT>::kTokens;
+  constexpr int kBuf = StageLayout<NT>::kBufBytes;
   const int ks = K >> 7;
-  Stage<NTT> st;
-  v8i a0[4], a1[4], a2[4];
-  int s0[4], s1[4], s2[4];
-  stage_load<NTT>(st, tok, toks, K, row0, ntt, 0, wave, lane);
+  v8i a0[4], a1[4];
+  int c0[4], c1[4];
+  load_slots<NT, PACKED, 0>(std::make_integer_sequence<int, kW + kT>{}, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0,
+                            lds, wave, lane);
+  load_slots<NT, PACKED, kW>(std::make_integer_sequence<int, kT>{}, a1, c1, wp, 0, tok, toks, ks, row0, ntt,
+                             min(1, ks - 1), lds + kBuf, wave, lane);
+  int s = 0, cur = 0;
+  if (ks & 1) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
 #pragma unroll
-  for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], 0, lane, a0[q], s0[q]);
-  if (PF == 2) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q) load_weight<PACKED>(wp[q], min(1, ks - 1), lane, a1[q], s1[q]);
+    for (int q = 0; q < 4; ++q) {
+      a0[q] = a1[q];
+      c0[q] = c1[q];
+    }
+    s = 1;
+    cur = 1;
   }
-  stage_store<NT, NTT>(st, lds, ntt, 0, wave, lane);
+  for (; s < ks; s += 2) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(s, ks, cur, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  wait_vmcnt<0>();
   __syncthreads();
-  if constexpr (PF == 2) {
-    // Three register buffers rotate with the K step. The ks % 3 leading steps run one
-    // at a time (rotating the buffers by copies); the loop body then holds three whole
-    // steps with no branch between them.
-    int s = 0;
-    for (const int lead = ks % 3; s < lead; ++s) {
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt,
-                                                 lds, wave, lane);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0[q] = a1[q];
-        s0[q] = s1[q];
-        a1[q] = a2[q];
-        s1[q] = s2[q];
-      }
-    }
-    for (; s < ks; s += 3) {
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s, ks, acc, wp, st, a0, s0, a2, s2, tok, toks, K, row0, nrows, ntt,
-                                                 lds, wave, lane);
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows,
-                                                 ntt, lds, wave, lane);
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 2>(s + 2, ks, acc, wp, st, a2, s2, a1, s1, tok, toks, K, row0, nrows,
-                                                 ntt, lds, wave, lane);
-    }
-  } else {
-    // Two register buffers alternate; the loop body holds two whole K steps with no
-    // branch between them (an odd step count runs its first step alone, with the
-    // buffers swapped afterwards), so every accumulator is updated in place.
-    int s = 0;
-    if (ks & 1) {
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(0, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt,
-                                                 lds, wave, lane);
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        a0[q] = a1[q];
-        s0[q] = s1[q];
-      }
-      s = 1;
-    }
-    for (; s < ks; s += 2) {
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(s, ks, acc, wp, st, a0, s0, a1, s1, tok, toks, K, row0, nrows, ntt,
-                                                 lds, wave, lane);
-      k_step<FMT, NT, NTT, PACKED, WEIGHTS_A, 1>(s + 1, ks, acc, wp, st, a1, s1, a0, s0, tok, toks, K, row0, nrows,
-                                                 ntt, lds, wave, lane);
-    }
-  }
-  (void)a2; (void)s2;
+}
+
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+__device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+                                       const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
+                                       int lane) {
+  if constexpr (WeightPrefetch<NT>::value == 2)
+    k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+  else
+    k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
 }
 
 // Occupancy targets: small token chunks (decode) want several waves per SIMD to keep
@@ -297,7 +374,8 @@ void gmm1_swiglu_kernel(
     const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
     int inter, uint8_t* __restrict__ aq, uint8_t* __restrict__ sa, float* __restrict__ h1) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int ncb = inter >> 7;                 // 128 gate channels per block
   const int n16 = (2 * inter) >> 4;            // 16-channel tiles per expert
@@ -320,7 +398,7 @@ void gmm1_swiglu_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, nrows, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
 
     // A^ goes out in the tiled layout with K = inter, where this block's 128 gate
     // channels are exactly K step cb: the wave's 32 channels are half wave/2 of it,
@@ -379,7 +457,8 @@ void gmm2_combine_kernel(
     int inter, const int32_t* __restrict__ row_token, const float* __restrict__ row_weight,
     float* __restrict__ y_accum, float* __restrict__ o) {
   extern __shared__ __align__(16) uint8_t lds[];
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
   const int ncb = (hidden + 255) >> 8;        // 256 channels per block (64 per wave)
   const int n16 = hidden >> 4;
@@ -403,7 +482,7 @@ void gmm2_combine_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, nrows, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, ntt, lds, wave, lane);
 
     // acc[q][t][i] = O[token row 16t + 4g + i][channel c0 + 16q + r]
 #pragma unroll
@@ -531,7 +610,7 @@ template <int FMT, int NT, bool PACKED>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED>;
   LaunchShape ls;
-  hipError_t e = persistent_shape(kern, 2 * StageLayout<NT>::kBufBytes, &ls);
+  hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
   kern<<<ls.grid, 256, ls.lds, st>>>(p.xq, p.sx, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.aq, p.sa,
                                      p.h1);
@@ -542,7 +621,7 @@ template <int FMT, int NT, bool PACKED>
 hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
   auto kern = gmm2_combine_kernel<FMT, NT, PACKED>;
   LaunchShape ls;
-  hipError_t e = persistent_shape(kern, 2 * StageLayout<NT>::kBufBytes, &ls);
+  hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
   kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.row_token,
                                      p.row_weight, p.y_accum, p.o);

@@ -31,6 +31,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0       # MI355X HBM3E
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.txt")
+COPY_BYTES = 1 << 30        # the plain copy measured for the counter calibration
 MXFP8_PEAK_TFLOPS = 5000.0  # MI355X dense FP8 / MXFP8 MFMA
 RIDGE = MXFP8_PEAK_TFLOPS * 1e12 / (HBM_PEAK_GBS * 1e9)
 
@@ -56,23 +58,81 @@ def library_weights(torch, rp, moe_inputs, cfg, n_experts, shared):
 
 
 def layer_work(cfg, ids):
-    """Algorithmic bytes and flops of the two grouped GEMMs (per launch)."""
+    """Algorithmic bytes and flops per launch of the two grouped GEMMs and the combine:
+    GMM1 reads the touched experts' W1 (codes + 1/32 scales) and the quantized rows, and
+    writes the requantized rows; GMM2 reads W2 and those rows and writes fp32 O; the
+    combine reads fp32 O (and the shared experts' O) and writes bf16 Y."""
     h, i, f = cfg.hidden, cfg.inter, cfg.flat
     touched = int(np.unique(ids).size)
     sc = 1.0 + 1.0 / 32.0
     gmm1_bytes = touched * 2 * i * h * sc + f * h * sc + f * i * sc
-    gmm2_bytes = touched * h * i * sc + f * i * sc + cfg.tokens * h * 4
+    gmm2_bytes = touched * h * i * sc + f * i * sc + f * h * 4
+    combine_bytes = f * h * 4 + cfg.shared * cfg.tokens * h * 4 + cfg.tokens * h * 2
     gmm1_flops = 2.0 * f * h * 2 * i
     gmm2_flops = 2.0 * f * i * h
     if cfg.shared:
         n = cfg.tokens
         gmm1_bytes_s = cfg.shared * (2 * i * h * sc + n * h * sc + n * i * sc)
-        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc)
+        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc + n * h * 4)
         shared = dict(bytes=gmm1_bytes_s + gmm2_bytes_s, flops=cfg.shared * 6.0 * n * h * i)
     else:
         shared = dict(bytes=0.0, flops=0.0)
     return dict(touched=touched, gmm1=dict(bytes=gmm1_bytes, flops=gmm1_flops),
-                gmm2=dict(bytes=gmm2_bytes, flops=gmm2_flops), shared=shared)
+                gmm2=dict(bytes=gmm2_bytes, flops=gmm2_flops), combine=dict(bytes=combine_bytes, flops=0.0),
+                shared=shared)
+
+
+def kernel_source_hash():
+    """sha256 over the library's kernel sources: a measured traffic figure is valid only
+    for the sources it was measured on."""
+    import hashlib
+    h = hashlib.sha256()
+    src = os.path.join(ROOT, "routing_permute_mxfp8_amd", "csrc")
+    for name in sorted(os.listdir(src)):
+        if name.endswith((".hip", ".h", ".cpp")):
+            with open(os.path.join(src, name), "rb") as f:
+                h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(kernel, workload):
+    """HBM bytes per launch of `kernel` on `workload` from the committed rocprofv3 counter
+    summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of the kernel, each scaled by
+    the bytes a plain copy of COPY_BYTES moves per KiB that counter reports for it.
+    None if there is no figure or the kernel sources changed since it was taken."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals, rows = {}, {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            parts = line.split()
+            if not parts or parts[0].startswith("#"):
+                continue
+            if parts[0] == "kernel" and len(parts) >= 9:
+                rows[(parts[1], parts[2])] = dict(zip(parts[3::2], parts[4::2]))
+            elif len(parts) == 2:
+                vals[parts[0]] = float(parts[1])
+    row = rows.get((kernel, workload))
+    if row is None or row.get("source") != kernel_source_hash():
+        return None
+    if not vals.get("copy_fetch_kib") or not vals.get("copy_write_kib"):
+        return None
+    fetch = float(row["fetch_kib"]) * vals["copy_bytes"] / vals["copy_fetch_kib"]
+    write = float(row["write_kib"]) * vals["copy_bytes"] / vals["copy_write_kib"]
+    return round(fetch + write)
+
+
+def calibrate_copy(args, torch):
+    """A plain device copy of COPY_BYTES (read COPY_BYTES, write COPY_BYTES), repeated, for
+    the counter calibration of measured_traffic (run under rocprofv3 --pmc)."""
+    x = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    for _ in range(args.steps):
+        y.copy_(x)
+    torch.cuda.synchronize()
+    print(json.dumps(dict(calibration="copy", bytes_read=COPY_BYTES, bytes_written=COPY_BYTES, copies=args.steps,
+                          source=kernel_source_hash())), flush=True)
 
 
 def roofline_entry(name, ms, work):
@@ -164,11 +224,13 @@ def bench_mega(args, torch, rp, moe_inputs):
         stage_ms[name] = float(np.mean([evs[k][j].elapsed_time(evs[k][j + 1]) for k in range(args.steps)]))
     work = layer_work(cfg, ids)
     roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], work["gmm1"]),
-            "gmm2_combine": roofline_entry("gmm2_combine_kernel", stage_ms["gmm2_combine"], work["gmm2"])}
+            "gmm2": roofline_entry("gmm2_kernel", stage_ms["gmm2"], work["gmm2"]),
+            "combine": roofline_entry("combine_kernel", stage_ms["combine"], work["combine"])}
     dominant = max(roof, key=lambda k: stage_ms[k])
     roofline = dict(roof[dominant])
+    roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name)
     roofline["other"] = {k: v for k, v in roof.items() if k != dominant}
-    total_bytes = work["gmm1"]["bytes"] + work["gmm2"]["bytes"] + work["shared"]["bytes"]
+    total_bytes = work["gmm1"]["bytes"] + work["gmm2"]["bytes"] + work["combine"]["bytes"] + work["shared"]["bytes"]
     total_flops = work["gmm1"]["flops"] + work["gmm2"]["flops"] + work["shared"]["flops"]
     out = dict(metric="MoE layer tokens/s", value=round(cfg.tokens / (ms * 1e-3), 1), unit="tokens/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True,
@@ -242,12 +304,17 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU oracle sample")
     ap.add_argument("--weights", default="packed", choices=["packed", "nd"],
                     help="weight layout: the library's MFMA-native packed layout or the pages' ND layout")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run a plain 1 GiB device copy --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
               "expert-parallel sharding is described in DESIGN.md", file=sys.stderr)
         sys.exit(2)
     import torch
+    if args.calibrate_copy:
+        calibrate_copy(args, torch)
+        return
     import moe_inputs
     import routing_permute_mxfp8_amd as rp
     rp.load()

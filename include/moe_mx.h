@@ -210,11 +210,12 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /* int32 [F] (flat row at each position). F = num_tokens*topk.                    */
 /* stage_events (nullable): MOE_MEGA_STAGE_EVENTS hipEvent_t handles (host array) */
 /* recorded on `stream` at the stage boundaries: [0] start, [1] routing + tile list */
-/* done, [2] gather/quantization done, [3] GMM1 done, [4] accumulator cleared,     */
-/* [5] GMM2 + combine done, [6] shared experts done, [7] bf16 finalize done.        */
+/* done, [2] gather/quantization done, [3] GMM1 done, [4] GMM2 done (O rows        */
+/* written), [5] shared experts done, [6] weighted combine into bf16 y done.        */
+/* The result is deterministic (no atomics on the mega_moe path).                  */
 /* ------------------------------------------------------------------------ */
 enum { MOE_ACT_SWIGLU = 0 };
-#define MOE_MEGA_STAGE_EVENTS 8
+#define MOE_MEGA_STAGE_EVENTS 7
 
 typedef struct {
   const void* x;
@@ -265,7 +266,8 @@ moe_status mega_moe(const moe_mega_args* args /* host */, void* workspace, size_
 /*   w1, w1_scales as in mega_moe with num_groups experts                      */
 /*   aq, sa        device out, fp8 [rows, inter], uint8 [rows, inter/32]       */
 /*   h1            device out, fp32 [rows, 2*inter] or NULL                    */
-/* moe_gmm2_combine: [MM] stages 3-4 for a grouped batch.                     */
+/* moe_gmm2_combine: [MM] stages 3-4 for a grouped batch (O computed, then     */
+/*   scattered into y_accum).                                                    */
 /*   aq, sa        device, fp8 [rows, inter], uint8 [rows, inter/32]           */
 /*   row_token     device, int32 [rows]: token receiving each row             */
 /*   row_weight    device, fp32 [rows]: its combine weight                     */
@@ -275,10 +277,11 @@ moe_status mega_moe(const moe_mega_args* args /* host */, void* workspace, size_
 /* moe_combine_finalize: y (bf16 [num_tokens, hidden]) = RNE(y_accum).         */
 /* Limits as in mega_moe; fp8 = quant_out_dtype (23/24); weights in           */
 /* weight_format. Workspace: moe_gmm_workspace_size (the same for both, given  */
-/* rows, num_groups, hidden and inter; it holds the chunk list and the token   */
+/* rows, num_groups, hidden and inter; it holds the chunk list, the token      */
 /* operands restaged into the kernels' tiled layout, each group padded to 16  */
 /* rows: (rows + 15 * min(rows, num_groups)) * (max(hidden, inter) + inter)   */
-/* bytes of codes plus 1/32 of that for scales, roughly).                      */
+/* bytes of codes plus 1/32 of that for scales, roughly, and an fp32 [rows,    */
+/* hidden] O buffer).                                                          */
 /* ------------------------------------------------------------------------ */
 moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, int64_t hidden, int64_t inter,
                                   size_t* bytes /* host out */);

@@ -59,9 +59,8 @@ class MegaArgs(ctypes.Structure):
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
     ]
 
-MEGA_STAGE_EVENTS = 8
-MEGA_STAGES = ["routing", "permute_quant", "gmm1_swiglu_quant", "zero_accum", "gmm2_combine", "shared_experts",
-               "finalize"]
+MEGA_STAGE_EVENTS = 7
+MEGA_STAGES = ["routing", "permute_quant", "gmm1_swiglu_quant", "gmm2", "shared_experts", "combine"]
 
 
 _lib = None

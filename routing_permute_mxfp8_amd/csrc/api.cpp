@@ -134,7 +134,8 @@ struct MegaWs {
   uint8_t* sx_sh;
   uint8_t* aq_sh;
   uint8_t* sa_sh;
-  float* y_acc;
+  float* o;       // fp32 [F, hidden] expert outputs (sorted rows) unless the caller's o
+  float* o_sh;    // fp32 [num_shared, tokens, hidden]
 };
 
 MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
@@ -166,7 +167,8 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
     w.aq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, i));
     w.sa_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, i));
   }
-  w.y_acc = cv.take<float>((size_t)n * h);
+  w.o = a->o ? nullptr : cv.take<float>((size_t)flat * h);
+  w.o_sh = a->num_shared > 0 ? cv.take<float>((size_t)a->num_shared * n * h) : nullptr;
   return w;
 }
 
@@ -232,6 +234,7 @@ struct GmmWs {
   uint8_t* in_scales;
   uint8_t* out_codes;
   uint8_t* out_scales;
+  float* o;   // fp32 [rows, hidden] GMM2 output when the caller passes no o
 };
 
 GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_t inter) {
@@ -245,6 +248,7 @@ GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_
   w.in_scales = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, kin));
   w.out_codes = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, inter));
   w.out_scales = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, inter));
+  w.o = cv.take<float>((size_t)rows * hidden);
   return w;
 }
 
@@ -511,16 +515,14 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     if (e != hipSuccess) return hip_fail(e, "mega_moe unpack launch");
   }
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  // stages 3-4: GMM2 with the weighted combine into fp32 token rows
-  e = moe::launch_fill_zero(w.y_acc, n * h, st);
-  if (e != hipSuccess) return hip_fail(e, "mega_moe zero-fill launch");
-  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // stage 3: GMM2, O rows in fp32
+  float* o = a->o ? a->o : w.o;
   moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, w.row_token, w.row_weight, w.y_acc, a->o, packed};
+                     (int)h, (int)inter, fmt, w.tt, o, packed};
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
-  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  // shared experts: same FFN over all tokens in token order, added unweighted
+  if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // shared experts: the same FFN over all tokens in token order
   for (int64_t s = 0; s < a->num_shared; ++s) {
     moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + s * 2 * inter * h,
                        a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
@@ -530,15 +532,19 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
     moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter,
                        a->shared_w2_scales + s * group_scale_bytes(h, inter, a->weight_format), w.sh_tiles,
-                       w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, nullptr, nullptr, w.y_acc,
-                       nullptr, packed};
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.o_sh + s * n * h, packed};
     e = moe::launch_gmm2(s2, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
   }
+  if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
+  // stage 4: weighted combine into bf16 y (one rounding, after the sum)
+  moe::CombineParams cp;
+  cp.o = o; cp.pos = w.scat; cp.w = a->topk_weights; cp.w_bf16 = a->topk_weights_dtype == MOE_DTYPE_BF16;
+  cp.topk = (int)a->topk; cp.o_shared = w.o_sh; cp.num_shared = (int)a->num_shared; cp.tokens = n;
+  cp.hidden = (int)h; cp.y = reinterpret_cast<uint16_t*>(a->y);
+  e = moe::launch_combine(cp, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe combine launch");
   if ((e = mark(6)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  e = moe::launch_finalize(w.y_acc, n * h, reinterpret_cast<uint16_t*>(a->y), st);
-  if (e != hipSuccess) return hip_fail(e, "mega_moe finalize launch");
-  if ((e = mark(7)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   return ok();
 }
 
@@ -606,10 +612,11 @@ moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, 
   e = moe::launch_pack_tokens(aq, sa, (int)inter, w.tiles, w.count, w.max_tiles, w.tt, w.in_codes, w.in_scales, st);
   if (e != hipSuccess) return hip_fail(e, "token pack launch");
   moe::Gmm2Params g{w.in_codes, w.in_scales, w2, w2_scales, w.tiles, w.count, w.max_tiles, (int)hidden, (int)inter,
-                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, row_token, row_weight, y_accum, o,
-                    weight_format};
+                    quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1, w.tt, o ? o : w.o, weight_format};
   e = moe::launch_gmm2(g, st);
   if (e != hipSuccess) return hip_fail(e, "gmm2 launch");
+  e = moe::launch_scatter_add(o ? o : w.o, rows, (int)hidden, row_token, row_weight, y_accum, st);
+  if (e != hipSuccess) return hip_fail(e, "scatter-add launch");
   return ok();
 }
 

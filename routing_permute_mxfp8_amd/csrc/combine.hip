@@ -1,0 +1,100 @@
+// Weighted combine of the expert outputs back into token order.
+//
+// MegaMoE README, "A8W8-FP quantization scenario", stage 4: Y[i] = sum_k W[i, k] *
+// O[pi(i, k)], with pi the permutation of the routing (token i's k-th expert row), plus
+// the outputs of the shared experts, which see every token, unweighted; the
+// moe_token_permute article's unpermute direction is the same gather. The expert outputs
+// O are kept in fp32 and Y is rounded to bf16 once, after the sum.
+//
+// One block per token: each thread owns 4 consecutive channels (16-byte loads of the
+// K expert rows and the shared rows, summed in the order k = 0..K-1, then the shared
+// experts in order), and writes 8 bytes of bf16.
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ pos,
+                                                      const void* __restrict__ wts, int w_bf16, int topk,
+                                                      const float* __restrict__ o_shared, int num_shared,
+                                                      int64_t tokens, int hidden, uint16_t* __restrict__ y) {
+  const int h4 = hidden >> 2;
+  for (int64_t t = blockIdx.x; t < tokens; t += gridDim.x) {
+    for (int c = threadIdx.x; c < h4; c += blockDim.x) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+      for (int k = 0; k < topk; ++k) {
+        const int64_t f = t * topk + k;
+        const int p = pos[f];
+        if (p < 0) continue;
+        const float w = w_bf16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(wts)[f])
+                               : reinterpret_cast<const float*>(wts)[f];
+        const float4 v = reinterpret_cast<const float4*>(o + (int64_t)p * hidden)[c];
+        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+      }
+      for (int s = 0; s < num_shared; ++s) {
+        const float4 v = reinterpret_cast<const float4*>(o_shared + ((int64_t)s * tokens + t) * hidden)[c];
+        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+      }
+      uint2 out;
+      out.x = (uint32_t)f_to_bf16(acc.x) | ((uint32_t)f_to_bf16(acc.y) << 16);
+      out.y = (uint32_t)f_to_bf16(acc.z) | ((uint32_t)f_to_bf16(acc.w) << 16);
+      reinterpret_cast<uint2*>(y + t * hidden)[c] = out;
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void scatter_add_kernel(const float* __restrict__ o, int64_t rows, int hidden,
+                                                          const int32_t* __restrict__ row_token,
+                                                          const float* __restrict__ row_weight,
+                                                          float* __restrict__ y_accum) {
+  for (int64_t r = blockIdx.x; r < rows; r += gridDim.x) {
+    const int64_t tok = row_token[r];
+    const float w = row_weight[r];
+    for (int c = threadIdx.x; c < hidden; c += blockDim.x)
+      unsafeAtomicAdd(y_accum + tok * hidden + c, w * o[r * hidden + c]);
+  }
+}
+
+__global__ void finalize_kernel(const float* __restrict__ acc, int64_t n, uint16_t* __restrict__ y) {
+  const int64_t n4 = n >> 2;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
+    const float4 v = reinterpret_cast<const float4*>(acc)[i];
+    uint2 out;
+    out.x = (uint32_t)f_to_bf16(v.x) | ((uint32_t)f_to_bf16(v.y) << 16);
+    out.y = (uint32_t)f_to_bf16(v.z) | ((uint32_t)f_to_bf16(v.w) << 16);
+    reinterpret_cast<uint2*>(y)[i] = out;
+  }
+  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
+    y[i] = f_to_bf16(acc[i]);
+}
+
+}  // namespace
+
+hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
+  if (p.tokens <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(p.tokens, 65536);
+  combine_kernel<<<grid, 256, 0, st>>>(p.o, p.pos, p.w, p.w_bf16, p.topk, p.o_shared, p.num_shared, p.tokens,
+                                       p.hidden, p.y);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_add(const float* o, int64_t rows, int hidden, const int32_t* row_token,
+                              const float* row_weight, float* y_accum, hipStream_t st) {
+  if (rows <= 0) return hipSuccess;
+  const unsigned grid = (unsigned)std::min<int64_t>(rows, 65536);
+  scatter_add_kernel<<<grid, 256, 0, st>>>(o, rows, hidden, row_token, row_weight, y_accum);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t st) {
+  if (count <= 0) return hipSuccess;
+  const int64_t blocks = std::min<int64_t>((count / 4 + 255) / 256 + 1, 65536);
+  finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(acc, count, y);
+  return hipGetLastError();
+}
+
+}  // namespace moe

@@ -448,14 +448,17 @@ void gmm1_swiglu_kernel(
   }
 }
 
-// ---- GMM2 + weighted combine -------------------------------------------------------
+// ---- GMM2 ---------------------------------------------------------------------------
+// O rows (fp32, sorted-row order) go out with plain stores; the weighted combine reads
+// them back per token (combine.hip). Combining here with fp32 atomics would send every
+// add to memory: a token's K rows are computed on different XCDs, whose L2s are not
+// coherent, so device-scope atomics are not resolved in L2.
 template <int FMT, int NT, bool PACKED>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
-void gmm2_combine_kernel(
+void gmm2_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
-    int inter, const int32_t* __restrict__ row_token, const float* __restrict__ row_weight,
-    float* __restrict__ y_accum, float* __restrict__ o) {
+    int inter, float* __restrict__ o) {
   extern __shared__ __align__(16) uint8_t lds[];
   // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -492,15 +495,9 @@ void gmm2_combine_kernel(
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * t + 4 * g + i;
         if (rr >= nrows) continue;
-        const int64_t row = srow0 + rr;
-        const int64_t tok = row_token ? (int64_t)row_token[row] : row;
-        const float wgt = row_token ? row_weight[row] : 1.0f;
-        float* yrow = y_accum + tok * hidden + c0 + r;
+        float* orow = o + (int64_t)(srow0 + rr) * hidden + c0 + r;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          unsafeAtomicAdd(yrow + 16 * q, wgt * acc[q][t][i]);
-          if (o) o[row * hidden + c0 + 16 * q + r] = acc[q][t][i];
-        }
+        for (int q = 0; q < 4; ++q) orow[16 * q] = acc[q][t][i];
       }
     }
   }
@@ -552,27 +549,6 @@ __global__ void single_group_tiles_kernel(int rows, int tm, int4* __restrict__ t
   if (blockIdx.x == 0 && threadIdx.x == 0) *count = nt;
 }
 
-__global__ void fill_zero_kernel(float* __restrict__ p, int64_t n) {
-  const int64_t n4 = n >> 2;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x)
-    reinterpret_cast<float4*>(p)[i] = make_float4(0.f, 0.f, 0.f, 0.f);
-  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    p[i] = 0.f;
-}
-
-__global__ void finalize_kernel(const float* __restrict__ acc, int64_t n, uint16_t* __restrict__ y) {
-  const int64_t n4 = n >> 2;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += (int64_t)gridDim.x * blockDim.x) {
-    const float4 v = reinterpret_cast<const float4*>(acc)[i];
-    uint2 out;
-    out.x = (uint32_t)f_to_bf16(v.x) | ((uint32_t)f_to_bf16(v.y) << 16);
-    out.y = (uint32_t)f_to_bf16(v.z) | ((uint32_t)f_to_bf16(v.w) << 16);
-    reinterpret_cast<uint2*>(y)[i] = out;
-  }
-  for (int64_t i = (n4 << 2) + (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x)
-    y[i] = f_to_bf16(acc[i]);
-}
-
 // ---- launch helpers: persistent grid = CUs x resident blocks per CU (multiple of 8) --
 struct LaunchShape {
   int grid = 0;
@@ -619,12 +595,11 @@ hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
 
 template <int FMT, int NT, bool PACKED>
 hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
-  auto kern = gmm2_combine_kernel<FMT, NT, PACKED>;
+  auto kern = gmm2_kernel<FMT, NT, PACKED>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
-  kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.row_token,
-                                     p.row_weight, p.y_accum, p.o);
+  kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.o);
   return hipGetLastError();
 }
 
@@ -686,24 +661,6 @@ hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t st) {
   single_group_tiles_kernel<<<64, 256, 0, st>>>(rows, tm, tiles, count);
-  return hipGetLastError();
-}
-
-hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t st) {
-  if (count <= 0) return hipSuccess;
-  int64_t blocks = (count / 4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  fill_zero_kernel<<<(unsigned)blocks, 256, 0, st>>>(p, count);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t st) {
-  if (count <= 0) return hipSuccess;
-  int64_t blocks = (count / 4 + 255) / 256;
-  if (blocks > 4096) blocks = 4096;
-  if (blocks < 1) blocks = 1;
-  finalize_kernel<<<(unsigned)blocks, 256, 0, st>>>(acc, count, y);
   return hipGetLastError();
 }
 

@@ -112,10 +112,7 @@ struct Gmm2Params {
   const uint8_t* w; const uint8_t* ws;         // [G, H, I], [G, H, I/32]
   const int4* tiles; const int* tile_count; int max_tiles;
   int hidden, inter, fmt, tt;
-  const int32_t* row_token;                    // nullptr: token = row, weight 1
-  const float* row_weight;
-  float* y_accum;                              // [tokens, H]
-  float* o;                                    // nullable [rows, H]
+  float* o;                                    // [rows, H] fp32, sorted rows
   int packed;
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
@@ -130,7 +127,27 @@ hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 
 // Chunks of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), i*tm}.
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);
-hipError_t launch_fill_zero(float* p, int64_t count, hipStream_t stream);
+
+// ---- weighted combine (combine.hip) -------------------------------------------------
+// Y[t] = bf16(sum_k w[t, k] * O[pos[t*K + k]] + sum_s O_shared[s][t]) for every token t:
+// O [rows, H] fp32 in sorted-row order, pos the scatter index (flat row -> sorted row,
+// -1 = none), w fp32 or bf16 [tokens * K], O_shared [num_shared][tokens, H] or null.
+struct CombineParams {
+  const float* o = nullptr;
+  const int32_t* pos = nullptr;
+  const void* w = nullptr;
+  int w_bf16 = 0;
+  int topk = 1;
+  const float* o_shared = nullptr;
+  int num_shared = 0;
+  int64_t tokens = 0;
+  int hidden = 0;                  // multiple of 4
+  uint16_t* y = nullptr;           // bf16 [tokens, H]
+};
+hipError_t launch_combine(const CombineParams& p, hipStream_t stream);
+// y_accum[row_token[r]] += row_weight[r] * O[r] (fp32 atomics), rows [0, rows).
+hipError_t launch_scatter_add(const float* o, int64_t rows, int hidden, const int32_t* row_token,
+                              const float* row_weight, float* y_accum, hipStream_t stream);
 hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t stream);
 
 }  // namespace moe

@@ -72,6 +72,7 @@ void route_chunks(int64_t flat, int active, int* nch, int* chunk) {
 struct RouteWs {
   int* hist;
   int* base;
+  int* totals;
   int* offsets;
 };
 
@@ -80,6 +81,7 @@ RouteWs carve_route(Carver& cv, int64_t flat, int active, int* nch, int* chunk) 
   RouteWs w;
   w.hist = cv.take<int>((size_t)*nch * std::max(active, 1));
   w.base = cv.take<int>((size_t)*nch * std::max(active, 1));
+  w.totals = cv.take<int>((size_t)std::max(active, 1));
   w.offsets = cv.take<int>((size_t)active + 1);
   return w;
 }
@@ -365,7 +367,7 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   moe::RouteParams rp;
   rp.keys = expert_idx; rp.key_is64 = 0; rp.flat = flat; rp.topk = (int)k;
   rp.s = (int)active_start; rp.e = (int)active_end; rp.nch = ws.nch; rp.chunk = ws.chunk;
-  rp.hist = ws.r.hist; rp.base = ws.r.base; rp.offsets = ws.r.offsets;
+  rp.hist = ws.r.hist; rp.base = ws.r.base; rp.totals = ws.r.totals; rp.offsets = ws.r.offsets;
   rp.avail64 = available_idx_num; rp.expert_tokens = expert_tokens; rp.tokens_type = expert_tokens_num_type;
   if (want_gather) {
     rp.scat = ws.scat; rp.gath = expanded_row_idx; rp.gath_fill = expanded_row_idx;
@@ -429,7 +431,7 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
   moe::RouteParams rp;
   rp.keys = indices; rp.key_is64 = indices_dtype == MOE_DTYPE_INT64; rp.flat = flat; rp.topk = (int)topk;
   rp.s = 0; rp.e = (int)num_experts; rp.nch = nch; rp.chunk = chunk;
-  rp.hist = rw.hist; rp.base = rw.base; rp.offsets = rw.offsets; rp.scat = sorted_indices;
+  rp.hist = rw.hist; rp.base = rw.base; rp.totals = rw.totals; rp.offsets = rw.offsets; rp.scat = sorted_indices;
   hipError_t e = moe::launch_routing(rp, st);
   if (e != hipSuccess) return hip_fail(e, "moe_token_permute routing launch");
   moe::PermuteParams pp;
@@ -469,7 +471,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   // stage 1a: routing (full expert range, scatter + gather forms, combine row maps)
   moe::RouteParams rp;
   rp.keys = a->topk_ids; rp.flat = flat; rp.topk = (int)a->topk; rp.s = 0; rp.e = (int)ne;
-  rp.nch = w.nch; rp.chunk = w.chunk; rp.hist = w.r.hist; rp.base = w.r.base; rp.offsets = w.r.offsets;
+  rp.nch = w.nch; rp.chunk = w.chunk; rp.hist = w.r.hist; rp.base = w.r.base; rp.totals = w.r.totals; rp.offsets = w.r.offsets;
   rp.token_nums32 = a->expert_token_nums; rp.scat = w.scat; rp.gath = gath;
   rp.row_token = w.row_token; rp.row_weight = w.row_weight; rp.topk_w = a->topk_weights;
   rp.topk_w_bf16 = a->topk_weights_dtype == MOE_DTYPE_BF16;

@@ -6,9 +6,9 @@
 // moe_token_permute article's unpermute direction is the same gather. The expert outputs
 // O are kept in fp32 and Y is rounded to bf16 once, after the sum.
 //
-// One block per token: each thread owns 4 consecutive channels (16-byte loads of the
-// K expert rows and the shared rows, summed in the order k = 0..K-1, then the shared
-// experts in order), and writes 8 bytes of bf16.
+// Each thread owns 4 consecutive channels of one token (16-byte loads of the K expert
+// rows and the shared rows, summed in the order k = 0..K-1, then the shared experts in
+// order) and writes 8 bytes of bf16.
 
 #include <algorithm>
 
@@ -18,32 +18,55 @@
 namespace moe {
 namespace {
 
+__device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
+  acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
+}
+
+// Block b covers token b / slices and 1024 channels (256 threads x 4) of it, so that few
+// tokens still fill the chip. The K rows are loaded four at a time, all four loads in
+// flight before their products are added (in order k = 0..K-1).
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ pos,
                                                       const void* __restrict__ wts, int w_bf16, int topk,
                                                       const float* __restrict__ o_shared, int num_shared,
                                                       int64_t tokens, int hidden, uint16_t* __restrict__ y) {
   const int h4 = hidden >> 2;
-  for (int64_t t = blockIdx.x; t < tokens; t += gridDim.x) {
-    for (int c = threadIdx.x; c < h4; c += blockDim.x) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-      for (int k = 0; k < topk; ++k) {
-        const int64_t f = t * topk + k;
-        const int p = pos[f];
-        if (p < 0) continue;
-        const float w = w_bf16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(wts)[f])
-                               : reinterpret_cast<const float*>(wts)[f];
-        const float4 v = reinterpret_cast<const float4*>(o + (int64_t)p * hidden)[c];
-        acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
-      }
-      for (int s = 0; s < num_shared; ++s) {
-        const float4 v = reinterpret_cast<const float4*>(o_shared + ((int64_t)s * tokens + t) * hidden)[c];
-        acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
-      }
-      uint2 out;
-      out.x = (uint32_t)f_to_bf16(acc.x) | ((uint32_t)f_to_bf16(acc.y) << 16);
-      out.y = (uint32_t)f_to_bf16(acc.z) | ((uint32_t)f_to_bf16(acc.w) << 16);
-      reinterpret_cast<uint2*>(y + t * hidden)[c] = out;
+  const int slices = (h4 + 255) >> 8;
+  const int64_t nblk = tokens * slices;
+  for (int64_t b = blockIdx.x; b < nblk; b += gridDim.x) {
+    const int64_t t = b / slices;
+    const int c = (int)(b - t * slices) * 256 + (int)threadIdx.x;
+    if (c >= h4) continue;
+    auto weight = [&](int64_t f) {
+      return w_bf16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(wts)[f]) : reinterpret_cast<const float*>(wts)[f];
+    };
+    auto row = [&](int p) { return reinterpret_cast<const float4*>(o + (int64_t)p * hidden)[c]; };
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    int k = 0;
+    for (; k + 4 <= topk; k += 4) {
+      const int64_t f = t * topk + k;
+      int p[4];
+      float4 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) p[j] = pos[f + j];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) v[j] = row(p[j] < 0 ? 0 : p[j]);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (p[j] >= 0) fma4(acc, weight(f + j), v[j]);
     }
+    for (; k < topk; ++k) {
+      const int64_t f = t * topk + k;
+      const int p = pos[f];
+      if (p >= 0) fma4(acc, weight(f), row(p));
+    }
+    for (int s = 0; s < num_shared; ++s) {
+      const float4 v = reinterpret_cast<const float4*>(o_shared + ((int64_t)s * tokens + t) * hidden)[c];
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    uint2 out;
+    out.x = (uint32_t)f_to_bf16(acc.x) | ((uint32_t)f_to_bf16(acc.y) << 16);
+    out.y = (uint32_t)f_to_bf16(acc.z) | ((uint32_t)f_to_bf16(acc.w) << 16);
+    reinterpret_cast<uint2*>(y + t * hidden)[c] = out;
   }
 }
 
@@ -76,7 +99,8 @@ __global__ void finalize_kernel(const float* __restrict__ acc, int64_t n, uint16
 
 hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
   if (p.tokens <= 0) return hipSuccess;
-  const unsigned grid = (unsigned)std::min<int64_t>(p.tokens, 65536);
+  const int64_t slices = ((p.hidden >> 2) + 255) >> 8;
+  const unsigned grid = (unsigned)std::min<int64_t>(p.tokens * slices, 1 << 20);
   combine_kernel<<<grid, 256, 0, st>>>(p.o, p.pos, p.w, p.w_bf16, p.topk, p.o_shared, p.num_shared, p.tokens,
                                        p.hidden, p.y);
   return hipGetLastError();

@@ -18,8 +18,9 @@ struct RouteParams {
   int s = 0, e = 0;             // active experts [s, e); A = e - s buckets
   int nch = 1, chunk = 64;
   // workspace
-  int* hist = nullptr;          // [nch * A], chunk-major
-  int* base = nullptr;          // [nch * A], chunk-major: first position of (chunk, expert)
+  int* hist = nullptr;          // [A * nch], expert-major: rows of (expert, chunk)
+  int* base = nullptr;          // [A * nch], expert-major: rows of the expert in earlier chunks
+  int* totals = nullptr;        // [A] rows per active expert
   int* offsets = nullptr;       // [A + 1] exclusive prefix of the active counts
   // outputs (nullable unless stated)
   int64_t* avail64 = nullptr;   // availableIdxNum

@@ -8,11 +8,12 @@
 // Expert ids are small integers (E <= 10240), so the sort is a three-pass counting
 // sort instead of a comparison sort:
 //   1. route_count   one workgroup per chunk of flat rows, LDS histogram over the
-//                    active experts, written chunk-major;
-//   2. route_scan    one workgroup, exclusive scan in expert-major, chunk-minor order:
-//                    base[c][a] = rows of experts < a + rows of expert a in chunks < c,
-//                    i.e. the first sorted position of (chunk c, expert a); also the
-//                    per-expert counts / cumsum and availableIdxNum;
+//                    active experts, written expert-major (hist[a][c]);
+//   2. route_scan    one wave per expert: exclusive scan of its row counts over the
+//                    chunks (base[a][c] = rows of expert a in chunks < c) and its total;
+//      route_offsets one workgroup: exclusive scan of the totals over the experts
+//                    (offsets, per-expert counts / cumsum, availableIdxNum). The first
+//                    sorted position of (chunk c, expert a) is offsets[a] + base[a][c];
 //   3. route_scatter one wave per chunk walks its rows in order, 64 at a time. The rank
 //                    of a row among the earlier lanes with the same expert comes from a
 //                    bit-sliced match: one ballot per bit of the expert id, AND-ed per
@@ -42,7 +43,7 @@ __global__ __launch_bounds__(256) void route_count(const KeyT* __restrict__ keys
     if (a >= 0 && a < A) atomicAdd(&lds_hist[a], 1);
   }
   __syncthreads();
-  for (int a = threadIdx.x; a < A; a += blockDim.x) hist[(int64_t)c * A + a] = lds_hist[a];
+  for (int a = threadIdx.x; a < A; a += blockDim.x) hist[(int64_t)a * gridDim.x + c] = lds_hist[a];
 }
 
 // Inclusive scan (sum, or max when MAX) of one int per thread over a 1024-thread block
@@ -61,38 +62,50 @@ __device__ int block_inclusive_scan_1024(int v, int* part) {
   return part[t];
 }
 
-__global__ __launch_bounds__(1024) void route_scan(const int* __restrict__ hist, int nch, int A,
-                                                   int* __restrict__ base, int* __restrict__ offsets,
-                                                   int64_t* avail64, int64_t* expert_tokens,
-                                                   int tokens_type, int32_t* token_nums32) {
-  __shared__ int part[1024];
-  extern __shared__ int lds_off[];  // A + 1
-  const int t = threadIdx.x;
-  const int64_t L = (int64_t)A * nch;
-  const int64_t P = (L + 1023) / 1024;
-  const int64_t j0 = min(L, t * P), j1 = min(L, j0 + P);
-  int sum = 0;
-  for (int64_t j = j0; j < j1; ++j) {
-    const int64_t a = j / nch, c = j - a * nch;
-    sum += hist[c * A + a];
+// Exclusive scan of one expert's chunk counts (one wave per expert, 64 chunks per step,
+// shuffle scan within the wave, the running total carried across steps).
+__global__ __launch_bounds__(64) void route_scan(const int* __restrict__ hist, int nch, int* __restrict__ base,
+                                                 int* __restrict__ totals) {
+  const int a = blockIdx.x, lane = threadIdx.x;
+  const int* h = hist + (int64_t)a * nch;
+  int* b = base + (int64_t)a * nch;
+  int carry = 0;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nch ? h[c] : 0;
+    int incl = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int x = __shfl_up(incl, d);
+      if (lane >= d) incl += x;
+    }
+    if (c < nch) b[c] = carry + incl - v;
+    carry += __shfl(incl, 63);
   }
+  if (lane == 0) totals[a] = carry;
+}
+
+__global__ __launch_bounds__(1024) void route_offsets(const int* __restrict__ totals, int A, int* __restrict__ offsets,
+                                                      int64_t* avail64, int64_t* expert_tokens, int tokens_type,
+                                                      int32_t* token_nums32) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int P = (A + 1023) / 1024;
+  const int a0 = min(A, t * P), a1 = min(A, a0 + P);
+  int sum = 0;
+  for (int a = a0; a < a1; ++a) sum += totals[a];
   const int incl = block_inclusive_scan_1024(sum, part);
   int run = incl - sum;
-  for (int64_t j = j0; j < j1; ++j) {
-    const int64_t a = j / nch, c = j - a * nch;
-    base[c * A + a] = run;
-    if (c == 0) lds_off[a] = run;
-    run += hist[c * A + a];
-  }
-  const int total = part[1023];
-  if (t == 0) lds_off[A] = total;
-  __syncthreads();
-  for (int a = t; a <= A; a += 1024) offsets[a] = lds_off[a];
-  if (t == 0 && avail64) *avail64 = total;
-  for (int a = t; a < A; a += 1024) {
-    const int cnt = lds_off[a + 1] - lds_off[a];
-    if (expert_tokens) expert_tokens[a] = tokens_type == 1 ? (int64_t)cnt : (int64_t)lds_off[a + 1];
+  for (int a = a0; a < a1; ++a) {
+    const int cnt = totals[a];
+    offsets[a] = run;
+    run += cnt;
+    if (expert_tokens) expert_tokens[a] = tokens_type == 1 ? (int64_t)cnt : (int64_t)run;
     if (token_nums32) token_nums32[a] = cnt;
+  }
+  if (t == 1023) {
+    offsets[A] = part[1023];
+    if (avail64) *avail64 = part[1023];
   }
 }
 
@@ -105,7 +118,7 @@ __global__ __launch_bounds__(64) void route_scatter(
   extern __shared__ int cursor[];  // A
   const int c = blockIdx.x;
   const int lane = threadIdx.x;
-  for (int a = lane; a < A; a += 64) cursor[a] = base[(int64_t)c * A + a];
+  for (int a = lane; a < A; a += 64) cursor[a] = offsets[a] + base[(int64_t)a * gridDim.x + c];
   __syncthreads();
   const int64_t lo = (int64_t)c * chunk;
   const int64_t hi = min(flat, lo + chunk);
@@ -208,8 +221,9 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
     else
       route_count<int32_t><<<p.nch, 256, lds_a, stream>>>((const int32_t*)p.keys, p.flat, p.s, A, p.chunk, p.hist);
   }
-  route_scan<<<1, 1024, sizeof(int) * (size_t)(A + 1), stream>>>(p.hist, p.nch, A, p.base, p.offsets, p.avail64,
-                                                                 p.expert_tokens, p.tokens_type, p.token_nums32);
+  if (A > 0) route_scan<<<A, 64, 0, stream>>>(p.hist, p.nch, p.base, p.totals);
+  route_offsets<<<1, 1024, 0, stream>>>(p.totals, A, p.offsets, p.avail64, p.expert_tokens, p.tokens_type,
+                                        p.token_nums32);
   int nbits = 0;
   while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
   if (p.key_is64)

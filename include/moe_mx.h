@@ -208,7 +208,8 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /* [F, 2*inter] (G then U); aq/sa the stage-2 requantized activations            */
 /* [F, inter] / [F, inter/32]; o fp32 [F, hidden] (unweighted); sorted_row_idx    */
 /* int32 [F] (flat row at each position). F = num_tokens*topk.                    */
-/* stage_events (nullable): MOE_MEGA_STAGE_EVENTS hipEvent_t handles (host array) */
+/* stage_events (nullable): MOE_MEGA_STAGE_EVENTS hipEvent_t handles (host array, */
+/* NULL entries skipped; a timed record costs a few microseconds of GPU time)     */
 /* recorded on `stream` at the stage boundaries: [0] start, [1] routing + tile list */
 /* done, [2] gather/quantization done, [3] GMM1 done, [4] GMM2 done (O rows        */
 /* written), [5] shared experts done, [6] weighted combine into bf16 y done.        */

@@ -259,8 +259,9 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     over the shared experts. workspace: optional preallocated uint8 device tensor.
     weight_format: WEIGHTS_ND (the pages' layout) or WEIGHTS_PACKED (w1/w2 and the
     shared weights as returned by pack_weights; the code tensors keep their [E, N, K] shape).
-    stage_events: optional list of MEGA_STAGE_EVENTS torch.cuda.Event(enable_timing=True),
-    recorded by the library on the stream at the boundaries of MEGA_STAGES."""
+    stage_events: optional list of MEGA_STAGE_EVENTS torch.cuda.Event(enable_timing=True) or
+    None entries, recorded by the library on the stream at the boundaries of MEGA_STAGES
+    (a None entry is skipped; each record costs a few microseconds of GPU time)."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
     n, h = x.shape
@@ -284,10 +285,12 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
                      weight_format)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
-            raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} events")
+            raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} entries (events or None)")
         for ev in stage_events:
-            ev.record()   # make sure the underlying HIP event exists before the library records it
-        handles = (ctypes.c_void_p * MEGA_STAGE_EVENTS)(*[ev.cuda_event for ev in stage_events])
+            if ev is not None and not ev.cuda_event:
+                ev.record()   # torch creates the HIP event at its first record
+        handles = (ctypes.c_void_p * MEGA_STAGE_EVENTS)(*[ev.cuda_event if ev is not None else None
+                                                          for ev in stage_events])
         a.stage_events = ctypes.cast(handles, ctypes.POINTER(ctypes.c_void_p))
     nbytes = ctypes.c_size_t()
     _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))

@@ -461,7 +461,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   MegaWs w = carve_mega(wc, a);
   hipStream_t st = (hipStream_t)stream;
   auto mark = [&](int k) -> hipError_t {
-    return a->stage_events ? hipEventRecord((hipEvent_t)a->stage_events[k], st) : hipSuccess;
+    return a->stage_events && a->stage_events[k] ? hipEventRecord((hipEvent_t)a->stage_events[k], st) : hipSuccess;
   };
   const int64_t n = a->num_tokens, h = a->hidden, inter = a->inter, ne = a->num_experts;
   const int64_t flat = n * a->topk;

@@ -11,8 +11,8 @@
 // in range, otherwise reads the bf16 row once, quantizes it once and stores the
 // same codes to every destination. Each lane owns 8 consecutive elements (one
 // 16-byte load), so a 32-element group is a DPP quad and its amax takes two
-// quad_perm max steps; a wave covers 512 elements per step and the loads of up to
-// 8 steps are issued before any store.
+// quad_perm max steps; a wave covers 512 elements per step and the loads of
+// kUnroll steps are issued before any store.
 
 #include "device_common.h"
 #include "internal.h"
@@ -20,7 +20,9 @@
 namespace moe {
 namespace {
 
-constexpr int kUnroll = 8;
+// Vectors (8 elements) per lane in flight per step: 4 measured fastest on the
+// 32768 x 7168 bf16 routing workload (8 and 16 cut occupancy).
+constexpr int kUnroll = 4;
 
 template <typename InT> struct Load8;
 template <> struct Load8<uint16_t> {  // bf16
@@ -108,7 +110,9 @@ __global__ __launch_bounds__(256) void permute_mx_kernel(
         for (uint64_t dm = dmask; dm; dm &= dm - 1) {
           const int k = __builtin_ctzll(dm);
           const int64_t d = __builtin_amdgcn_readlane(dest, k);
-          *reinterpret_cast<uint2*>(out + d * hidden + (int64_t)v * 8) = q;
+          // the permuted rows are written once and not read back here: non-temporal
+          __builtin_nontemporal_store(((uint64_t)q.y << 32) | q.x,
+                                      reinterpret_cast<uint64_t*>(out + d * hidden + (int64_t)v * 8));
           if (scale_lane) out_scales[d * scale_cols + (v >> 2)] = (uint8_t)b;
         }
         if (tok_out) {

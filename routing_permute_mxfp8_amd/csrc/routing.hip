@@ -13,7 +13,9 @@
 //                    chunks (base[a][c] = rows of expert a in chunks < c) and its total;
 //      route_offsets one workgroup: exclusive scan of the totals over the experts
 //                    (offsets, per-expert counts / cumsum, availableIdxNum). The first
-//                    sorted position of (chunk c, expert a) is offsets[a] + base[a][c];
+//                    sorted position of (chunk c, expert a) is offsets[a] + base[a][c].
+//                    When the histogram fits in LDS (A * chunks <= kFusedScan) both run
+//                    as one workgroup (route_scan_fused), one launch instead of two;
 //   3. route_scatter one wave per chunk walks its rows in order, 64 at a time. The rank
 //                    of a row among the earlier lanes with the same expert comes from a
 //                    bit-sliced match: one ballot per bit of the expert id, AND-ed per
@@ -85,19 +87,19 @@ __global__ __launch_bounds__(64) void route_scan(const int* __restrict__ hist, i
   if (lane == 0) totals[a] = carry;
 }
 
-__global__ __launch_bounds__(1024) void route_offsets(const int* __restrict__ totals, int A, int* __restrict__ offsets,
-                                                      int64_t* avail64, int64_t* expert_tokens, int tokens_type,
-                                                      int32_t* token_nums32) {
-  __shared__ int part[1024];
+// Exclusive scan over the experts of the totals held by every thread in tot[a0, a1)
+// (the thread's contiguous share), writing the routing summaries. part: 1024 ints.
+__device__ void offsets_from_totals(const int* tot, int A, int* part, int* __restrict__ offsets, int64_t* avail64,
+                                    int64_t* expert_tokens, int tokens_type, int32_t* token_nums32) {
   const int t = threadIdx.x;
   const int P = (A + 1023) / 1024;
   const int a0 = min(A, t * P), a1 = min(A, a0 + P);
   int sum = 0;
-  for (int a = a0; a < a1; ++a) sum += totals[a];
+  for (int a = a0; a < a1; ++a) sum += tot[a];
   const int incl = block_inclusive_scan_1024(sum, part);
   int run = incl - sum;
   for (int a = a0; a < a1; ++a) {
-    const int cnt = totals[a];
+    const int cnt = tot[a];
     offsets[a] = run;
     run += cnt;
     if (expert_tokens) expert_tokens[a] = tokens_type == 1 ? (int64_t)cnt : (int64_t)run;
@@ -107,6 +109,64 @@ __global__ __launch_bounds__(1024) void route_offsets(const int* __restrict__ to
     offsets[A] = part[1023];
     if (avail64) *avail64 = part[1023];
   }
+}
+
+constexpr int kFusedScan = 14336;   // ints (histogram + totals) route_scan_fused holds in LDS (56 KB)
+
+// route_scan + route_offsets in one workgroup of 16 waves: the histogram is loaded into
+// LDS with coalesced loads; each expert's chunk counts are scanned by one thread (32 or
+// fewer chunks) or one wave (experts wave, wave + 16, ...); then the totals are scanned
+// over the experts.
+__global__ __launch_bounds__(1024) void route_scan_fused(const int* __restrict__ hist, int nch, int A,
+                                                         int* __restrict__ base, int* __restrict__ offsets,
+                                                         int64_t* avail64, int64_t* expert_tokens, int tokens_type,
+                                                         int32_t* token_nums32) {
+  __shared__ int part[1024];
+  extern __shared__ int lds[];   // hist [A * nch], then totals [A]
+  int* tot = lds + A * nch;
+  const int L = A * nch;
+  for (int j = threadIdx.x; j < L; j += 1024) lds[j] = hist[j];
+  __syncthreads();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (nch <= 32) {   // few chunks: one thread per expert walks its chunk counts
+    for (int a = threadIdx.x; a < A; a += 1024) {
+      const int* h = lds + a * nch;
+      int* b = base + (int64_t)a * nch;
+      int run = 0;
+      for (int c = 0; c < nch; ++c) {
+        b[c] = run;
+        run += h[c];
+      }
+      tot[a] = run;
+    }
+  }
+  for (int a = nch <= 32 ? A : wave; a < A; a += 16) {
+    const int* h = lds + a * nch;
+    int* b = base + (int64_t)a * nch;
+    int carry = 0;
+    for (int c0 = 0; c0 < nch; c0 += 64) {
+      const int c = c0 + lane;
+      const int v = c < nch ? h[c] : 0;
+      int incl = v;
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int x = __shfl_up(incl, d);
+        if (lane >= d) incl += x;
+      }
+      if (c < nch) b[c] = carry + incl - v;
+      carry += __shfl(incl, 63);
+    }
+    if (lane == 0) tot[a] = carry;
+  }
+  __syncthreads();
+  offsets_from_totals(tot, A, part, offsets, avail64, expert_tokens, tokens_type, token_nums32);
+}
+
+__global__ __launch_bounds__(1024) void route_offsets(const int* __restrict__ totals, int A, int* __restrict__ offsets,
+                                                      int64_t* avail64, int64_t* expert_tokens, int tokens_type,
+                                                      int32_t* token_nums32) {
+  __shared__ int part[1024];
+  offsets_from_totals(totals, A, part, offsets, avail64, expert_tokens, tokens_type, token_nums32);
 }
 
 template <typename KeyT>
@@ -122,38 +182,53 @@ __global__ __launch_bounds__(64) void route_scatter(
   __syncthreads();
   const int64_t lo = (int64_t)c * chunk;
   const int64_t hi = min(flat, lo + chunk);
-  for (int64_t r0 = lo; r0 < hi; r0 += 64) {
-    const int64_t r = r0 + lane;
-    const bool valid = r < hi;
-    int a = A;  // sentinel for rows outside the active range (and past the end)
-    if (valid) {
-      const int64_t d = (int64_t)keys[r] - s;
-      if (d >= 0 && d < A) a = (int)d;
+  // The keys of 16 steps (1024 rows) are loaded before they are walked, so the walk
+  // pays the memory latency once per 1024 rows instead of once per 64.
+  constexpr int kPre = 16;
+  for (int64_t r1 = lo; r1 < hi; r1 += 64 * kPre) {
+    int ak[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int64_t r = r1 + 64 * u + lane;
+      int a = A;  // sentinel for rows outside the active range (and past the end)
+      if (r < hi) {
+        const int64_t d = (int64_t)keys[r] - s;
+        if (d >= 0 && d < A) a = (int)d;
+      }
+      ak[u] = a;
     }
-    const bool act = a < A;
-    uint64_t match = __ballot(act);
-    for (int b = 0; b < nbits; ++b) {
-      const bool bit = (a >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      match &= bit ? bal : ~bal;
-    }
-    const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
-                                               __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
-    const int total = __popcll(match);
-    int pos = -1;
-    if (act) pos = cursor[a] + rank;
-    // Within one wave LDS accesses complete in program order: every lane has read its
-    // cursor before the last lane of each expert advances it.
-    if (act && rank == total - 1) cursor[a] = pos + 1;
-    if (valid) scat[r] = pos;
-    if (act) {
-      if (gath) gath[pos] = (int32_t)r;
-      if (row_token) row_token[pos] = (int32_t)(r / topk);
-      if (row_weight) {
-        float w;
-        if (topk_w_bf16) w = bf16_to_f(reinterpret_cast<const uint16_t*>(topk_w)[r]);
-        else w = reinterpret_cast<const float*>(topk_w)[r];
-        row_weight[pos] = w;
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+      const int64_t r0 = r1 + 64 * u;
+      if (r0 >= hi) break;   // uniform
+      const int64_t r = r0 + lane;
+      const bool valid = r < hi;
+      const int a = ak[u];
+      const bool act = a < A;
+      uint64_t match = __ballot(act);
+      for (int b = 0; b < nbits; ++b) {
+        const bool bit = (a >> b) & 1;
+        const uint64_t bal = __ballot(bit);
+        match &= bit ? bal : ~bal;
+      }
+      const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32),
+                                                 __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
+      const int total = __popcll(match);
+      int pos = -1;
+      if (act) pos = cursor[a] + rank;
+      // Within one wave LDS accesses complete in program order: every lane has read its
+      // cursor before the last lane of each expert advances it.
+      if (act && rank == total - 1) cursor[a] = pos + 1;
+      if (valid) scat[r] = pos;
+      if (act) {
+        if (gath) gath[pos] = (int32_t)r;
+        if (row_token) row_token[pos] = (int32_t)(r / topk);
+        if (row_weight) {
+          float w;
+          if (topk_w_bf16) w = bf16_to_f(reinterpret_cast<const uint16_t*>(topk_w)[r]);
+          else w = reinterpret_cast<const float*>(topk_w)[r];
+          row_weight[pos] = w;
+        }
       }
     }
   }
@@ -221,9 +296,14 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
     else
       route_count<int32_t><<<p.nch, 256, lds_a, stream>>>((const int32_t*)p.keys, p.flat, p.s, A, p.chunk, p.hist);
   }
-  if (A > 0) route_scan<<<A, 64, 0, stream>>>(p.hist, p.nch, p.base, p.totals);
-  route_offsets<<<1, 1024, 0, stream>>>(p.totals, A, p.offsets, p.avail64, p.expert_tokens, p.tokens_type,
-                                        p.token_nums32);
+  if ((int64_t)A * p.nch + A + 1 <= kFusedScan) {
+    route_scan_fused<<<1, 1024, sizeof(int) * ((size_t)A * p.nch + A + 1), stream>>>(
+        p.hist, p.nch, A, p.base, p.offsets, p.avail64, p.expert_tokens, p.tokens_type, p.token_nums32);
+  } else {
+    route_scan<<<A, 64, 0, stream>>>(p.hist, p.nch, p.base, p.totals);
+    route_offsets<<<1, 1024, 0, stream>>>(p.totals, A, p.offsets, p.avail64, p.expert_tokens, p.tokens_type,
+                                          p.token_nums32);
+  }
   int nbits = 0;
   while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
   if (p.key_is64)

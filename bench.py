@@ -128,10 +128,15 @@ def calibrate_copy(args, torch):
     x = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda").fill_(1)
     y = torch.empty_like(x)
     torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
     for _ in range(args.steps):
         y.copy_(x)
+    end.record()
     torch.cuda.synchronize()
+    ms = start.elapsed_time(end) / max(args.steps, 1)
     print(json.dumps(dict(calibration="copy", bytes_read=COPY_BYTES, bytes_written=COPY_BYTES, copies=args.steps,
+                          ms_per_copy=round(ms, 4), copy_gbs=round(2 * COPY_BYTES / (ms * 1e-3) / 1e9, 1),
                           source=kernel_source_hash())), flush=True)
 
 
@@ -292,10 +297,11 @@ def bench_routing(args, torch, rp, moe_inputs):
                config=dict(workload=f"routing: {cfg.tokens} tokens x {h}, topK {cfg.topk}, {cfg.experts} experts, "
                                     f"active [{s},{e}), scatter index, count histogram, MXFP8 E4M3",
                            active_rows=avail, distinct_tokens=distinct),
-               roofline=dict(kernel="moe_init_routing (count, scan, scatter, permute_mx)", bound="hbm",
-                             achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                             frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, algorithmic_per_launch=alg,
-                             avg_launch_ms=round(ms, 5)),
+               roofline=dict(kernel="moe_init_routing", bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS,
+                             unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
+                             traffic=measured_traffic("moe_init_routing", "routing"), algorithmic_per_launch=alg,
+                             avg_launch_ms=round(ms, 5),
+                             kernels="route_count, route_scan_fused, route_scatter, permute_mx_kernel (one call)"),
                cpu_baseline=None)
     return out
 

@@ -140,6 +140,54 @@ def calibrate_copy(args, torch):
                           source=kernel_source_hash())), flush=True)
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def percentiles(xs):
+    a = np.sort(np.asarray(xs, dtype=np.float64))
+    return dict(median=round(float(np.median(a)), 5), p10=round(float(np.percentile(a, 10)), 5),
+                p90=round(float(np.percentile(a, 90)), 5))
+
+
+def measure_peaks(torch, rp, nbytes=1 << 30, reps=5):
+    """Measured peaks of this GPU with the library's probes: a streaming read and a copy
+    of nbytes (16-byte lanes), and the FP8 block-scaled MFMA loop. Each median of reps."""
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    read_ms = timed(lambda: rp.probe_stream(src))
+    copy_ms = timed(lambda: rp.probe_stream(src, dst, copy=True))
+    out, flops = rp.probe_mfma(2000)
+    mfma_ms = timed(lambda: rp.probe_mfma(2000, out))
+    del src, dst
+    torch.cuda.empty_cache()
+    return dict(read_gbs=round(nbytes / (read_ms * 1e-3) / 1e9, 1),
+                copy_gbs=round(2 * nbytes / (copy_ms * 1e-3) / 1e9, 1),
+                mfma_fp8_tflops=round(flops / (mfma_ms * 1e-3) / 1e12, 1),
+                note="library probes (peaks.hip): 1 GiB streaming read, 1 GiB copy, FP8 scaled-MFMA loop")
+
+
 def roofline_entry(name, ms, work):
     intensity = work["flops"] / max(work["bytes"], 1.0)
     if intensity >= RIDGE:
@@ -181,7 +229,7 @@ def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs):
     return dict(value=round(sample_tokens / dt, 4), unit="tokens/s", cores=int(cores), kind="oracle",
                 sample=f"{sample_tokens} tokens x topK {cfg.topk} experts ({len(experts)} distinct"
                        f"{', plus shared' if cfg.shared else ''}), per-token float64 oracle, {dt:.1f} s",
-                seconds=round(dt, 2), host_cpus=os.cpu_count())
+                seconds=round(dt, 2), host_cpus=os.cpu_count(), cpu_model=cpu_model())
 
 
 def bench_mega(args, torch, rp, moe_inputs):
@@ -211,7 +259,7 @@ def bench_mega(args, torch, rp, moe_inputs):
     # Stage events only where the stage times are read (GMM1, GMM2, shared experts +
     # combine): a timed event record costs a few microseconds of GPU time, inside the
     # timed region.
-    timed = {2, 3, 4, 6}
+    timed = {0, 2, 3, 4, 6}
     evs = [[torch.cuda.Event(enable_timing=True) if j in timed else None for j in range(rp.MEGA_STAGE_EVENTS)]
            for _ in range(args.steps)]
     for st in evs:
@@ -233,13 +281,18 @@ def bench_mega(args, torch, rp, moe_inputs):
     def between(j0, j1):
         return float(np.mean([evs[k][j0].elapsed_time(evs[k][j1]) for k in range(args.steps)]))
     stage_ms = {"gmm1_swiglu_quant": between(2, 3), "gmm2": between(3, 4), "shared_experts_and_combine": between(4, 6)}
-    stage_ms["routing_and_permute"] = ms - sum(stage_ms.values())
+    stage_ms["routing_and_permute"] = between(0, 2)
+    step_ms = [evs[k][0].elapsed_time(evs[k][6]) for k in range(args.steps)]
     work = layer_work(cfg, ids)
     roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], work["gmm1"]),
             "gmm2": roofline_entry("gmm2_kernel", stage_ms["gmm2"], work["gmm2"])}
     dominant = max(roof, key=lambda k: stage_ms[k])
     roofline = dict(roof[dominant])
     roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name)
+    peaks = measure_peaks(torch, rp)
+    ref = peaks["mfma_fp8_tflops"] if roofline["bound"] == "mfma" else peaks["read_gbs"]
+    roofline["measured_peak"] = ref
+    roofline["frac_of_measured"] = round(roofline["achieved"] / ref, 4)
     roofline["other"] = {k: v for k, v in roof.items() if k != dominant}
     total_bytes = work["gmm1"]["bytes"] + work["gmm2"]["bytes"] + work["combine"]["bytes"] + work["shared"]["bytes"]
     total_flops = work["gmm1"]["flops"] + work["gmm2"]["flops"] + work["shared"]["flops"]
@@ -257,6 +310,8 @@ def bench_mega(args, torch, rp, moe_inputs):
                           hbm_frac=round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                           mfma_frac=round(total_flops / (ms * 1e-3) / 1e12 / MXFP8_PEAK_TFLOPS, 4)),
                stages_ms={k: round(v, 5) for k, v in stage_ms.items()},
+               measured_peaks=peaks,
+               step_ms=percentiles(step_ms),
                wall_ms_per_step=round(wall * 1e3 / args.steps, 5))
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
@@ -268,6 +323,10 @@ def bench_mega(args, torch, rp, moe_inputs):
 
 
 def bench_routing(args, torch, rp, moe_inputs):
+    """moe_init_routing on the routing workload. Each timed call is bracketed by its own
+    events, and a streaming read of a 512 MB scratch buffer between calls evicts x from
+    the 256 MB MALL so that it is read from HBM (a read, not a write, leaves no dirty
+    lines to drain during the call; the flush is outside the events)."""
     cfg = moe_inputs.config("routing")
     ids = moe_inputs.expert_ids(cfg)
     x_cpu = moe_inputs.activations(cfg)
@@ -275,22 +334,28 @@ def bench_routing(args, torch, rp, moe_inputs):
     ids_d = torch.from_numpy(ids).cuda()
     s, e = cfg.active_range
     q = rp.QUANT_E4M3
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
     for _ in range(args.warmup):
         rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
     torch.cuda.synchronize()
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    start.record()
-    for _ in range(args.steps):
-        rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
-    end.record()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ms = start.elapsed_time(end) / args.steps
+    flush.fill_(0)
+    for a, b in evs:
+        rp.probe_stream(flush)
+        a.record()
+        rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
+        b.record()
+    torch.cuda.synchronize()
+    times = [a.elapsed_time(b) for a, b in evs]
+    ms = float(np.mean(times))
     in_range = (ids >= s) & (ids < e)
     avail = int(in_range.sum())
     distinct = int(in_range.any(axis=1).sum())
     h = cfg.hidden
     alg = distinct * 2 * h + avail * (h + h // 32) + cfg.flat * 8 + (e - s) * 8
     achieved = alg / (ms * 1e-3) / 1e9
+    peaks = measure_peaks(torch, rp)
     out = dict(metric="MoeInitRoutingV3 rows/s", value=round(avail / (ms * 1e-3), 1), unit="rows/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True,
                scaling="weak", vs_baseline=None, dtype="u8 (fp8 e4m3 codes + e8m0)", data="synthetic",
@@ -301,7 +366,10 @@ def bench_routing(args, torch, rp, moe_inputs):
                              unit="GB/s", frac=round(achieved / HBM_PEAK_GBS, 4),
                              traffic=measured_traffic("moe_init_routing", "routing"), algorithmic_per_launch=alg,
                              avg_launch_ms=round(ms, 5),
-                             kernels="route_count, route_scan_fused, route_scatter, permute_mx_kernel (one call)"),
+                             kernels="route_count, route_scan_fused, route_scatter, permute_mx_kernel (one call)",
+                             measured_peak=peaks["copy_gbs"],
+                             frac_of_measured=round(achieved / peaks["copy_gbs"], 4)),
+               step_ms=percentiles(times), measured_peaks=peaks, mall_flush="512 MB streaming read between calls",
                cpu_baseline=None)
     return out
 

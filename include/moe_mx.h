@@ -300,6 +300,20 @@ moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, 
 moe_status moe_combine_finalize(const float* y_accum, int64_t num_tokens, int64_t hidden, void* y,
                                 void* stream);
 
+/* ------------------------------------------------------------------------ */
+/* Measured peaks for the roofline report (one launch each; the caller times   */
+/* it with events on `stream`).                                                */
+/* moe_probe_stream: mode 0 reads `bytes` from src (dst receives nothing      */
+/*   unless an impossible value turns up; give a 16-byte buffer), mode 1     */
+/*   copies them to dst. bytes: a positive multiple of 16; both device.       */
+/* moe_probe_mfma: `iters` rounds of 16 independent V_MFMA_SCALE 16x16x128    */
+/*   FP8 products per wave, two 256-thread blocks per compute unit; out:     */
+/*   device fp32, at least *out_floats (host out, may be queried with        */
+/*   out = NULL) elements; *flops (host out) = MFMA flops of the launch.     */
+/* ------------------------------------------------------------------------ */
+moe_status moe_probe_stream(int mode, const void* src, void* dst, int64_t bytes, void* stream);
+moe_status moe_probe_mfma(int iters, float* out, int64_t* out_floats, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -88,6 +88,8 @@ _SIGS = {
     "moe_gmm2_combine": ([_VP, _VP, _I64, _I64, _I64, _VP, _I64, _VP, _VP, _INT, _INT, _VP, _VP, _I64, _VP,
                           _VP, _VP, _SZ, _VP], _INT),
     "moe_combine_finalize": ([_VP, _I64, _I64, _VP, _VP], _INT),
+    "moe_probe_stream": ([_INT, _VP, _VP, _I64, _VP], _INT),
+    "moe_probe_mfma": ([_INT, _VP, ctypes.POINTER(_I64), ctypes.POINTER(ctypes.c_double), _VP], _INT),
 }
 
 
@@ -360,3 +362,27 @@ def combine_finalize(y_accum):
     y = torch.empty((n, h), dtype=torch.bfloat16, device=y_accum.device)
     _check(lib.moe_combine_finalize(_ptr(y_accum), n, h, _ptr(y), _stream(y_accum.device)))
     return y
+
+
+def probe_stream(src, dst=None, copy: bool = False):
+    """One launch of the library's streaming kernel: read src (uint8 device tensor, a
+    multiple of 16 bytes), or copy it to dst. Returns None; time it with events."""
+    lib = load()
+    _need_gpu(src)
+    if copy and (dst is None or dst.numel() < src.numel()):
+        raise ValueError("probe_stream: copy needs a dst at least as large as src")
+    if dst is None:
+        dst = torch.empty(16, dtype=torch.uint8, device=src.device)
+    _check(lib.moe_probe_stream(1 if copy else 0, _ptr(src), _ptr(dst), src.numel(), _stream(src.device)))
+
+
+def probe_mfma(iters: int, out=None, device="cuda"):
+    """One launch of the library's MFMA loop; returns (out tensor, flops of the launch)."""
+    lib = load()
+    n = ctypes.c_int64()
+    fl = ctypes.c_double()
+    _check(lib.moe_probe_mfma(iters, None, ctypes.byref(n), ctypes.byref(fl), None))
+    if out is None or out.numel() < n.value:
+        out = torch.empty(n.value, dtype=torch.float32, device=device)
+    _check(lib.moe_probe_mfma(iters, _ptr(out), None, None, _stream(out.device)))
+    return out, fl.value

@@ -631,4 +631,24 @@ moe_status moe_combine_finalize(const float* y_accum, int64_t num_tokens, int64_
   return ok();
 }
 
+moe_status moe_probe_stream(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
+  if (mode != 0 && mode != 1) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream: mode %d not 0 or 1", mode);
+  if (bytes <= 0 || bytes % 16 != 0) return fail(MOE_ERR_SHAPE, "moe_probe_stream: bytes must be a positive multiple of 16");
+  if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream: NULL buffer");
+  hipError_t e = moe::launch_probe_stream(mode, src, dst, bytes, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "stream probe launch");
+  return ok();
+}
+
+moe_status moe_probe_mfma(int iters, float* out, int64_t* out_floats, double* flops, void* stream) {
+  if (iters < 1) return fail(MOE_ERR_SHAPE, "moe_probe_mfma: iters must be >= 1");
+  const int64_t need = (int64_t)moe::probe_mfma_blocks() * 256;
+  if (out_floats) *out_floats = need;
+  if (flops) *flops = moe::probe_mfma_flops(iters);
+  if (!out) return ok();
+  hipError_t e = moe::launch_probe_mfma(iters, out, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "mfma probe launch");
+  return ok();
+}
+
 }  // extern "C"

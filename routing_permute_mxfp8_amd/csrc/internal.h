@@ -151,4 +151,11 @@ hipError_t launch_scatter_add(const float* o, int64_t rows, int hidden, const in
                               const float* row_weight, float* y_accum, hipStream_t stream);
 hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t stream);
 
+
+// ---- measured peaks (peaks.hip) ------------------------------------------------------
+hipError_t launch_probe_stream(int copy, const void* src, void* dst, int64_t bytes, hipStream_t stream);
+int probe_mfma_blocks();   // blocks of 256 threads the MFMA probe launches (one per CU)
+hipError_t launch_probe_mfma(int iters, float* out, hipStream_t stream);
+double probe_mfma_flops(int iters);
+
 }  // namespace moe

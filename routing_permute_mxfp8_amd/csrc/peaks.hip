@@ -1,0 +1,91 @@
+// Measured peaks of the GPU the library runs on, for the roofline report: a streaming
+// read and a copy of a caller buffer (16-byte lanes, four loads per lane in flight), and
+// a loop of independent block-scaled FP8 MFMAs (16 accumulators per wave, two waves per
+// SIMD, 16x16x128: the instruction of the grouped GEMMs). Each entry point is one launch on the caller's
+// stream; the caller times it.
+
+#include <algorithm>
+
+#include "device_common.h"
+#include "internal.h"
+
+namespace moe {
+namespace {
+
+constexpr int kU = 4;
+
+template <bool COPY>
+__global__ __launch_bounds__(256) void stream_kernel(const u32x4* __restrict__ a, u32x4* __restrict__ b, int64_t n) {
+  const int64_t stride = (int64_t)gridDim.x * 256 * kU;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int64_t i0 = (int64_t)blockIdx.x * 256 * kU + threadIdx.x; i0 < n; i0 += stride) {
+    u32x4 v[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * 256;
+      v[u] = i < n ? a[i] : u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int64_t i = i0 + u * 256;
+      if (COPY) {
+        if (i < n) b[i] = v[u];
+      } else {
+        acc ^= v[u];
+      }
+    }
+  }
+  // read mode: keep the loads alive; the store happens only for an impossible value
+  if (!COPY && acc[0] == 0x9e3779b9u && acc[1] == 0x7f4a7c15u && acc[2] == 1u && acc[3] == 2u) b[0] = acc;
+}
+
+constexpr int kAcc = 16;
+
+__global__ __launch_bounds__(256) void mfma_kernel(float* __restrict__ out, int iters) {
+  const int lane = threadIdx.x & 63;
+  v8i a = {lane, iters, 3, 4, 5, 6, 7, 8}, b = {iters, lane, 8, 7, 6, 5, 4, 3};
+  v4f acc[kAcc];
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) acc[i] = v4f{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < kAcc; ++i) acc[i] = mfma_mx16<0>(a, b, acc[i], 127, 127);
+  }
+  float s = 0.f;
+#pragma unroll
+  for (int i = 0; i < kAcc; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  out[(int64_t)blockIdx.x * 256 + threadIdx.x] = s;
+}
+
+int device_cus() {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  return cus;
+}
+
+}  // namespace
+
+hipError_t launch_probe_stream(int copy, const void* src, void* dst, int64_t bytes, hipStream_t st) {
+  const int64_t n = bytes / 16;
+  const int cus = std::max(device_cus(), 1);
+  const unsigned grid = (unsigned)std::max<int64_t>(1, std::min<int64_t>((n + 256 * kU - 1) / (256 * kU), cus * 16));
+  if (copy)
+    stream_kernel<true><<<grid, 256, 0, st>>>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n);
+  else
+    stream_kernel<false><<<grid, 256, 0, st>>>(reinterpret_cast<const u32x4*>(src), reinterpret_cast<u32x4*>(dst), n);
+  return hipGetLastError();
+}
+
+int probe_mfma_blocks() { return 2 * std::max(device_cus(), 1); }   // two waves per SIMD
+
+hipError_t launch_probe_mfma(int iters, float* out, hipStream_t st) {
+  mfma_kernel<<<probe_mfma_blocks(), 256, 0, st>>>(out, iters);
+  return hipGetLastError();
+}
+
+double probe_mfma_flops(int iters) {
+  return (double)probe_mfma_blocks() * 4 /*waves*/ * (double)iters * kAcc * 2.0 * 16 * 16 * 128;
+}
+
+}  // namespace moe

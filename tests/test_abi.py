@@ -140,3 +140,12 @@ def test_mega_moe_validation(lib):
     a = args()
     assert lib.mega_moe(ctypes.byref(a), FAKE, 16, None) == 5
     assert "bytes required" in lib.moe_last_error().decode()
+
+
+def test_probe_validation(lib):
+    """The measurement probes reject bad arguments before any launch."""
+    assert lib.moe_probe_stream(2, FAKE, FAKE, 1024, None) == 1          # mode
+    assert lib.moe_probe_stream(0, FAKE, FAKE, 1000, None) == 2          # not a multiple of 16
+    assert lib.moe_probe_stream(0, FAKE, FAKE, 0, None) == 2
+    assert lib.moe_probe_stream(1, None, FAKE, 1024, None) == 1          # NULL buffer
+    assert lib.moe_probe_mfma(0, None, None, None, None) == 2            # iters

@@ -136,6 +136,23 @@ __device__ __forceinline__ void block_items(int total, int* first, int* stride, 
   *last = hi;
 }
 
+// Workgroup barrier at the top of a K step. __syncthreads fences global memory, which
+// waits for every outstanding load, the prefetches of later steps included; the waits
+// this barrier must cover (every wave's DMA writes of the step's token tiles) are the
+// explicit vmcnt wait before it, so chunks of 4 or more tiles use the bare s_barrier
+// (scheduling fences keep the LDS accesses on their side of it). For 1- and 2-tile
+// chunks the fenced barrier measured faster.
+template <int NT>
+__device__ __forceinline__ void block_barrier() {
+  if constexpr (NT >= 4) {
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+  } else {
+    __syncthreads();
+  }
+}
+
 // ---- the K loop shared by both GEMMs ---------------------------------------------
 // Loads issued in K step s, numbered: first the weights of step s + WPF (per weight
 // tile: operand lo half, hi half, scale dword; from HBM into the VGPR buffer that step
@@ -227,7 +244,7 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT]
   constexpr int kTop = NT < 4 ? kLoads : (kLoads > 4 * NT ? kLoads - 4 * NT : 0);
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   wait_vmcnt<Batch<NT>::kInFlight>();
-  __syncthreads();
+  block_barrier<NT>();
   const int wstep = min(s + WeightPrefetch<NT>::value, ks - 1), tstep = min(s + 2, ks - 1);
   uint8_t* slot = lds + (cur == 0 ? 2 : cur - 1) * kBuf;   // (cur + 2) % 3
   const uint8_t* buf = lds + cur * kBuf;

@@ -21,6 +21,9 @@
 //                    bit-sliced match: one ballot per bit of the expert id, AND-ed per
 //                    lane (bit set ? ballot : ~ballot), then mbcnt below the lane. An LDS
 //                    cursor per expert carries the running position across steps.
+//                    For chunks of up to 1024 rows over at most 512 active experts,
+//                    route_scatter_block ranks the whole chunk at once (one thread per
+//                    row, per-wave counts scanned over the waves in LDS).
 // Positions are relative to the start of the active segment [s, e).
 
 #include <climits>
@@ -238,6 +241,69 @@ __global__ __launch_bounds__(64) void route_scatter(
   }
 }
 
+// route_scatter for chunks of at most 1024 rows over at most kBlockScatterMaxActive
+// experts: one thread per row, so the chunk is ranked in one step instead of chunk / 64
+// dependent ones. Each wave ranks its 64 rows by the same bit-sliced match; the
+// per-wave counts of every expert are then scanned over the waves in LDS, starting
+// from the chunk's first position offsets[a] + base[a][c].
+constexpr int kBlockScatterMaxActive = 512;
+
+template <typename KeyT>
+__global__ __launch_bounds__(1024) void route_scatter_block(
+    const KeyT* __restrict__ keys, int64_t flat, int topk, int s, int A, int nbits, int chunk,
+    const int* __restrict__ base, const int* __restrict__ offsets, int32_t* __restrict__ scat,
+    int32_t* __restrict__ gath, int32_t* __restrict__ gath_fill, int32_t* __restrict__ row_token,
+    float* __restrict__ row_weight, const void* __restrict__ topk_w, int topk_w_bf16) {
+  extern __shared__ int wcnt[];  // [waves][A]: counts, then first positions
+  const int nw = blockDim.x >> 6;
+  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < nw * A; i += blockDim.x) wcnt[i] = 0;
+  const int64_t r = (int64_t)c * chunk + tid;
+  const bool valid = tid < chunk && r < flat;
+  int a = A;  // sentinel for rows outside the active range (and past the end)
+  if (valid) {
+    const int64_t d = (int64_t)keys[r] - s;
+    if (d >= 0 && d < A) a = (int)d;
+  }
+  const bool act = a < A;
+  uint64_t match = __ballot(act);
+  for (int b = 0; b < nbits; ++b) {
+    const bool bit = (a >> b) & 1;
+    const uint64_t bal = __ballot(bit);
+    match &= bit ? bal : ~bal;
+  }
+  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
+  __syncthreads();
+  if (act && rank == __popcll(match) - 1) wcnt[wave * A + a] = rank + 1;
+  __syncthreads();
+  for (int ex = tid; ex < A; ex += blockDim.x) {
+    int run = offsets[ex] + base[(int64_t)ex * gridDim.x + c];
+    for (int w = 0; w < nw; ++w) {
+      const int v = wcnt[w * A + ex];
+      wcnt[w * A + ex] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  const int pos = act ? wcnt[wave * A + a] + rank : -1;
+  if (valid) scat[r] = pos;
+  if (act) {
+    if (gath) gath[pos] = (int32_t)r;
+    if (row_token) row_token[pos] = (int32_t)(r / topk);
+    if (row_weight) {
+      float w;
+      if (topk_w_bf16) w = bf16_to_f(reinterpret_cast<const uint16_t*>(topk_w)[r]);
+      else w = reinterpret_cast<const float*>(topk_w)[r];
+      row_weight[pos] = w;
+    }
+  }
+  if (gath_fill) {
+    const int avail = offsets[A];
+    for (int64_t p = avail + (int64_t)c * blockDim.x + tid; p < flat; p += (int64_t)gridDim.x * blockDim.x)
+      gath_fill[p] = -1;
+  }
+}
+
 // Offsets are clamped into [0, rows] and made non-decreasing, and at most max_tiles
 // tiles are written, so caller-given offsets can never send a GEMM out of bounds.
 // Each group is padded to whole 16-row tiles in the tiled token layout: its padded
@@ -306,6 +372,18 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
   }
   int nbits = 0;
   while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
+  if (p.chunk <= 1024 && A <= kBlockScatterMaxActive) {
+    const size_t lds = sizeof(int) * (size_t)(p.chunk / 64) * (size_t)(A > 0 ? A : 1);
+    if (p.key_is64)
+      route_scatter_block<int64_t><<<p.nch, p.chunk, lds, stream>>>(
+          (const int64_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
+          p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
+    else
+      route_scatter_block<int32_t><<<p.nch, p.chunk, lds, stream>>>(
+          (const int32_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
+          p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
+    return hipGetLastError();
+  }
   if (p.key_is64)
     route_scatter<int64_t><<<p.nch, 64, lds_a, stream>>>(
         (const int64_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,

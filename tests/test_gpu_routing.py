@@ -95,6 +95,20 @@ def test_many_experts_and_chunks():
     check_init_routing(x, ids, cfg.experts, (100, 4000), rp.QUANT_E5M2, 0, 0)
 
 
+@pytest.mark.parametrize("tokens,topk,experts,active,row_idx_type,tokens_type,quant",
+                         [(10000, 8, 600, (50, 550), 0, 0, 2),     # 1024-row chunks, 500 buckets, gather index
+                          (9000, 4, 64, (0, 64), 1, 1, 3),         # 256-row chunks, every expert active
+                          (1111, 16, 300, (17, 290), 0, 1, 3),     # ragged last chunk, K = 16
+                          (5000, 5, 40, (3, 37), 1, 0, 2)])        # K = 5: tokens straddle chunks
+def test_chunked_routing_shapes(tokens, topk, experts, active, row_idx_type, tokens_type, quant):
+    # several hundred chunks, hundreds of buckets, ragged last chunk, K = 16 and odd K
+    cfg = moe_inputs.config("tiny", tokens=tokens, hidden=256, topk=topk, experts=experts, seed=tokens)
+    say(f"init_routing chunked N={tokens} K={topk} E={experts} active={active}")
+    ids = moe_inputs.expert_ids(cfg)
+    x = moe_inputs.activations(cfg)
+    check_init_routing(x, ids, cfg.experts, active, quant, row_idx_type, tokens_type, run_twice=True)
+
+
 def test_empty_input():
     say("init_routing empty")
     x = torch.zeros((0, 64), dtype=torch.bfloat16)

@@ -21,9 +21,12 @@
 //                    bit-sliced match: one ballot per bit of the expert id, AND-ed per
 //                    lane (bit set ? ballot : ~ballot), then mbcnt below the lane. An LDS
 //                    cursor per expert carries the running position across steps.
-//                    For chunks of up to 1024 rows over at most 512 active experts,
-//                    route_scatter_block ranks the whole chunk at once (one thread per
-//                    row, per-wave counts scanned over the waves in LDS).
+// Block path, for chunks of up to 1024 rows over at most 512 active experts: one thread
+// per row in both passes (route_count_block, route_scatter_block), each wave ranking its
+// 64 rows at once, per-wave counts scanned over the waves in LDS; when the histogram is
+// small (at most 64 chunks, or at most two experts per wave) the scatter pass also
+// derives its chunk's first positions from it, so the scan pass disappears (two
+// launches in all).
 // Positions are relative to the start of the active segment [s, e).
 
 #include <climits>
@@ -241,43 +244,163 @@ __global__ __launch_bounds__(64) void route_scatter(
   }
 }
 
-// route_scatter for chunks of at most 1024 rows over at most kBlockScatterMaxActive
-// experts: one thread per row, so the chunk is ranked in one step instead of chunk / 64
-// dependent ones. Each wave ranks its 64 rows by the same bit-sliced match; the
-// per-wave counts of every expert are then scanned over the waves in LDS, starting
-// from the chunk's first position offsets[a] + base[a][c].
-constexpr int kBlockScatterMaxActive = 512;
+// ---- block path: chunks of at most 1024 rows over at most 512 active experts -------
+// One thread per row. Each wave ranks its 64 rows by expert with the bit-sliced match
+// of route_scatter (rank = matching lanes below, count = matching lanes); per-wave
+// counts of every expert go to LDS ([waves][A]).
+constexpr int kBlockMaxActive = 512;
+// Histogram entries (A * chunks) up to which the scatter pass may derive its chunk's
+// first positions from the histogram itself instead of a separate scan pass.
+constexpr int kScanInScatter = 16384;
 
 template <typename KeyT>
-__global__ __launch_bounds__(1024) void route_scatter_block(
-    const KeyT* __restrict__ keys, int64_t flat, int topk, int s, int A, int nbits, int chunk,
-    const int* __restrict__ base, const int* __restrict__ offsets, int32_t* __restrict__ scat,
-    int32_t* __restrict__ gath, int32_t* __restrict__ gath_fill, int32_t* __restrict__ row_token,
-    float* __restrict__ row_weight, const void* __restrict__ topk_w, int topk_w_bf16) {
-  extern __shared__ int wcnt[];  // [waves][A]: counts, then first positions
-  const int nw = blockDim.x >> 6;
-  const int c = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < nw * A; i += blockDim.x) wcnt[i] = 0;
-  const int64_t r = (int64_t)c * chunk + tid;
-  const bool valid = tid < chunk && r < flat;
+__device__ __forceinline__ void block_rank(const KeyT* __restrict__ keys, int64_t r, bool valid, int s, int A,
+                                           int nbits, int* a_out, int* rank_out, int* count_out) {
   int a = A;  // sentinel for rows outside the active range (and past the end)
   if (valid) {
     const int64_t d = (int64_t)keys[r] - s;
     if (d >= 0 && d < A) a = (int)d;
   }
-  const bool act = a < A;
-  uint64_t match = __ballot(act);
+  uint64_t match = __ballot(a < A);
   for (int b = 0; b < nbits; ++b) {
     const bool bit = (a >> b) & 1;
     const uint64_t bal = __ballot(bit);
     match &= bit ? bal : ~bal;
   }
-  const int rank = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
+  *a_out = a;
+  *rank_out = __builtin_amdgcn_mbcnt_hi((uint32_t)(match >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)match, 0));
+  *count_out = __popcll(match);
+}
+
+// Counting pass of the block path: hist[a][c] = sum over the waves of their counts.
+template <typename KeyT>
+__global__ __launch_bounds__(1024) void route_count_block(const KeyT* __restrict__ keys, int64_t flat, int s, int A,
+                                                          int nbits, int chunk, int* __restrict__ hist) {
+  extern __shared__ int wcnt[];  // [waves][A]
+  const int nw = blockDim.x >> 6;
+  const int c = blockIdx.x, tid = threadIdx.x, wave = tid >> 6;
+  for (int i = tid; i < nw * A; i += blockDim.x) wcnt[i] = 0;
+  const int64_t r = (int64_t)c * chunk + tid;
+  int a, rank, cnt;
+  block_rank(keys, r, tid < chunk && r < flat, s, A, nbits, &a, &rank, &cnt);
   __syncthreads();
-  if (act && rank == __popcll(match) - 1) wcnt[wave * A + a] = rank + 1;
+  if (a < A && rank == cnt - 1) wcnt[wave * A + a] = cnt;
   __syncthreads();
   for (int ex = tid; ex < A; ex += blockDim.x) {
-    int run = offsets[ex] + base[(int64_t)ex * gridDim.x + c];
+    int sum = 0;
+    for (int w = 0; w < nw; ++w) sum += wcnt[w * A + ex];
+    hist[(int64_t)ex * gridDim.x + c] = sum;
+  }
+}
+
+// Scatter pass of the block path. The chunk's first position of expert a is
+// offsets[a] + base[a][c]; with SCAN the workgroup derives both from the histogram
+// (rows of a in chunks < c, one thread or one wave per expert; exclusive scan of the
+// per-expert totals),
+// and workgroup 0 writes the routing summaries route_scan_fused would. The per-wave
+// counts are then turned into per-wave first positions by a scan over the waves.
+template <typename KeyT, bool SCAN>
+__global__ __launch_bounds__(1024) void route_scatter_block(
+    const KeyT* __restrict__ keys, int64_t flat, int topk, int s, int A, int nbits, int chunk,
+    const int* __restrict__ hist, const int* __restrict__ base, int* __restrict__ offsets, int64_t* avail64,
+    int64_t* expert_tokens, int tokens_type, int32_t* token_nums32, int32_t* __restrict__ scat,
+    int32_t* __restrict__ gath, int32_t* __restrict__ gath_fill, int32_t* __restrict__ row_token,
+    float* __restrict__ row_weight, const void* __restrict__ topk_w, int topk_w_bf16) {
+  extern __shared__ int sh[];
+  const int nw = blockDim.x >> 6;
+  int* wcnt = sh;              // [waves][A]: counts, then first positions
+  int* pre = wcnt + nw * A;    // [A] first position of (this chunk, expert)
+  int* tot = pre + A;          // [A] rows per expert (SCAN)
+  int* part = tot + A;         // [waves + 1] scan of the per-thread sums (SCAN)
+  const int c = blockIdx.x, nch = gridDim.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < nw * A; i += blockDim.x) wcnt[i] = 0;
+  const int64_t r = (int64_t)c * chunk + tid;
+  const bool valid = tid < chunk && r < flat;
+  int a, rank, cnt;
+  block_rank(keys, r, valid, s, A, nbits, &a, &rank, &cnt);
+  const bool act = a < A;
+  int avail;
+  if constexpr (SCAN) {
+    if (nch <= 64) {   // few chunks: one thread per expert walks its chunk counts
+      for (int ex = tid; ex < A; ex += blockDim.x) {
+        const int* h = hist + (int64_t)ex * nch;
+        int before = 0, total = 0;
+        for (int cc = 0; cc < nch; ++cc) {
+          const int v = h[cc];
+          total += v;
+          if (cc < c) before += v;
+        }
+        pre[ex] = before;
+        tot[ex] = total;
+      }
+    }
+    for (int ex = nch <= 64 ? A : wave; ex < A; ex += nw) {   // else one wave per expert
+      const int* h = hist + (int64_t)ex * nch;
+      int before = 0, total = 0;
+      for (int cc = lane; cc < nch; cc += 64) {
+        const int v = h[cc];
+        total += v;
+        if (cc < c) before += v;
+      }
+#pragma unroll
+      for (int d = 32; d >= 1; d >>= 1) {
+        before += __shfl_xor(before, d);
+        total += __shfl_xor(total, d);
+      }
+      if (lane == 0) {
+        pre[ex] = before;
+        tot[ex] = total;
+      }
+    }
+    __syncthreads();
+    // exclusive scan of the totals over the experts: thread t takes experts [a0, a1)
+    const int P = (A + blockDim.x - 1) / blockDim.x;
+    const int a0 = min(A, tid * P), a1 = min(A, a0 + P);
+    int sum = 0;
+    for (int e = a0; e < a1; ++e) sum += tot[e];
+    int incl = sum;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int x = __shfl_up(incl, d);
+      if (lane >= d) incl += x;
+    }
+    if (lane == 63) part[wave] = incl;
+    __syncthreads();
+    if (tid == 0) {
+      int run = 0;
+      for (int w = 0; w < nw; ++w) {
+        const int v = part[w];
+        part[w] = run;
+        run += v;
+      }
+      part[nw] = run;
+    }
+    __syncthreads();
+    int run = part[wave] + incl - sum;
+    for (int e = a0; e < a1; ++e) {
+      const int n_e = tot[e];
+      pre[e] += run;
+      if (c == 0) {
+        offsets[e] = run;
+        if (expert_tokens) expert_tokens[e] = tokens_type == 1 ? (int64_t)n_e : (int64_t)(run + n_e);
+        if (token_nums32) token_nums32[e] = n_e;
+      }
+      run += n_e;
+    }
+    avail = part[nw];
+    if (c == 0 && tid == 0) {
+      offsets[A] = avail;
+      if (avail64) *avail64 = avail;
+    }
+  } else {
+    for (int ex = tid; ex < A; ex += blockDim.x) pre[ex] = offsets[ex] + base[(int64_t)ex * nch + c];
+    avail = offsets[A];
+  }
+  __syncthreads();
+  if (act && rank == cnt - 1) wcnt[wave * A + a] = cnt;
+  __syncthreads();
+  for (int ex = tid; ex < A; ex += blockDim.x) {
+    int run = pre[ex];
     for (int w = 0; w < nw; ++w) {
       const int v = wcnt[w * A + ex];
       wcnt[w * A + ex] = run;
@@ -297,11 +420,40 @@ __global__ __launch_bounds__(1024) void route_scatter_block(
       row_weight[pos] = w;
     }
   }
-  if (gath_fill) {
-    const int avail = offsets[A];
-    for (int64_t p = avail + (int64_t)c * blockDim.x + tid; p < flat; p += (int64_t)gridDim.x * blockDim.x)
+  if (gath_fill)
+    for (int64_t p = avail + (int64_t)c * blockDim.x + tid; p < flat; p += (int64_t)nch * blockDim.x)
       gath_fill[p] = -1;
+}
+
+template <typename KeyT>
+hipError_t routing_block_path(const RouteParams& p, int A, int nbits, hipStream_t stream) {
+  const KeyT* keys = (const KeyT*)p.keys;
+  const size_t wl = sizeof(int) * (size_t)(p.chunk / 64) * (size_t)A;
+  route_count_block<KeyT><<<p.nch, p.chunk, wl, stream>>>(keys, p.flat, p.s, A, nbits, p.chunk, p.hist);
+  // in-kernel scan only where it is short: at most 64 chunk counts per thread (thread per
+  // expert) or at most two experts per wave (wave per expert)
+  const bool scan_here = (p.nch <= 64 && (int64_t)A * p.nch <= kScanInScatter) || A <= 2 * (p.chunk / 64);
+  const size_t sl = wl + sizeof(int) * ((size_t)2 * A + p.chunk / 64 + 1);
+  if (scan_here) {
+    route_scatter_block<KeyT, true><<<p.nch, p.chunk, sl, stream>>>(
+        keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.hist, p.base, p.offsets, p.avail64, p.expert_tokens,
+        p.tokens_type, p.token_nums32, p.scat, p.gath, p.gath_fill, p.row_token, p.row_weight, p.topk_w,
+        p.topk_w_bf16);
+    return hipGetLastError();
   }
+  if ((int64_t)A * p.nch + A + 1 <= kFusedScan) {
+    route_scan_fused<<<1, 1024, sizeof(int) * ((size_t)A * p.nch + A + 1), stream>>>(
+        p.hist, p.nch, A, p.base, p.offsets, p.avail64, p.expert_tokens, p.tokens_type, p.token_nums32);
+  } else {
+    route_scan<<<A, 64, 0, stream>>>(p.hist, p.nch, p.base, p.totals);
+    route_offsets<<<1, 1024, 0, stream>>>(p.totals, A, p.offsets, p.avail64, p.expert_tokens, p.tokens_type,
+                                          p.token_nums32);
+  }
+  route_scatter_block<KeyT, false><<<p.nch, p.chunk, sl, stream>>>(
+      keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.hist, p.base, p.offsets, p.avail64, p.expert_tokens,
+      p.tokens_type, p.token_nums32, p.scat, p.gath, p.gath_fill, p.row_token, p.row_weight, p.topk_w,
+      p.topk_w_bf16);
+  return hipGetLastError();
 }
 
 // Offsets are clamped into [0, rows] and made non-decreasing, and at most max_tiles
@@ -355,6 +507,11 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
 
 hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
   const int A = p.e - p.s;
+  int nbits = 0;
+  while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
+  if (A >= 1 && A <= kBlockMaxActive && p.chunk <= 1024)
+    return p.key_is64 ? routing_block_path<int64_t>(p, A, nbits, stream)
+                      : routing_block_path<int32_t>(p, A, nbits, stream);
   const size_t lds_a = sizeof(int) * (size_t)(A > 0 ? A : 1);
   if (A > 0) {
     if (p.key_is64)
@@ -369,20 +526,6 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
     route_scan<<<A, 64, 0, stream>>>(p.hist, p.nch, p.base, p.totals);
     route_offsets<<<1, 1024, 0, stream>>>(p.totals, A, p.offsets, p.avail64, p.expert_tokens, p.tokens_type,
                                           p.token_nums32);
-  }
-  int nbits = 0;
-  while ((1 << nbits) <= A) ++nbits;  // bits of the sentinel value A
-  if (p.chunk <= 1024 && A <= kBlockScatterMaxActive) {
-    const size_t lds = sizeof(int) * (size_t)(p.chunk / 64) * (size_t)(A > 0 ? A : 1);
-    if (p.key_is64)
-      route_scatter_block<int64_t><<<p.nch, p.chunk, lds, stream>>>(
-          (const int64_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
-          p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
-    else
-      route_scatter_block<int32_t><<<p.nch, p.chunk, lds, stream>>>(
-          (const int32_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
-          p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
-    return hipGetLastError();
   }
   if (p.key_is64)
     route_scatter<int64_t><<<p.nch, 64, lds_a, stream>>>(

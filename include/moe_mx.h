@@ -202,7 +202,24 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /*   y            out, bf16 [num_tokens, hidden]                                  */
 /*   expert_token_nums  out, int32 [num_experts] (nullable)                       */
 /* Limits: hidden % 128 == 0, inter % 128 == 0, topk in [1, 32], num_experts in   */
-/* [1, 1024]; activation must be MOE_ACT_SWIGLU (no clamp).                       */
+/* [1, 1024].                                                                    */
+/* activation ([MM] "Activation function formulas"; G = first inter channels of   */
+/* the GMM1 output, U = the last inter, c the clamp, Gc = min(G, c),              */
+/* Uc = clip(U, -c, c), sigma the logistic function):                             */
+/*   MOE_ACT_SWIGLU      A = SiLU(Gc) * Uc;             params [] or [clamp]       */
+/*   MOE_ACT_SWIGLUSTEP  A = min(SiLU(G), c) * Uc;      params [] or [clamp]       */
+/*   MOE_ACT_SWIGLUOAI   A = Gc sigma(alpha Gc)(Uc + beta); params [] or          */
+/*                       [clamp, alpha, beta] (defaults: no clamp, 1.702, 1.0)     */
+/*   MOE_ACT_SITUGLU     A = beta tanh(G/beta) sigma(G) L(U), L(U) = U, or         */
+/*                       lb tanh(U/lb) when linear_beta lb is given; params [],    */
+/*                       [beta] or [beta, linear_beta] (default beta 1.0)          */
+/*   MOE_ACT_GELU        A = Z sigma(sqrt(8/pi)(Z + 0.044715 Z^3)) on all 2*inter */
+/*                       channels Z of the GMM1 output (no split, no clamp):      */
+/*                       A and w2's input width are then 2*inter (w2 [num_experts,*/
+/*                       hidden, 2*inter], aq/sa [F, 2*inter] / [F, 2*inter/32]);  */
+/*                       params [] or the placeholder [FLT_MAX].                    */
+/* A clamp of 0 (or none) means no clamp; clamp >= 0, alpha and beta finite,      */
+/* situglu's betas finite and > 0; anything else is MOE_ERR_INVALID_ARG.           */
 /* Optional device outputs for parity checks (NULL to skip): xq/sx the stage-1    */
 /* operands [F, hidden] / [F, hidden/32] in expert-contiguous order; h1 fp32      */
 /* [F, 2*inter] (G then U); aq/sa the stage-2 requantized activations            */
@@ -215,7 +232,8 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /* written), [5] shared experts done, [6] weighted combine into bf16 y done.        */
 /* The result is deterministic (no atomics on the mega_moe path).                  */
 /* ------------------------------------------------------------------------ */
-enum { MOE_ACT_SWIGLU = 0 };
+enum { MOE_ACT_SWIGLU = 0, MOE_ACT_SWIGLUSTEP = 1, MOE_ACT_SWIGLUOAI = 2, MOE_ACT_SITUGLU = 3,
+       MOE_ACT_GELU = 4 };
 #define MOE_MEGA_STAGE_EVENTS 7
 
 typedef struct {
@@ -238,7 +256,7 @@ typedef struct {
   const uint8_t* shared_w2;
   const uint8_t* shared_w2_scales;
   int quant_out_dtype;            /* MOE_FP8_E5M2 or MOE_FP8_E4M3 (= the weights' FP8 type) */
-  int activation;                 /* MOE_ACT_SWIGLU */
+  int activation;                 /* MOE_ACT_*, see above */
   int weight_format;              /* MOE_WEIGHTS_ND or MOE_WEIGHTS_PACKED (routed and shared) */
   void* y;
   int32_t* expert_token_nums;
@@ -251,6 +269,8 @@ typedef struct {
   float* o;
   int32_t* sorted_row_idx;
   void** stage_events;            /* nullable, see above */
+  int num_activation_params;      /* 0..3, see the activations above */
+  float activation_params[3];
 } moe_mega_args;
 
 moe_status mega_moe_workspace_size(const moe_mega_args* args /* host */, size_t* bytes /* host out */);

@@ -87,7 +87,7 @@ def config(name: str, **overrides) -> LayerConfig:
     return dataclasses.replace(CONFIGS[name], **overrides)
 
 
-_TAGS = {"ids": 1, "gate": 2, "x": 3, "w1": 4, "w2": 5, "sw1": 6, "sw2": 7}
+_TAGS = {"ids": 1, "gate": 2, "x": 3, "w1": 4, "w2": 5, "sw1": 6, "sw2": 7, "w2g": 8, "sw2g": 9}
 
 
 def derive_seed(seed: int, tag: str, index: int = 0) -> int:
@@ -151,14 +151,15 @@ def weight_master(cfg: LayerConfig, which: str, expert: int, device="cpu") -> to
 
     which: "w1" -> [2I, H] (gate rows [0, I), up rows [I, 2I)), fan_in H
            "w2" -> [H, I], fan_in I
-           "sw1"/"sw2" -> the same for shared expert ``expert``.
+           "w2g" -> [H, 2I], fan_in 2I (weight2 of a gelu layer, whose A is 2I wide)
+           "sw1"/"sw2"/"sw2g" -> the same for shared expert ``expert``.
     Drawn with torch's generator on ``device`` seeded per (config, tensor, expert),
     so any single expert can be regenerated on its own. CPU and GPU generators give
     different (equally valid) draws; a given device always gives the same ones.
     """
     h, i = cfg.hidden, cfg.inter
-    shape, fan_in = {"w1": ((2 * i, h), h), "w2": ((h, i), i),
-                     "sw1": ((2 * i, h), h), "sw2": ((h, i), i)}[which]
+    shape, fan_in = {"w1": ((2 * i, h), h), "w2": ((h, i), i), "w2g": ((h, 2 * i), 2 * i),
+                     "sw1": ((2 * i, h), h), "sw2": ((h, i), i), "sw2g": ((h, 2 * i), 2 * i)}[which]
     gen = torch.Generator(device=device)
     gen.manual_seed(derive_seed(cfg.seed, which, expert))
     w = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)

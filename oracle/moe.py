@@ -6,8 +6,19 @@ MegaMoE page, "A8W8-FP quantization scenario":
            A_e = Activation(G_e, U_e),  A^_e, S_A,e = Q_MX(A_e)  (same FP8 type)
   stage 3  O_e = DQ(A^_e) . DQ(W2_e)
   stage 4  Y[i] = sum_k W[i,k] O[pi(i,k)] + sum_s O_s^shared[i],  Y is BF16
-"Activation function formulas": sigma(z) = 1/(1+e^-z), SiLU(z) = z sigma(z),
-swiglu A = SiLU(G_c) * U_c, with c = +inf when no clamp is configured.
+"Activation function formulas": sigma(z) = 1/(1+e^-z), SiLU(z) = z sigma(z); with
+the clamp c (+inf when not configured or 0), G_c = min(G, c), U_c = clip(U, -c, c):
+  swiglu      A = SiLU(G_c) * U_c
+  swiglustep  A = min(SiLU(G), c) * U_c
+  swigluoai   A = G_c * sigma(alpha G_c) * (U_c + beta)
+  situglu     A = beta tanh(G / beta) * sigma(G) * L(U), L(U) = U, or
+              lb tanh(U / lb) when linear_beta lb is configured
+  gelu        A = Z * sigma(sqrt(8/pi) (Z + 0.044715 Z^3)) on the whole GMM1 output
+              Z (no split, no clamp), so A and weight2's input are 2I wide.
+Parameter lists and defaults (activation_params): swiglu / swiglustep [] or
+[clamp]; swigluoai [] or [clamp, alpha, beta] with defaults alpha 1.702, beta 1.0;
+situglu [], [beta] or [beta, linear_beta] with default beta 1.0; gelu takes none
+(its placeholder [FLT_MAX] is ignored).
 "MXFP quantization scenario constraints": weight1 (E, 2I, H) and weight2
 (E, H, I), each output channel holding its K-contiguous inputs; G is the first
 I output channels of weight1 and U the last I (the page splits the logical
@@ -29,12 +40,69 @@ from . import mxfp, routing
 
 def silu(z):
     z = np.asarray(z, dtype=np.float64)
-    return z / (1.0 + np.exp(-z))
+    with np.errstate(over="ignore"):   # e^-z = inf for very negative z: the limit 0 is right
+        return z / (1.0 + np.exp(-z))
 
 
 def swiglu(g, u):
     """A = SiLU(G) * U (no clamp)."""
     return silu(g) * np.asarray(u, dtype=np.float64)
+
+
+def sigmoid(z):
+    with np.errstate(over="ignore"):
+        return 1.0 / (1.0 + np.exp(-np.asarray(z, dtype=np.float64)))
+
+
+ACTIVATIONS = ("swiglu", "swiglustep", "swigluoai", "situglu", "gelu")
+
+
+def activation_settings(kind, params=()):
+    """The (clamp, alpha, beta, linear_beta) an activation uses, from its parameter list
+    with the pages' defaults; clamp +inf = none (0 means none), linear_beta None = L(U) = U."""
+    p = [float(v) for v in params]
+    clamp, alpha, beta, lin = np.inf, 1.702, 1.0, None
+    if kind in ("swiglu", "swiglustep"):
+        assert len(p) in (0, 1)
+        if p and p[0] > 0:
+            clamp = p[0]
+    elif kind == "swigluoai":
+        assert len(p) in (0, 3)
+        if p:
+            clamp = p[0] if p[0] > 0 else np.inf
+            alpha, beta = p[1], p[2]
+    elif kind == "situglu":
+        assert len(p) in (0, 1, 2) and all(v > 0 for v in p)
+        if p:
+            beta = p[0]
+        if len(p) == 2:
+            lin = p[1]
+    else:
+        assert kind == "gelu" and len(p) <= 1
+    return clamp, alpha, beta, lin
+
+
+def activate(h1, kind="swiglu", params=()):
+    """Activation of GMM1's output h1 [m, 2I] (float64): gated kinds take G = h1[:, :I]
+    and U = h1[:, I:] and return [m, I]; gelu returns [m, 2I]."""
+    h1 = np.asarray(h1, dtype=np.float64)
+    c, alpha, beta, lin = activation_settings(kind, params)
+    if kind == "gelu":
+        z = h1
+        return z * sigmoid(np.sqrt(8.0 / np.pi) * (z + 0.044715 * z ** 3))
+    inter = h1.shape[1] // 2
+    g, u = h1[:, :inter], h1[:, inter:]
+    gc, uc = np.minimum(g, c), np.clip(u, -c, c)
+    if kind == "swiglu":
+        return silu(gc) * uc
+    if kind == "swiglustep":
+        return np.minimum(silu(g), c) * uc
+    if kind == "swigluoai":
+        return gc * sigmoid(alpha * gc) * (uc + beta)
+    if kind == "situglu":
+        lu = u if lin is None else lin * np.tanh(u / lin)
+        return beta * np.tanh(g / beta) * sigmoid(g) * lu
+    raise ValueError(kind)
 
 
 def gmm(aq, sa, wq, ws, fmt):
@@ -44,11 +112,12 @@ def gmm(aq, sa, wq, ws, fmt):
     return ad @ wd.T
 
 
-def expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt):
-    """Stages 2-3 for the rows of one expert. xq/sx: [m, H] codes/scales."""
-    inter = w2q.shape[1]
+def expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt, act=("swiglu", ())):
+    """Stages 2-3 for the rows of one expert. xq/sx: [m, H] codes/scales;
+    act = (activation kind, parameter list)."""
     h1 = gmm(xq, sx, w1q, w1s, fmt)
-    a = mxfp.fp32_round(swiglu(h1[:, :inter], h1[:, inter:]))
+    a = mxfp.fp32_round(activate(h1, *act))
+    assert a.shape[1] == w2q.shape[1], "weight2's input width must equal A's"
     aq, sa = mxfp.quantize(a, fmt)
     o = gmm(aq, sa, w2q, w2s, fmt)
     return dict(h1=h1, a=a, aq=aq, sa=sa, o=o)
@@ -76,7 +145,7 @@ def combine(o_rows, expanded_row_idx, topk_weights, shared_o=()):
     return mxfp.bf16_round(y)
 
 
-def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=()) -> dict:
+def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), act=("swiglu", ())) -> dict:
     """The whole layer on all tokens, in the permuted (expert-contiguous) order.
 
     x: [N, H] values (bf16 as float64); topk_ids int [N, K]; topk_weights [N, K];
@@ -94,13 +163,14 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=()) ->
     for e in range(num_experts):
         lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
         if hi > lo:
-            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt)
+            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt, act)
     hidden = x.shape[1]
-    inter = get(0)[2].shape[1]
+    two_i = get(0)[0].shape[0]
+    aw = get(0)[2].shape[1]            # width of A: I (gated) or 2I (gelu)
     out = dict(routing=r, xq=xq, sx=sx,
-               h1=np.zeros((flat, 2 * inter)), a=np.zeros((flat, inter)),
-               aq=np.zeros((flat, inter), np.uint8),
-               sa=np.zeros((flat, mxfp.scale_cols(inter)), np.uint8),
+               h1=np.zeros((flat, two_i)), a=np.zeros((flat, aw)),
+               aq=np.zeros((flat, aw), np.uint8),
+               sa=np.zeros((flat, mxfp.scale_cols(aw)), np.uint8),
                o=np.zeros((flat, hidden)))
     for e, p in parts.items():
         lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
@@ -111,7 +181,7 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=()) ->
         xq_tok, sx_tok = mxfp.quantize(x, fmt)
         out["xq_tok"], out["sx_tok"] = xq_tok, sx_tok
         for sw in shared:
-            shared_o.append(expert_ffn(xq_tok, sx_tok, *sw, fmt)["o"])
+            shared_o.append(expert_ffn(xq_tok, sx_tok, *sw, fmt, act)["o"])
     out["shared_o"] = shared_o
     full_scatter = routing.inverse(r["sorted_row_idx"])
     out["y"] = combine(out["o"], full_scatter, topk_weights, shared_o)
@@ -119,7 +189,7 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=()) ->
     return out
 
 
-def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=()) -> dict:
+def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("swiglu", ())) -> dict:
     """The layer for selected tokens, one (token, k) at a time, with no permutation
     (the "brute force" form of stage 1-4: each expert receives a copy of x_t).
 
@@ -146,12 +216,12 @@ def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=()) -> dic
         acc = np.zeros((1, x.shape[1]))
         h1_t, o_t = [], []
         for j in range(k):
-            r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt)
+            r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt, act)
             acc = acc + w[t, j] * r["o"]
             h1_t.append(r["h1"][0])
             o_t.append(r["o"][0])
         for sw in shared:
-            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt)["o"]
+            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt, act)["o"]
         ys.append(mxfp.bf16_round(acc)[0])
         h1s.append(h1_t)
         os_.append(o_t)

@@ -57,9 +57,12 @@ class MegaArgs(ctypes.Structure):
         ("aq", ctypes.c_void_p), ("sa", ctypes.c_void_p), ("o", ctypes.c_void_p),
         ("sorted_row_idx", ctypes.c_void_p),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
+        ("num_activation_params", ctypes.c_int), ("activation_params", ctypes.c_float * 3),
     ]
 
 MEGA_STAGE_EVENTS = 7
+# activation kinds of mega_moe (MegaMoE "Activation function formulas")
+ACT_SWIGLU, ACT_SWIGLUSTEP, ACT_SWIGLUOAI, ACT_SITUGLU, ACT_GELU = 0, 1, 2, 3, 4
 MEGA_STAGES = ["routing", "permute_quant", "gmm1_swiglu_quant", "gmm2", "shared_experts", "combine"]
 
 
@@ -229,7 +232,7 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
 
 
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
-                 debug, weight_format=WEIGHTS_ND):
+                 debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=()):
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -244,7 +247,12 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
         a.num_shared = sw1.shape[0]
         a.shared_w1, a.shared_w1_scales = _ptr(_u8(sw1)), _ptr(_u8(ss1))
         a.shared_w2, a.shared_w2_scales = _ptr(_u8(sw2)), _ptr(_u8(ss2))
-    a.quant_out_dtype, a.activation, a.weight_format = quant_out_dtype, 0, weight_format
+    a.quant_out_dtype, a.activation, a.weight_format = quant_out_dtype, activation, weight_format
+    if len(activation_params) > 3:
+        raise ValueError("activation_params holds at most 3 values")
+    a.num_activation_params = len(activation_params)
+    for j, v in enumerate(activation_params):
+        a.activation_params[j] = float(v)
     a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
     for name in ("xq", "sx", "h1", "aq", "sa", "o", "sorted_row_idx"):
         setattr(a, name, _ptr(debug.get(name)) if debug else None)
@@ -253,7 +261,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
 
 def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
              quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None,
-             weight_format: int = WEIGHTS_ND):
+             weight_format: int = WEIGHTS_ND, activation: int = ACT_SWIGLU, activation_params=()):
     """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
     debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
 
@@ -263,13 +271,16 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     shared weights as returned by pack_weights; the code tensors keep their [E, N, K] shape).
     stage_events: optional list of MEGA_STAGE_EVENTS torch.cuda.Event(enable_timing=True) or
     None entries, recorded by the library on the stream at the boundaries of MEGA_STAGES
-    (a None entry is skipped; each record costs a few microseconds of GPU time)."""
+    (a None entry is skipped; each record costs a few microseconds of GPU time).
+    activation / activation_params: ACT_* and its parameter list as in the C header (gelu
+    makes A, and w2's input width, 2 * inter)."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
     inter = two_i // 2
+    aw = two_i if activation == ACT_GELU else inter   # width of A
     dev = x.device
     y = torch.empty((n, h), dtype=torch.bfloat16, device=dev)
     etn = torch.empty((e,), dtype=torch.int32, device=dev)
@@ -279,12 +290,12 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
         dbg = dict(xq=torch.empty((f, h), dtype=torch.uint8, device=dev),
                    sx=torch.empty((f, h // 32), dtype=torch.uint8, device=dev),
                    h1=torch.empty((f, 2 * inter), dtype=torch.float32, device=dev),
-                   aq=torch.empty((f, inter), dtype=torch.uint8, device=dev),
-                   sa=torch.empty((f, inter // 32), dtype=torch.uint8, device=dev),
+                   aq=torch.empty((f, aw), dtype=torch.uint8, device=dev),
+                   sa=torch.empty((f, aw // 32), dtype=torch.uint8, device=dev),
                    o=torch.empty((f, h), dtype=torch.float32, device=dev),
                    sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg,
-                     weight_format)
+                     weight_format, activation, activation_params)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} entries (events or None)")
@@ -304,10 +315,11 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
 
 
 def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
-                             quant_out_dtype: int = FP8_E4M3, weight_format: int = WEIGHTS_ND) -> int:
+                             quant_out_dtype: int = FP8_E4M3, weight_format: int = WEIGHTS_ND,
+                             activation: int = ACT_SWIGLU, activation_params=()) -> int:
     lib = load()
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None,
-                     weight_format)
+                     weight_format, activation, activation_params)
     nbytes = ctypes.c_size_t()
     _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     return nbytes.value

@@ -7,6 +7,8 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cfloat>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <string>
@@ -140,9 +142,13 @@ struct MegaWs {
   float* o_sh;    // fp32 [num_shared, tokens, hidden]
 };
 
+// Width of GMM1's activation output A (= GMM2's K): inter for the gated activations,
+// 2 * inter for gelu ([MM] "Activation function formulas", gelu).
+int64_t act_width(const moe_mega_args* a) { return a->activation == MOE_ACT_GELU ? 2 * a->inter : a->inter; }
+
 MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   MegaWs w{};
-  const int64_t n = a->num_tokens, h = a->hidden, i = a->inter, e = a->num_experts;
+  const int64_t n = a->num_tokens, h = a->hidden, i = act_width(a), e = a->num_experts;
   const int64_t flat = n * a->topk;
   w.r = carve_route(cv, flat, (int)e, &w.nch, &w.chunk);
   w.scat = cv.take<int32_t>(flat);
@@ -174,6 +180,54 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   return w;
 }
 
+// activation + activation_params -> kernel parameters, with the pages' defaults
+// ([MM] parameter description of activation_params): clamp none (0 = none), alpha
+// 1.702, swigluoai beta 1.0, situglu beta 1.0 and no linear_beta.
+moe_status act_params(const moe_mega_args* a, moe::ActParams* out) {
+  const int np = a->num_activation_params;
+  const float* v = a->activation_params;
+  moe::ActParams p;
+  p.kind = a->activation;
+  auto bad = [&](const char* what) {
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: activation %d: %s", a->activation, what);
+  };
+  auto clamp_of = [&](float c, moe::ActParams* q) -> bool {
+    if (std::isnan(c) || c < 0.0f) return false;
+    if (c > 0.0f) q->clamp = c;
+    return true;
+  };
+  switch (a->activation) {
+    case MOE_ACT_SWIGLU:
+    case MOE_ACT_SWIGLUSTEP:
+      if (np != 0 && np != 1) return bad("takes [] or [clamp]");
+      if (np == 1 && !clamp_of(v[0], &p)) return bad("clamp must be >= 0 and not NaN");
+      break;
+    case MOE_ACT_SWIGLUOAI:
+      if (np != 0 && np != 3) return bad("takes [] or [clamp, alpha, beta]");
+      if (np == 3) {
+        if (!clamp_of(v[0], &p)) return bad("clamp must be >= 0 and not NaN");
+        if (!std::isfinite(v[1]) || !std::isfinite(v[2])) return bad("alpha and beta must be finite");
+        p.alpha = v[1];
+        p.beta = v[2];
+      }
+      break;
+    case MOE_ACT_SITUGLU:
+      if (np < 0 || np > 2) return bad("takes [], [beta] or [beta, linear_beta]");
+      for (int j = 0; j < np; ++j)
+        if (!std::isfinite(v[j]) || !(v[j] > 0.0f)) return bad("beta and linear_beta must be finite and > 0");
+      if (np >= 1) p.beta = v[0];
+      if (np == 2) p.lin_beta = v[1];
+      break;
+    case MOE_ACT_GELU:
+      if (np != 0 && !(np == 1 && v[0] == FLT_MAX)) return bad("takes no clamp ([] or the placeholder [FLT_MAX])");
+      break;
+    default:
+      return fail(MOE_ERR_INVALID_ARG, "mega_moe: activation %d not one of MOE_ACT_*", a->activation);
+  }
+  if (out) *out = p;
+  return MOE_OK;
+}
+
 moe_status check_mega(const moe_mega_args* a) {
   if (!a) return fail(MOE_ERR_INVALID_ARG, "mega_moe: args is NULL");
   if (a->num_tokens < 0) return fail(MOE_ERR_SHAPE, "mega_moe: num_tokens %lld < 0", (long long)a->num_tokens);
@@ -196,8 +250,7 @@ moe_status check_mega(const moe_mega_args* a) {
   if (a->quant_out_dtype != MOE_FP8_E5M2 && a->quant_out_dtype != MOE_FP8_E4M3)
     return fail(MOE_ERR_DTYPE, "mega_moe: quant_out_dtype %d must be 23 (FLOAT8_E5M2) or 24 (FLOAT8_E4M3FN)",
                 a->quant_out_dtype);
-  if (a->activation != MOE_ACT_SWIGLU)
-    return fail(MOE_ERR_UNSUPPORTED, "mega_moe: activation %d not supported (only swiglu)", a->activation);
+  if (moe_status st = act_params(a, nullptr)) return st;
   if (a->topk_weights_dtype != MOE_DTYPE_FP32 && a->topk_weights_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_DTYPE, "mega_moe: topk_weights_dtype must be FP32 or BF16");
   if (a->weight_format != MOE_WEIGHTS_ND && a->weight_format != MOE_WEIGHTS_PACKED)
@@ -464,8 +517,11 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     return a->stage_events && a->stage_events[k] ? hipEventRecord((hipEvent_t)a->stage_events[k], st) : hipSuccess;
   };
   const int64_t n = a->num_tokens, h = a->hidden, inter = a->inter, ne = a->num_experts;
+  const int64_t aw = act_width(a);   // width of A = K of GMM2
   const int64_t flat = n * a->topk;
   const int fmt = a->quant_out_dtype == MOE_FP8_E4M3 ? 0 : 1;
+  moe::ActParams act;
+  act_params(a, &act);
   int32_t* gath = a->sorted_row_idx ? a->sorted_row_idx : w.gath;
 
   // stage 1a: routing (full expert range, scatter + gather forms, combine row maps)
@@ -508,19 +564,18 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   // stage 2: GMM1 + SwiGLU + MX requantization
   const int packed = a->weight_format == MOE_WEIGHTS_PACKED;
   moe::Gmm1Params g1{w.xq, w.sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed};
+                     (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed, act};
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
   if (a->aq || a->sa) {
-    e = moe::launch_unpack_tokens(w.aq, w.sa, (int)inter, w.tiles, w.tile_count, w.max_tiles, w.tt, a->aq, a->sa,
-                                  st);
+    e = moe::launch_unpack_tokens(w.aq, w.sa, (int)aw, w.tiles, w.tile_count, w.max_tiles, w.tt, a->aq, a->sa, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe unpack launch");
   }
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 3: GMM2, O rows in fp32
   float* o = a->o ? a->o : w.o;
   moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, o, packed};
+                     (int)h, (int)aw, fmt, w.tt, o, packed};
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
@@ -529,12 +584,12 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + s * 2 * inter * h,
                        a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
                        w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr,
-                       packed};
+                       packed, act};
     e = moe::launch_gmm1(s1, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
-    moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * inter,
-                       a->shared_w2_scales + s * group_scale_bytes(h, inter, a->weight_format), w.sh_tiles,
-                       w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.o_sh + s * n * h, packed};
+    moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * aw,
+                       a->shared_w2_scales + s * group_scale_bytes(h, aw, a->weight_format), w.sh_tiles,
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)aw, fmt, w.sh_tt, w.o_sh + s * n * h, packed};
     e = moe::launch_gmm2(s2, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
   }

@@ -383,13 +383,76 @@ __device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&w
 // accumulators.
 template <int NT> struct WavesPerEU { static constexpr int value = NT <= 2 ? 2 : 1; };
 
-// ---- GMM1 + SwiGLU + MX requantization ------------------------------------------
-template <int FMT, int NT, bool PACKED>
+// ---- activations (MegaMoE README, "Activation function formulas") ------------------
+// sigma(z) = 1 / (1 + e^-z); SiLU(z) = z sigma(z); with the clamp c (+inf when none),
+// Gc = min(G, c), Uc = clip(U, -c, c).
+__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+
+// swiglu: SiLU(Gc) Uc.
+__device__ __forceinline__ float swiglu_act(float g, float u, float c) {
+  const float gc = fminf(g, c), uc = fminf(fmaxf(u, -c), c);
+  return gc / (1.0f + expf(-gc)) * uc;
+}
+
+// The gated activations of one (gate, up) pair; KIND = ActParams::kind (0-3).
+// GMM1's epilogue is a template parameter (EPI = the activation kind), so that each
+// kernel holds only its own activation code: with several behind a run-time switch
+// the 256-row kernel runs out of registers and spills accumulators in its K loop.
+template <int KIND>
+__device__ __forceinline__ float gated_act(float g, float u, const ActParams& p) {
+  if constexpr (KIND == 1) {  // swiglustep: min(SiLU(G), c) Uc
+    const float uc = fminf(fmaxf(u, -p.clamp), p.clamp);
+    return fminf(g / (1.0f + expf(-g)), p.clamp) * uc;
+  } else if constexpr (KIND == 2) {  // swigluoai: Gc sigma(alpha Gc) (Uc + beta)
+    const float gc = fminf(g, p.clamp), uc = fminf(fmaxf(u, -p.clamp), p.clamp);
+    return gc * sigmoid(p.alpha * gc) * (uc + p.beta);
+  } else if constexpr (KIND == 3) {  // situglu: beta tanh(G / beta) sigma(G) L(U) (no clamp)
+    const float l = p.lin_beta > 0.0f ? p.lin_beta * tanhf(u / p.lin_beta) : u;
+    return p.beta * tanhf(g / p.beta) * sigmoid(g) * l;
+  } else {
+    return swiglu_act(g, u, p.clamp);
+  }
+}
+
+// gelu (tanh form), element-wise on every GMM1 output channel: Z sigma(sqrt(8/pi)(Z + 0.044715 Z^3)).
+__device__ __forceinline__ float gelu_act(float z) {
+  constexpr float kSqrt8OverPi = 1.5957691216057308f;
+  return z * sigmoid(kSqrt8OverPi * (z + 0.044715f * z * z * z));
+}
+
+// MX-quantize one 32-channel group held as 8 values per lane by the lanes of one 16-lane
+// row (lane groups g = 0..3, xor 16 / 32), and store it into the tiled A layout at K step
+// `step`, half `half` of the step, lane groups 2 * sub + jj: act[jj][i] is channel
+// 16 jj + 4 g + i of the group.
+template <int FMT>
+__device__ __forceinline__ void store_group(const float (&act)[2][4], uint8_t* __restrict__ aq,
+                                            uint8_t* __restrict__ sa, int64_t tl, int ks2, int kq2, int step,
+                                            int cw, int g, int r) {
+  int m = 0;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) m = max(m, __float_as_int(fabsf(act[jj][i])));
+  m = max(m, __shfl_xor(m, 16));
+  m = max(m, __shfl_xor(m, 32));
+  const int b = mx_scale_byte<FMT>(__int_as_float(m));
+  const float inv = mx_inv_scale(b);
+  uint8_t* ob = aq + t16_codes(tl, ks2, step) + (cw >> 1) * 1024;
+#pragma unroll
+  for (int jj = 0; jj < 2; ++jj) {
+    const uint32_t codes = pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
+    *reinterpret_cast<uint32_t*>(ob + ((2 * (cw & 1) + jj) * 16 + r) * 16 + 4 * g) = codes;
+  }
+  if (g == 0) sa[t16_scales(tl, kq2, step >> 2) + (cw * 16 + r) * 4 + (step & 3)] = (uint8_t)b;
+}
+
+// ---- GMM1 + activation + MX requantization --------------------------------------
+template <int FMT, int NT, bool PACKED, int EPI>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
 void gmm1_swiglu_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ sx, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
-    int inter, uint8_t* __restrict__ aq, uint8_t* __restrict__ sa, float* __restrict__ h1) {
+    int inter, uint8_t* __restrict__ aq, uint8_t* __restrict__ sa, float* __restrict__ h1, ActParams act_p) {
   extern __shared__ __align__(16) uint8_t lds[];
   // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -417,39 +480,38 @@ void gmm1_swiglu_kernel(
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
     k_loop<FMT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
 
-    // A^ goes out in the tiled layout with K = inter, where this block's 128 gate
-    // channels are exactly K step cb: the wave's 32 channels are half wave/2 of it,
-    // lane groups 2 (wave % 2) + jj, byte 4g + i, and its MX group is K-block `wave`.
-    const int ks2 = inter >> 7, kq2 = (ks2 + 3) >> 2;
+    // A^ goes out in the tiled layout with K = inter (2 inter for gelu), where this
+    // block's 128 gate channels are exactly K step cb: the wave's 32 channels are half
+    // wave/2 of it, lane groups 2 (wave % 2) + jj, byte 4g + i, and its MX group is
+    // K-block `wave`. For gelu the up half's channels are K step cb + inter/128.
+    // Every row of the tile is written: rows past the chunk are zero tokens (the tiled
+    // X holds zeros there), so they requantize to code 0 and scale 0.
+    const int ks2 = (EPI == kActGelu ? 2 * inter : inter) >> 7, kq2 = (ks2 + 3) >> 2;
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
       if (t >= ntt) continue;                   // uniform per wave
       const int rr = 16 * t + r;
       const int64_t tl = (int64_t)(row0 >> 4) + t;
-      float act[2][4];
-      int m = 0;
+      if constexpr (EPI == kActGelu) {
+        float ag[2][4], au[2][4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj)
+        for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float gv = acc[jj][t][i], uv = acc[2 + jj][t][i];
-          const float a = gv / (1.0f + expf(-gv)) * uv;
-          act[jj][i] = a;
-          m = max(m, __float_as_int(fabsf(a)));
-        }
-      m = max(m, __shfl_xor(m, 16));
-      m = max(m, __shfl_xor(m, 32));
-      const int b = mx_scale_byte<FMT>(__int_as_float(m));
-      const float inv = mx_inv_scale(b);
-      // Every row of the tile is written: rows past the chunk are zero tokens (the
-      // tiled X holds zeros there), so they requantize to code 0 and scale 0.
-      uint8_t* tb = aq + t16_codes(tl, ks2, cb) + (wave >> 1) * 1024;
+          for (int i = 0; i < 4; ++i) {
+            ag[jj][i] = gelu_act(acc[jj][t][i]);
+            au[jj][i] = gelu_act(acc[2 + jj][t][i]);
+          }
+        store_group<FMT>(ag, aq, sa, tl, ks2, kq2, cb, wave, g, r);
+        store_group<FMT>(au, aq, sa, tl, ks2, kq2, cb + (inter >> 7), wave, g, r);
+      } else {
+        float a2[2][4];
 #pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const uint32_t codes = pack4<FMT>(act[jj][0] * inv, act[jj][1] * inv, act[jj][2] * inv, act[jj][3] * inv);
-        *reinterpret_cast<uint32_t*>(tb + ((2 * (wave & 1) + jj) * 16 + r) * 16 + 4 * g) = codes;
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            a2[jj][i] = gated_act<EPI>(acc[jj][t][i], acc[2 + jj][t][i], act_p);
+        store_group<FMT>(a2, aq, sa, tl, ks2, kq2, cb, wave, g, r);
       }
-      if (g == 0) sa[t16_scales(tl, kq2, cb >> 2) + (wave * 16 + r) * 4 + (cb & 3)] = (uint8_t)b;
       if (h1 && rr < nrows) {
         const int64_t row = srow0 + rr;
 #pragma unroll
@@ -599,14 +661,14 @@ hipError_t persistent_shape(K kernel, size_t lds, LaunchShape* out) {
   return hipSuccess;
 }
 
-template <int FMT, int NT, bool PACKED>
+template <int FMT, int NT, bool PACKED, int EPI>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
-  auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED>;
+  auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
   kern<<<ls.grid, 256, ls.lds, st>>>(p.xq, p.sx, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.aq, p.sa,
-                                     p.h1);
+                                     p.h1, p.act);
   return hipGetLastError();
 }
 
@@ -620,14 +682,25 @@ hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
+template <int FMT, bool PACKED, int EPI>
+hipError_t gmm1_epi(const Gmm1Params& p, hipStream_t st) {
+  switch (p.tt) {
+    case 1: return gmm1_go<FMT, 1, PACKED, EPI>(p, st);
+    case 2: return gmm1_go<FMT, 2, PACKED, EPI>(p, st);
+    case 4: return gmm1_go<FMT, 4, PACKED, EPI>(p, st);
+    case 8: return gmm1_go<FMT, 8, PACKED, EPI>(p, st);
+    default: return gmm1_go<FMT, 16, PACKED, EPI>(p, st);
+  }
+}
+
 template <int FMT, bool PACKED>
 hipError_t gmm1_nt(const Gmm1Params& p, hipStream_t st) {
-  switch (p.tt) {
-    case 1: return gmm1_go<FMT, 1, PACKED>(p, st);
-    case 2: return gmm1_go<FMT, 2, PACKED>(p, st);
-    case 4: return gmm1_go<FMT, 4, PACKED>(p, st);
-    case 8: return gmm1_go<FMT, 8, PACKED>(p, st);
-    default: return gmm1_go<FMT, 16, PACKED>(p, st);
+  switch (p.act.kind) {
+    case 1: return gmm1_epi<FMT, PACKED, 1>(p, st);
+    case 2: return gmm1_epi<FMT, PACKED, 2>(p, st);
+    case 3: return gmm1_epi<FMT, PACKED, 3>(p, st);
+    case kActGelu: return gmm1_epi<FMT, PACKED, kActGelu>(p, st);
+    default: return gmm1_epi<FMT, PACKED, 0>(p, st);
   }
 }
 

@@ -95,6 +95,16 @@ struct PermuteParams {
 hipError_t launch_permute(const PermuteParams& p, hipStream_t stream);
 
 // ---- grouped GEMMs (gmm.hip) -------------------------------------------------------
+// GMM1's activation (MOE_ACT_* kinds; validated and defaulted by the API layer).
+struct ActParams {
+  int kind = 0;                  // 0 swiglu, 1 swiglustep, 2 swigluoai, 3 situglu, 4 gelu
+  float clamp = __builtin_huge_valf();   // c; +inf = no clamp
+  float alpha = 1.702f;          // swigluoai
+  float beta = 1.0f;             // swigluoai beta / situglu beta
+  float lin_beta = 0.0f;         // situglu linear beta; 0 = L(U) = U
+};
+constexpr int kActGelu = 4;
+
 // Token operands and GMM1's requantized output are in the tiled layout, indexed by the
 // chunks' padded rows; h1, o, row_token and row_weight are indexed by sorted rows.
 struct Gmm1Params {
@@ -102,9 +112,10 @@ struct Gmm1Params {
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
   const int4* tiles; const int* tile_count; int max_tiles;
   int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16)
-  uint8_t* aq; uint8_t* sa;                    // tiled [padded rows, I]
+  uint8_t* aq; uint8_t* sa;                    // tiled [padded rows, I] (2I for gelu)
   float* h1;                                   // nullable [rows, 2I]
   int packed;                                  // weights in the MFMA-native packed layout
+  ActParams act;                               // A = act(G, U) [rows, I], or gelu(Z) [rows, 2I]
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 

@@ -12,7 +12,7 @@ import torch
 
 import moe_inputs
 import routing_permute_mxfp8_amd as rp
-from oracle import mxfp
+from oracle import moe, mxfp
 
 DEV = "cuda"
 QMODE = {"e4m3": rp.QUANT_E4M3, "e5m2": rp.QUANT_E5M2}
@@ -30,10 +30,13 @@ def to_dev(a, dtype=None):
     return t.to(DEV)
 
 
-def oracle_weights(cfg, n_experts=None, shared=False):
-    """Oracle-quantized weights (numpy): w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I], w2s [E,H,I/32]."""
+def oracle_weights(cfg, n_experts=None, shared=False, gelu=False):
+    """Oracle-quantized weights (numpy): w1q [E,2I,H], w1s [E,2I,H/32], w2q [E,H,I], w2s [E,H,I/32]
+    (w2 [E,H,2I] for a gelu layer)."""
     n_experts = cfg.experts if n_experts is None else n_experts
     t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
+    if gelu:
+        t2 += "g"
     out = [[], [], [], []]
     for e in range(n_experts):
         q1, s1 = mxfp.quantize(moe_inputs.weight_master(cfg, t1, e).double().numpy(), cfg.fmt)
@@ -114,6 +117,26 @@ def swiglu_delta(h1_ref, abs_h1, k_len, inter):
     silu = g / (1.0 + np.exp(-g))
     a = silu * u
     return 1.1 * dg * (np.abs(u) + du) + np.abs(silu) * du + np.abs(a) * 2.0 ** -20 + 1e-30
+
+
+def act_delta(h1_ref, abs_h1, k_len, kind, params):
+    """Bound on |A_gpu - A_ref| for any activation: the largest change of A over the box
+    G +- dG, U +- dU (Z +- dZ for gelu) of GEMM errors, probed at its corners and centre
+    lines, with a 25% margin, plus a few fp32 roundings in the activation itself."""
+    gam = gemm_gamma(k_len)
+    d = gam * np.asarray(abs_h1)
+    a_ref = moe.activate(h1_ref, kind, params)
+    if kind == "gelu":
+        probes = [moe.activate(h1_ref + sz * d, kind, params) for sz in (-1.0, -0.5, 0.5, 1.0)]
+    else:
+        inter = h1_ref.shape[1] // 2
+        probes = []
+        for sg in (-1.0, 0.0, 1.0):
+            for su in (-1.0, 0.0, 1.0):
+                sh = np.concatenate([sg * d[:, :inter], su * d[:, inter:]], axis=1)
+                probes.append(moe.activate(h1_ref + sh, kind, params))
+    dev = np.max([np.abs(p - a_ref) for p in probes], axis=0)
+    return 1.25 * dev + np.abs(a_ref) * 2.0 ** -18 + 1e-30
 
 
 def check_requant(aq_gpu, sa_gpu, a_ref, delta, fmt, max_code_diff=0.02, max_scale_diff=0.01):

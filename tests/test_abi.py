@@ -3,6 +3,8 @@ its host-side validation rejects bad arguments before any launch (MegaMoE README
 Constraints: errors raised up front with the required bytes, no silent fallback).
 No call here reaches a kernel, so these run without a GPU."""
 import ctypes
+
+import numpy as np
 import os
 import re
 
@@ -131,7 +133,24 @@ def test_mega_moe_validation(lib):
     assert status(topk=0) == 2 and status(topk=33) == 2 and status(topk=9) == 2
     assert status(num_experts=2000) == 2
     assert status(quant_out_dtype=1) == 3
-    assert status(activation=3) == 4
+    assert status(activation=5) == 1 and status(activation=-1) == 1
+
+    def act(kind, *vals):
+        a = args(activation=kind, num_activation_params=len(vals))
+        for j, v in enumerate(vals):
+            a.activation_params[j] = v
+        b = ctypes.c_size_t()
+        return lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(b))
+
+    flt_max = float(np.finfo(np.float32).max)
+    assert act(0) == 0 and act(0, 7.0) == 0 and act(0, 0.0) == 0       # swiglu, clamp 0 = none
+    assert act(0, -1.0) == 1 and act(0, float("nan")) == 1 and act(0, 1.0, 2.0) == 1
+    assert act(1, 3.0) == 0 and act(1, 1.0, 1.0) == 1                   # swiglustep
+    assert act(2) == 0 and act(2, 7.0, 1.702, 1.0) == 0 and act(2, 7.0) == 1
+    assert act(2, 7.0, float("inf"), 1.0) == 1                          # swigluoai alpha finite
+    assert act(3) == 0 and act(3, 2.0) == 0 and act(3, 2.0, 4.0) == 0   # situglu
+    assert act(3, 0.0) == 1 and act(3, 2.0, -1.0) == 1
+    assert act(4) == 0 and act(4, flt_max) == 0 and act(4, 5.0) == 1     # gelu: no clamp
     assert status(topk_weights_dtype=1) == 3
     assert status(num_shared=5) == 2
     assert status(num_shared=1) == 1   # shared weights missing

@@ -14,7 +14,8 @@ import torch
 import moe_inputs
 import routing_permute_mxfp8_amd as rp
 from oracle import moe, mxfp, routing
-from gpu_support import (DEV, FP8, abs_gmm, check_gemm_elementwise, check_requant, library_weights, normwise_err,
+from gpu_support import (DEV, FP8, abs_gmm, act_delta, check_gemm_elementwise, check_requant, library_weights,
+                         normwise_err,
                          oracle_expert_from_gpu_masters, oracle_experts_parallel, oracle_weights, say, swiglu_delta,
                          to_dev, y_errors)
 
@@ -78,6 +79,56 @@ def test_small_layers(case, wdtype, wf):
     check_gemm_elementwise(h1_got, ref["h1"], h1_abs, cfg.hidden)
     delta = swiglu_delta(ref["h1"], h1_abs, cfg.hidden, cfg.inter)
     codes, scales = check_requant(dbg["aq"].cpu().numpy(), dbg["sa"].cpu().numpy(), ref["a"], delta, cfg.fmt)
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  h1 err {err:.3g} requant codes differing {codes:.3g} scales {scales:.3g} Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
+ACTS = [("swiglu", (0.8,)), ("swiglustep", (0.6,)), ("swiglustep", ()), ("swigluoai", ()),
+        ("swigluoai", (0.9, 1.2, 0.5)), ("situglu", (2.0,)), ("situglu", (1.5, 0.7)), ("situglu", ()),
+        ("gelu", ()), ("gelu", (float(np.finfo(np.float32).max),))]
+ACT_KIND = {"swiglu": rp.ACT_SWIGLU, "swiglustep": rp.ACT_SWIGLUSTEP, "swigluoai": rp.ACT_SWIGLUOAI,
+            "situglu": rp.ACT_SITUGLU, "gelu": rp.ACT_GELU}
+
+
+@pytest.mark.parametrize("kind,params", ACTS, ids=lambda v: str(v))
+@pytest.mark.parametrize("tt", ["small", "wide"])
+def test_activations(kind, params, tt):
+    """MegaMoE "Activation function formulas": every activation and parameter list, routed
+    and shared experts, in 1-tile (small) and 16-tile (wide) chunks; clamps that bite."""
+    if tt == "small":
+        cfg = moe_inputs.config("tiny", tokens=96, hidden=256, inter=256, experts=8, topk=2, shared=1, seed=47)
+    else:
+        cfg = moe_inputs.config("tiny", tokens=600, hidden=256, inter=128, experts=4, topk=2, shared=1, seed=48)
+    say(f"mega_moe activation {kind} {params} N={cfg.tokens} I={cfg.inter} E={cfg.experts}")
+    gelu = kind == "gelu"
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    x = x_t.double().numpy()
+    w = moe_inputs.gate_weights(cfg)
+    weights = oracle_weights(cfg, gelu=gelu)
+    sh = oracle_weights(cfg, cfg.shared, shared=True, gelu=gelu)
+    wf = rp.WEIGHTS_PACKED
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf),
+                              shared=tuple(device_weights(sh, wf)), quant_out_dtype=FP8[cfg.fmt], debug=True,
+                              weight_format=wf, activation=ACT_KIND[kind], activation_params=params)
+    torch.cuda.synchronize()
+    act = (kind, params)
+    ref = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=[tuple(a[0] for a in sh)], act=act)
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    h1_got = dbg["h1"].cpu().numpy()
+    err = normwise_err(h1_got, ref["h1"])
+    assert err <= 2e-3, err
+    offs = ref["routing"]["offsets"]
+    h1_abs = np.zeros_like(ref["h1"])
+    for e in range(cfg.experts):
+        if offs[e + 1] > offs[e]:
+            h1_abs[offs[e]:offs[e + 1]] = abs_gmm(ref["xq"][offs[e]:offs[e + 1]], ref["sx"][offs[e]:offs[e + 1]],
+                                                  weights[0][e], weights[1][e], cfg.fmt)
+    delta = act_delta(ref["h1"], h1_abs, cfg.hidden, kind, params)
+    aq, sa = dbg["aq"].cpu().numpy(), dbg["sa"].cpu().numpy()
+    assert aq.shape[1] == (2 * cfg.inter if gelu else cfg.inter)
+    codes, scales = check_requant(aq, sa, ref["a"], delta, cfg.fmt)
     mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
     say(f"  h1 err {err:.3g} requant codes differing {codes:.3g} scales {scales:.3g} Y max {mx:.3g} mean {mean:.3g}")
     assert mx <= 2e-2 and mean <= 5e-3

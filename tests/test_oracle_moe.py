@@ -40,6 +40,77 @@ def test_silu_closed_forms():
     assert moe.swiglu(np.array([0.0]), np.array([5.0]))[0] == 0.0
 
 
+def _h1(g, u):
+    return np.concatenate([np.atleast_2d(np.asarray(g, np.float64)), np.atleast_2d(np.asarray(u, np.float64))],
+                          axis=1)
+
+
+def test_activation_special_cases():
+    """MegaMoE "Activation function formulas", checked through special cases that reduce
+    to something else: no clamp gives the plain SwiGLU; a clamp saturates G from above and
+    U on both sides; swigluoai with alpha = 1, beta = 0 is SwiGLU and with alpha = 0 is
+    G (U + beta) / 2; situglu with a huge beta is SwiGLU; G = 0 gives 0 for every gated kind."""
+    rng = np.random.default_rng(3)
+    g, u = rng.normal(0, 2, (4, 64)), rng.normal(0, 2, (4, 64))
+    h1 = np.concatenate([g, u], axis=1)
+    plain = moe.swiglu(g, u)
+    assert np.array_equal(moe.activate(h1, "swiglu"), plain)
+    assert np.array_equal(moe.activate(h1, "swiglu", (0.0,)), plain)          # clamp 0 = none
+    assert np.allclose(moe.activate(h1, "swigluoai", (0.0, 1.0, 0.0)), plain, rtol=1e-14, atol=0)
+    assert np.allclose(moe.activate(h1, "situglu", (1e7,)), plain, rtol=1e-9, atol=1e-12)
+    half = moe.activate(h1, "swigluoai", (0.0, 0.0, 0.75))
+    assert np.allclose(half, g * (u + 0.75) / 2.0, rtol=1e-14, atol=0)
+    for kind in ("swiglu", "swiglustep", "swigluoai", "situglu"):
+        assert np.all(moe.activate(_h1(np.zeros(8), rng.normal(size=8)), kind) == 0.0)
+    # clamp c = 1.5: G = 10 -> G_c = 1.5; U = -9 -> -1.5, U = 0.25 unchanged
+    a = moe.activate(_h1([10.0, 10.0], [-9.0, 0.25]), "swiglu", (1.5,))[0]
+    s15 = 1.5 / (1.0 + math.exp(-1.5))
+    assert a[0] == pytest.approx(-1.5 * s15, rel=1e-15) and a[1] == pytest.approx(0.25 * s15, rel=1e-15)
+    # swiglustep clamps SiLU(G) itself, not G: SiLU(10) ~ 10 -> 2; SiLU(1) < 2 untouched
+    st = moe.activate(_h1([10.0, 1.0], [1.0, 1.0]), "swiglustep", (2.0,))[0]
+    assert st[0] == 2.0 and st[1] == pytest.approx(1.0 / (1.0 + math.exp(-1.0)), rel=1e-15)
+    # situglu's linear beta: L(U) = lb tanh(U / lb) saturates at lb
+    sl = moe.activate(_h1([50.0], [1e6]), "situglu", (3.0, 0.5))[0]
+    assert sl[0] == pytest.approx(3.0 * 1.0 * 0.5, rel=1e-12)
+
+
+def test_activation_defaults():
+    """Empty parameter lists take the pages' defaults: swigluoai (no clamp, alpha 1.702,
+    beta 1.0), situglu (beta 1.0, L(U) = U)."""
+    rng = np.random.default_rng(4)
+    h1 = rng.normal(0, 3, (3, 40))
+    assert np.array_equal(moe.activate(h1, "swigluoai"), moe.activate(h1, "swigluoai", (0.0, 1.702, 1.0)))
+    assert np.array_equal(moe.activate(h1, "situglu"), moe.activate(h1, "situglu", (1.0,)))
+    assert np.array_equal(moe.activate(h1, "gelu"), moe.activate(h1, "gelu", (float(np.finfo(np.float32).max),)))
+
+
+def test_gelu_tanh_form_and_width():
+    """The page writes gelu two ways: Z (1 + tanh(sqrt(2/pi)(Z + 0.044715 Z^3))) / 2 and
+    Z sigma(sqrt(8/pi)(...)); the oracle uses the second, the first must agree (since
+    (1 + tanh x) / 2 = sigma(2x)). gelu keeps every channel: [m, 2I] in, [m, 2I] out,
+    and gelu(0) = 0, gelu(Z) -> Z for large Z, -> 0 for very negative Z."""
+    z = np.linspace(-8, 8, 321).reshape(3, 107)
+    tanh_form = 0.5 * z * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (z + 0.044715 * z ** 3)))
+    got = moe.activate(z, "gelu")
+    assert got.shape == z.shape
+    assert np.allclose(got, tanh_form, rtol=1e-13, atol=1e-15)
+    edge = moe.activate(np.array([[0.0, 30.0, -30.0]]), "gelu")[0]
+    assert edge[0] == 0.0 and edge[1] == pytest.approx(30.0, rel=1e-15) and abs(edge[2]) < 1e-300
+
+
+def test_gelu_layer_uses_all_channels():
+    """A gelu expert: A = gelu(h1) over all 2I channels and weight2 has 2I inputs."""
+    cfg = moe_inputs.config("tiny", tokens=16, hidden=64, inter=64, experts=2, topk=1, seed=5)
+    x, ids, w = layer_inputs(cfg)
+    w1q, w1s = mxfp.quantize(moe_inputs.weight_master(cfg, "w1", 0).double().numpy(), cfg.fmt)
+    w2q, w2s = mxfp.quantize(moe_inputs.weight_master(cfg, "w2g", 0).double().numpy(), cfg.fmt)
+    assert w2q.shape == (64, 128)
+    xq, sx = mxfp.quantize(x, cfg.fmt)
+    r = moe.expert_ffn(xq, sx, w1q, w1s, w2q, w2s, cfg.fmt, ("gelu", ()))
+    assert r["a"].shape == (16, 128) and r["aq"].shape == (16, 128)
+    assert np.array_equal(r["a"], mxfp.fp32_round(moe.activate(r["h1"], "gelu")))
+
+
 def test_gate_is_first_half_up_is_second_half():
     """x one-hot at k=0 with value 1, all scales 2^0: G = W1[n, 0], U = W1[I + n, 0].
     With G=2, U=3 the activation is SiLU(2)*3 (swapping the halves would give SiLU(3)*2)."""

@@ -58,8 +58,11 @@ typedef enum {
 enum { MOE_DTYPE_FP32 = 0, MOE_DTYPE_FP16 = 1, MOE_DTYPE_BF16 = 2,
        MOE_DTYPE_INT32 = 3, MOE_DTYPE_INT64 = 4 };
 
-/* quantMode values of [V3] / quant_mode of [TP]: -1 none, 2 MXFP8 E5M2, 3 MXFP8 E4M3FN. */
-enum { MOE_QUANT_NONE = -1, MOE_QUANT_MXFP8_E5M2 = 2, MOE_QUANT_MXFP8_E4M3 = 3 };
+/* quantMode values of [V3] / quant_mode of [TP]: -1 none, 2 MXFP8 E5M2, 3 MXFP8 E4M3FN, */
+/* 9 MXFP4 E2M1. MXFP4 codes are stored two per byte: element 2j in the low nibble,   */
+/* 2j + 1 in the high nibble, so a row of `hidden` elements takes hidden / 2 bytes; E2M1 */
+/* has magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (sign bit 0x8, no inf or NaN), emax 2.       */
+enum { MOE_QUANT_NONE = -1, MOE_QUANT_MXFP8_E5M2 = 2, MOE_QUANT_MXFP8_E4M3 = 3, MOE_QUANT_MXFP4_E2M1 = 9 };
 
 /* dispatchQuantOutDtype values of [MM]: 23 FLOAT8_E5M2, 24 FLOAT8_E4M3FN. */
 enum { MOE_FP8_E5M2 = 23, MOE_FP8_E4M3 = 24 };
@@ -67,8 +70,8 @@ enum { MOE_FP8_E5M2 = 23, MOE_FP8_E4M3 = 24 };
 /* rowIdxType of [V3]: 0 gather-type index, 1 scatter-type index. */
 enum { MOE_ROW_IDX_GATHER = 0, MOE_ROW_IDX_SCATTER = 1 };
 
-/* expertTokensNumType of [V3]: 0 cumsum, 1 count. */
-enum { MOE_TOKENS_CUMSUM = 0, MOE_TOKENS_COUNT = 1 };
+/* expertTokensNumType of [V3]: 0 cumsum, 1 count, 2 key_value. */
+enum { MOE_TOKENS_CUMSUM = 0, MOE_TOKENS_COUNT = 1, MOE_TOKENS_KEY_VALUE = 2 };
 
 /* Largest expert count accepted ([V3] expertNum range, non key_value modes). */
 #define MOE_MAX_EXPERTS 10240
@@ -89,14 +92,15 @@ int64_t moe_mx_scale_cols(int64_t cols);
 /* MX quantization of rows (weight preparation; the same Q_MX as stage 1 of   */
 /* [MM] "A8W8-FP quantization scenario").                                    */
 /*   x        device, [rows, cols] of `dtype` (BF16, FP16 or FP32), row-major */
-/*   quant_mode  MOE_QUANT_MXFP8_E5M2 or MOE_QUANT_MXFP8_E4M3                 */
-/*   codes    device out, uint8 [rows, cols] FP8 codes                        */
+/*   quant_mode  MOE_QUANT_MXFP8_E5M2, MOE_QUANT_MXFP8_E4M3 or MOE_QUANT_MXFP4_E2M1 */
+/*   codes    device out, uint8 [rows, cols] FP8 codes ([rows, cols / 2] MXFP4) */
 /*   scales   device out, uint8 [rows, moe_mx_scale_cols(cols)] E8M0 bytes;   */
 /*            a padding column (odd group count) is written as 0x00           */
 /* Scale rule: E8M0 = clamp(floor(log2(amax of the 32-group)) - emax + 127,   */
-/* 0, 254), emax 8 (E4M3) / 15 (E5M2), 0 for an all-zero group; elements are   */
-/* x / 2^(E8M0-127) rounded to nearest-even and clamped to the largest finite */
-/* FP8 value, sign kept. Requires cols % 8 == 0. No workspace.                */
+/* 0, 254), emax 8 (E4M3) / 15 (E5M2) / 2 (E2M1), 0 for an all-zero group;    */
+/* elements are x / 2^(E8M0-127) rounded to nearest-even and clamped to the     */
+/* largest finite value of the format, sign kept. Requires cols % 8 == 0. No    */
+/* workspace.                                                                   */
 /* ------------------------------------------------------------------------ */
 moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols, int quant_mode,
                            uint8_t* codes, uint8_t* scales, void* stream);
@@ -125,20 +129,25 @@ moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 /*   expert_idx   device, int32 [num_rows, k]; flat row r = t*k + j            */
 /*   expert_num   number of experts E, 1..MOE_MAX_EXPERTS                      */
 /*   active_start, active_end  activeExpertRange [s, e), 0 <= s <= e <= E     */
-/*   quant_mode   -1, 2 or 3 (MX modes need hidden % 32 == 0)                  */
-/*   row_idx_type 0 gather / 1 scatter; expert_tokens_num_type 0 cumsum / 1 count */
+/*   quant_mode   -1, 2, 3 or 9 (MX modes need hidden % 32 == 0)               */
+/*   row_idx_type 0 gather / 1 scatter; expert_tokens_num_type 0 cumsum /      */
+/*                1 count / 2 key_value (then expert_num <= 5120)               */
 /* Outputs (device):                                                            */
 /*   expanded_x        [num_rows*k, hidden]: row i (< availableIdxNum) holds     */
 /*                     Q(x[src(i) / k]) where src(i) is the flat row at position */
 /*                     i of the stable expert-major order restricted to [s, e);  */
-/*                     FP8 codes in MX modes, x_dtype values otherwise. Rows     */
+/*                     FP8 codes in MX modes (packed MXFP4, hidden / 2 bytes a  */
+/*                     row, in mode 9), x_dtype values otherwise. Rows           */
 /*                     >= availableIdxNum are not written.                      */
 /*   expanded_row_idx  int32 [num_rows*k]. Scatter type: entry r = position of   */
 /*                     flat row r in expanded_x, or -1 if its expert is outside  */
 /*                     [s, e). Gather type: entry i < availableIdxNum = src(i),  */
 /*                     the rest -1.                                             */
 /*   expert_tokens     int64 [e - s]: per-expert counts (count) or their          */
-/*                     inclusive prefix sum (cumsum)                             */
+/*                     inclusive prefix sum (cumsum); key_value: int64           */
+/*                     [expert_num, 2], one row (expert id, count) per expert of */
+/*                     [s, e) with a non-zero count, ascending, then zero rows   */
+/*                     (the pages leave those rows open)                        */
 /*   expanded_scale    uint8 [num_rows*k, moe_mx_scale_cols(hidden)] in MX modes  */
 /*                     (NULL allowed when quant_mode = -1)                       */
 /*   available_idx_num int64 [1]: #{r : s <= expert_idx[r] < e}                 */
@@ -164,7 +173,7 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
 /*   num_out_tokens  0 = None; > 0 keeps min(n_out, F) rows; < 0 drops |n_out| */
 /*                 rows from the end (M = max(F + n_out, 0))                   */
 /*   padded_mode   must be 0 (MOE_ERR_UNSUPPORTED otherwise)                   */
-/*   quant_mode    -1, 2 or 3                                                   */
+/*   quant_mode    -1, 2, 3 or 9 (permuted_tokens rows of hidden / 2 bytes)      */
 /* Outputs (device):                                                            */
 /*   permuted_tokens  [M, hidden]: row i = Q(tokens[first(i) / topk]) where      */
 /*                    first = stable argsort of the flattened indices           */

@@ -1,4 +1,4 @@
-"""FP8 (E4M3FN, E5M2), E8M0 and MX group quantization, in float64.
+"""FP8 (E4M3FN, E5M2), FP4 (E2M1), E8M0 and MX group quantization, in float64.
 
 MegaMoE page, "A8W8-FP quantization scenario", stage 1: Q_MX takes groups of
 32 consecutive elements, extracts a shared exponent per group (an E8M0 scale
@@ -18,6 +18,12 @@ definitions, the standard meaning of a per-group shared exponent stored as E8M0:
 Scale storage (moe_token_permute 返回值说明, MegaMoE "MXFP quantization
 scenario constraints"): [rows, AlignUp(CeilDiv(cols, 32), 2)] bytes, i.e. pairs
 of scales; a padding scale (odd group count) is 0x00.
+
+MXFP4 (quantMode 9 of MoeInitRoutingV3 / moe_token_permute): FLOAT4_E2M1 elements
+(1 sign, 2 exponent bits with bias 1, 1 mantissa bit; values 0, 0.5, 1, 1.5, 2, 3,
+4, 6; no inf or NaN), emax_elem = 2, the same E8M0 scale rule and storage. Two
+codes share a byte (moe_token_permute: hidden dimension H / 2 in bytes); reading:
+element 2j in the low nibble, 2j + 1 in the high nibble (pack_fp4).
 """
 
 from __future__ import annotations
@@ -32,21 +38,28 @@ GROUP = 32
 FORMATS = {
     "e4m3": (4, 3, 7, False),   # FLOAT8_E4M3FN: no inf, only S.1111.111 is NaN
     "e5m2": (5, 2, 15, True),   # FLOAT8_E5M2: IEEE-like inf and NaN
+    "e2m1": (2, 1, 1, False),   # FLOAT4_E2M1: every code finite
 }
-EMAX = {"e4m3": 8, "e5m2": 15}
+EMAX = {"e4m3": 8, "e5m2": 15, "e2m1": 2}
+
+
+def code_bits(fmt: str) -> int:
+    eb, mb, _, _ = FORMATS[fmt]
+    return 1 + eb + mb
 
 
 @functools.lru_cache(maxsize=None)
 def _decode_table(fmt: str) -> np.ndarray:
     eb, mb, bias, has_inf = FORMATS[fmt]
-    out = np.empty(256, dtype=np.float64)
-    for code in range(256):
-        sign = -1.0 if code & 0x80 else 1.0
+    nbits = code_bits(fmt)
+    out = np.empty(1 << nbits, dtype=np.float64)
+    for code in range(1 << nbits):
+        sign = -1.0 if code >> (nbits - 1) else 1.0
         e = (code >> mb) & ((1 << eb) - 1)
         m = code & ((1 << mb) - 1)
         if e == (1 << eb) - 1 and has_inf:
             val = np.inf if m == 0 else np.nan
-        elif e == (1 << eb) - 1 and m == (1 << mb) - 1 and not has_inf:
+        elif e == (1 << eb) - 1 and m == (1 << mb) - 1 and not has_inf and nbits == 8:
             val = np.nan
         elif e == 0:
             val = m * 2.0 ** (1 - bias - mb)          # subnormal
@@ -58,7 +71,7 @@ def _decode_table(fmt: str) -> np.ndarray:
 
 
 def decode_table(fmt: str) -> np.ndarray:
-    """float64[256]: the value of every code, from the sign/exponent/mantissa fields."""
+    """float64[2^bits]: the value of every code, from the sign/exponent/mantissa fields."""
     return _decode_table(fmt)
 
 
@@ -89,10 +102,11 @@ def round_to_format(y: np.ndarray, fmt: str) -> np.ndarray:
     """Codes of y (already divided by the group scale): nearest value, ties to the
     even code, clamped to +-max finite, sign kept (-0 and negative underflow -> 0x80).
     Done by searching the table of the format's non-negative finite values, which is
-    increasing in the code (0x00 .. max code)."""
+    increasing in the code (0x00 .. max code). FP4 codes use 4 bits (sign 0x8)."""
     table = decode_table(fmt)
     top = max_finite(fmt)
-    pos_codes = np.array([c for c in range(128) if np.isfinite(table[c])], dtype=np.int64)
+    half = len(table) // 2
+    pos_codes = np.array([c for c in range(half) if np.isfinite(table[c])], dtype=np.int64)
     pos_vals = table[pos_codes]
     assert np.all(np.diff(pos_vals) > 0)
     y = np.asarray(y, dtype=np.float64)
@@ -108,7 +122,7 @@ def round_to_format(y: np.ndarray, fmt: str) -> np.ndarray:
     code = np.where(pick_hi, c_hi, c_lo)
     code = np.where(a == pos_vals[hi], c_hi, code)            # exact hits
     neg = np.signbit(y)
-    return (code | np.where(neg, 0x80, 0)).astype(np.uint8)
+    return (code | np.where(neg, half, 0)).astype(np.uint8)
 
 
 def quantize(v, fmt: str):
@@ -153,6 +167,21 @@ def _quantize_rows(v, fmt: str):
     scales = np.zeros(lead + (scale_cols(cols),), dtype=np.uint8)
     scales[..., :ngroups] = b.astype(np.uint8)
     return np.ascontiguousarray(codes), scales
+
+
+def pack_fp4(codes) -> np.ndarray:
+    """FP4 codes [..., C] (C even) -> bytes [..., C/2]: element 2j low nibble, 2j+1 high."""
+    c = np.asarray(codes, dtype=np.uint8)
+    assert c.shape[-1] % 2 == 0 and np.all(c < 16)
+    return (c[..., 0::2] | (c[..., 1::2] << 4)).astype(np.uint8)
+
+
+def unpack_fp4(packed) -> np.ndarray:
+    p = np.asarray(packed, dtype=np.uint8)
+    out = np.empty(p.shape[:-1] + (2 * p.shape[-1],), dtype=np.uint8)
+    out[..., 0::2] = p & 0xF
+    out[..., 1::2] = p >> 4
+    return out
 
 
 def dequantize(codes, scales, fmt: str) -> np.ndarray:

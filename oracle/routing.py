@@ -73,7 +73,8 @@ def init_routing(expert_idx, num_experts: int, active=None, row_idx_type: int = 
       active_start     int        offsets[s]
       avail            int        availableIdxNum
       expanded_row_idx int32 [F]  per row_idx_type (1 scatter, 0 gather)
-      expert_tokens    int64 [e-s] per tokens_num_type (1 count, 0 cumsum)
+      expert_tokens    int64 [e-s] per tokens_num_type (1 count, 0 cumsum), or
+                       [E, 2] (expert, count) rows for 2 (key_value)
     """
     keys, k = flatten_ids(expert_idx)
     assert keys.size == 0 or (keys.min() >= 0 and keys.max() < num_experts)
@@ -100,25 +101,36 @@ def init_routing(expert_idx, num_experts: int, active=None, row_idx_type: int = 
         tok = active_counts.copy()
     elif tokens_num_type == 0:
         tok = np.cumsum(active_counts)
+    elif tokens_num_type == 2:
+        # key_value (README, expertTokensCountOrCumsumOut): shape [num_experts, 2], one row
+        # (expert id, its row count) per active expert with a non-zero count, in ascending
+        # expert order. Reading: the rows past them are 0 (the pages leave them open).
+        tok = np.zeros((num_experts, 2), dtype=np.int64)
+        row = 0
+        for j, c in enumerate(active_counts):
+            if c > 0:
+                tok[row] = (s + j, c)
+                row += 1
     else:
-        raise ValueError("tokens_num_type must be 0 (cumsum) or 1 (count)")
+        raise ValueError("tokens_num_type must be 0 (cumsum), 1 (count) or 2 (key_value)")
     return dict(sorted_row_idx=sorted_row_idx, sorted_keys=sorted_keys, counts=counts,
                 offsets=offsets, active_start=off0, avail=avail, topk=k,
                 expanded_row_idx=idx.astype(np.int32), expert_tokens=tok.astype(np.int64))
 
 
 def quant_mode_format(quant_mode: int):
-    """quantMode 2 -> E5M2, 3 -> E4M3FN, -1 -> no quantization (None)."""
-    return {-1: None, 2: "e5m2", 3: "e4m3"}[quant_mode]
+    """quantMode 2 -> E5M2, 3 -> E4M3FN, 9 -> E2M1 (MXFP4), -1 -> no quantization (None)."""
+    return {-1: None, 2: "e5m2", 3: "e4m3", 9: "e2m1"}[quant_mode]
 
 
 def gather_rows(x, sorted_row_idx, topk: int, quant_mode: int, start: int = 0, count=None):
     """expandedX[i] = Q(x[sortedRowIdx[start + i] // K]) for i < count.
 
     x: float array [N, H] (bf16 values as float64). quant_mode -1 returns the
-    rows unchanged (float64) and scales None; 2/3 return (codes, scales) of the
+    rows unchanged (float64) and scales None; 2/3/9 return (codes, scales) of the
     MX quantization of each gathered row (Q_MX is row-local, so quantizing then
-    gathering is the same as gathering then quantizing)."""
+    gathering is the same as gathering then quantizing); for 9 the codes come
+    packed two per byte ([count, H / 2], mxfp.pack_fp4)."""
     x = np.asarray(x, dtype=np.float64)
     if count is None:
         count = sorted_row_idx.size - start
@@ -127,7 +139,10 @@ def gather_rows(x, sorted_row_idx, topk: int, quant_mode: int, start: int = 0, c
     fmt = quant_mode_format(quant_mode)
     if fmt is None:
         return rows, None
-    return mxfp.quantize(rows, fmt)
+    codes, scales = mxfp.quantize(rows, fmt)
+    if fmt == "e2m1":
+        codes = mxfp.pack_fp4(codes)
+    return codes, scales
 
 
 def actual_num_out_tokens(flat: int, num_out_tokens) -> int:

@@ -21,13 +21,13 @@ import torch
 from .build import lib_path
 
 __all__ = [
-    "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "FP8_E5M2", "FP8_E4M3",
+    "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "QUANT_MXFP4", "FP8_E5M2", "FP8_E4M3",
     "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "token_permute",
     "mega_moe", "mega_moe_workspace_bytes", "gmm1_swiglu_quant", "gmm2_combine", "combine_finalize",
     "pack_weights", "WEIGHTS_ND", "WEIGHTS_PACKED",
 ]
 
-QUANT_NONE, QUANT_E5M2, QUANT_E4M3 = -1, 2, 3
+QUANT_NONE, QUANT_E5M2, QUANT_E4M3, QUANT_MXFP4 = -1, 2, 3, 9
 FP8_E5M2, FP8_E4M3 = 23, 24
 WEIGHTS_ND, WEIGHTS_PACKED = 0, 1
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int32: 3, torch.int64: 4}
@@ -154,11 +154,12 @@ def token_permute_out_rows(flat: int, num_out_tokens) -> int:
 
 
 def mx_quantize(x: torch.Tensor, quant_mode: int = QUANT_E4M3):
-    """MX-quantize the rows of a 2-D bf16/fp16/fp32 tensor: (codes uint8 [R, C], scales uint8 [R, AlignUp(C/32, 2)])."""
+    """MX-quantize the rows of a 2-D bf16/fp16/fp32 tensor: (codes uint8 [R, C] ([R, C/2] packed
+    for QUANT_MXFP4), scales uint8 [R, AlignUp(C/32, 2)])."""
     lib = load()
     _need_gpu(x)
     rows, cols = x.shape
-    codes = torch.empty((rows, cols), dtype=torch.uint8, device=x.device)
+    codes = torch.empty((rows, cols // 2 if quant_mode == QUANT_MXFP4 else cols), dtype=torch.uint8, device=x.device)
     scales = torch.empty((rows, mx_scale_cols(cols)), dtype=torch.uint8, device=x.device)
     _check(lib.moe_mx_quantize(_ptr(x), _DT[x.dtype], rows, cols, quant_mode, _ptr(codes), _ptr(scales),
                                _stream(x.device)))
@@ -190,9 +191,13 @@ def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: 
     flat = n * k
     mx = quant_mode != QUANT_NONE
     dev = x.device
-    ex = torch.empty((flat, h), dtype=torch.uint8 if mx else x.dtype, device=dev)
+    ex = torch.empty((flat, h // 2 if quant_mode == QUANT_MXFP4 else h), dtype=torch.uint8 if mx else x.dtype,
+                     device=dev)
     idx = torch.empty((flat,), dtype=torch.int32, device=dev)
-    tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
+    if expert_tokens_num_type == 2:   # key_value: (expert, count) rows
+        tok = torch.empty((expert_num, 2), dtype=torch.int64, device=dev)
+    else:
+        tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
     sc = torch.empty((flat, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx else None
     avail = torch.empty((1,), dtype=torch.int64, device=dev)
     nbytes = ctypes.c_size_t()
@@ -217,7 +222,8 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
     m = token_permute_out_rows(flat, num_out_tokens)
     mx = quant_mode != QUANT_NONE
     dev = tokens.device
-    out = torch.empty((m, h), dtype=torch.uint8 if mx else tokens.dtype, device=dev)
+    out = torch.empty((m, h // 2 if quant_mode == QUANT_MXFP4 else h), dtype=torch.uint8 if mx else tokens.dtype,
+                      device=dev)
     srt = torch.empty((flat,), dtype=torch.int32, device=dev)
     sc = (torch.empty((m, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx
           else torch.empty((0,), dtype=torch.float32, device=dev))

@@ -88,7 +88,14 @@ RouteWs carve_route(Carver& cv, int64_t flat, int active, int* nch, int* chunk) 
   return w;
 }
 
-int quant_fmt(int quant_mode) { return quant_mode == MOE_QUANT_MXFP8_E4M3 ? 0 : 1; }
+// quantMode -> element format of the permute kernels: 0 E4M3FN, 1 E5M2, 2 E2M1 (MXFP4).
+int quant_fmt(int quant_mode) {
+  return quant_mode == MOE_QUANT_MXFP8_E4M3 ? 0 : quant_mode == MOE_QUANT_MXFP4_E2M1 ? 2 : 1;
+}
+
+bool valid_quant_mode(int q) {
+  return q == MOE_QUANT_NONE || q == MOE_QUANT_MXFP8_E5M2 || q == MOE_QUANT_MXFP8_E4M3 || q == MOE_QUANT_MXFP4_E2M1;
+}
 
 bool valid_x_dtype(int d) { return d == MOE_DTYPE_FP32 || d == MOE_DTYPE_FP16 || d == MOE_DTYPE_BF16; }
 
@@ -337,8 +344,8 @@ moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
     return fail(MOE_ERR_SHAPE, "moe_mx_quantize: rows %lld >= 0 and cols %lld > 0 with cols %% 8 == 0 required",
                 (long long)rows, (long long)cols);
   if (!valid_x_dtype(dtype)) return fail(MOE_ERR_DTYPE, "moe_mx_quantize: dtype %d not BF16/FP16/FP32", dtype);
-  if (quant_mode != MOE_QUANT_MXFP8_E4M3 && quant_mode != MOE_QUANT_MXFP8_E5M2)
-    return fail(MOE_ERR_UNSUPPORTED, "moe_mx_quantize: quant_mode %d not 2 or 3", quant_mode);
+  if (quant_mode != MOE_QUANT_MXFP8_E4M3 && quant_mode != MOE_QUANT_MXFP8_E5M2 && quant_mode != MOE_QUANT_MXFP4_E2M1)
+    return fail(MOE_ERR_UNSUPPORTED, "moe_mx_quantize: quant_mode %d not 2, 3 or 9", quant_mode);
   if (rows == 0) return ok();
   if (!x || !codes || !scales) return fail(MOE_ERR_INVALID_ARG, "moe_mx_quantize: NULL buffer");
   moe::PermuteParams p;
@@ -392,20 +399,22 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   const int64_t flat = num_rows * k;
   if (flat >= MOE_MAX_FLAT_ROWS) return fail(MOE_ERR_SHAPE, "%s: num_rows*k must be < %d", who, MOE_MAX_FLAT_ROWS);
   if (!valid_x_dtype(x_dtype)) return fail(MOE_ERR_DTYPE, "%s: x_dtype %d not FP32/FP16/BF16", who, x_dtype);
-  if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_MXFP8_E5M2 && quant_mode != MOE_QUANT_MXFP8_E4M3)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3)", who, quant_mode);
+  if (!valid_quant_mode(quant_mode))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3, 9)", who, quant_mode);
   const bool mx = quant_mode != MOE_QUANT_NONE;
   if (mx && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: MX quantization needs hidden %% 32 == 0", who);
   if (row_idx_type != MOE_ROW_IDX_GATHER && row_idx_type != MOE_ROW_IDX_SCATTER)
     return fail(MOE_ERR_INVALID_ARG, "%s: row_idx_type %d not 0 or 1", who, row_idx_type);
-  if (expert_tokens_num_type == 2)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: expert_tokens_num_type 2 (key_value) not supported", who);
-  if (expert_tokens_num_type != MOE_TOKENS_CUMSUM && expert_tokens_num_type != MOE_TOKENS_COUNT)
-    return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens_num_type %d not 0 or 1", who, expert_tokens_num_type);
+  if (expert_tokens_num_type != MOE_TOKENS_CUMSUM && expert_tokens_num_type != MOE_TOKENS_COUNT &&
+      expert_tokens_num_type != MOE_TOKENS_KEY_VALUE)
+    return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens_num_type %d not 0, 1 or 2", who, expert_tokens_num_type);
+  if (expert_tokens_num_type == MOE_TOKENS_KEY_VALUE && expert_num > 5120)
+    return fail(MOE_ERR_SHAPE, "%s: key_value counts take expert_num <= 5120 (got %lld)", who, (long long)expert_num);
   if (flat > 0 && (!x || !expert_idx || !expanded_x || !expanded_row_idx))
     return fail(MOE_ERR_INVALID_ARG, "%s: x, expert_idx, expanded_x, expanded_row_idx must be non-NULL", who);
   if (!available_idx_num) return fail(MOE_ERR_INVALID_ARG, "%s: available_idx_num must be non-NULL", who);
-  if (active_end > active_start && !expert_tokens)
+  const bool key_value = expert_tokens_num_type == MOE_TOKENS_KEY_VALUE;
+  if ((active_end > active_start || key_value) && !expert_tokens)
     return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens must be non-NULL", who);
   if (mx && flat > 0 && !expanded_scale) return fail(MOE_ERR_INVALID_ARG, "%s: expanded_scale must be non-NULL in MX modes", who);
   const int active = (int)(active_end - active_start);
@@ -421,7 +430,8 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   rp.keys = expert_idx; rp.key_is64 = 0; rp.flat = flat; rp.topk = (int)k;
   rp.s = (int)active_start; rp.e = (int)active_end; rp.nch = ws.nch; rp.chunk = ws.chunk;
   rp.hist = ws.r.hist; rp.base = ws.r.base; rp.totals = ws.r.totals; rp.offsets = ws.r.offsets;
-  rp.avail64 = available_idx_num; rp.expert_tokens = expert_tokens; rp.tokens_type = expert_tokens_num_type;
+  rp.avail64 = available_idx_num; rp.expert_tokens = key_value ? nullptr : expert_tokens;
+  rp.tokens_type = expert_tokens_num_type;
   if (want_gather) {
     rp.scat = ws.scat; rp.gath = expanded_row_idx; rp.gath_fill = expanded_row_idx;
   } else {
@@ -429,6 +439,10 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   }
   hipError_t e = moe::launch_routing(rp, st);
   if (e != hipSuccess) return hip_fail(e, "moe_init_routing routing launch");
+  if (key_value) {
+    e = moe::launch_key_value(ws.r.offsets, active, (int)active_start, (int)expert_num, expert_tokens, st);
+    if (e != hipSuccess) return hip_fail(e, "moe_init_routing key_value launch");
+  }
   moe::PermuteParams pp;
   pp.x = x; pp.in_dtype = x_dtype; pp.n = num_rows; pp.hidden = hidden; pp.topk = (int)k; pp.scat = rp.scat;
   pp.m_limit = flat; pp.quant = mx ? quant_fmt(quant_mode) : -1; pp.out = expanded_x;
@@ -464,8 +478,8 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
   if (indices_dtype != MOE_DTYPE_INT32 && indices_dtype != MOE_DTYPE_INT64)
     return fail(MOE_ERR_DTYPE, "%s: indices dtype must be INT32 or INT64", who);
   if (!valid_x_dtype(dtype)) return fail(MOE_ERR_DTYPE, "%s: tokens dtype %d not FP32/FP16/BF16", who, dtype);
-  if (quant_mode != MOE_QUANT_NONE && quant_mode != MOE_QUANT_MXFP8_E5M2 && quant_mode != MOE_QUANT_MXFP8_E4M3)
-    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3)", who, quant_mode);
+  if (!valid_quant_mode(quant_mode))
+    return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3, 9)", who, quant_mode);
   const bool mx = quant_mode != MOE_QUANT_NONE;
   if (mx && dtype == MOE_DTYPE_FP32) return fail(MOE_ERR_DTYPE, "%s: MX quant modes take FP16/BF16 tokens", who);
   if (mx && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: MX quantization needs hidden %% 32 == 0", who);

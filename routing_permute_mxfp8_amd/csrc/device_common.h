@@ -23,6 +23,30 @@ template <> struct Fp8<1> {
   static constexpr int emax = 15;         // 57344 = 1.75 * 2^15
   static constexpr float maxv = 57344.0f;
 };
+// 2 = FLOAT4_E2M1 (MXFP4; permute output only): magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6.
+template <> struct Fp8<2> {
+  static constexpr int emax = 2;          // 6 = 1.5 * 2^2
+  static constexpr float maxv = 6.0f;
+};
+
+// E2M1 code (sign 0x8) of a scaled float: round to the nearest of the eight
+// magnitudes, ties to the even code, saturating at 6; the sign is kept (negative
+// values that round to 0 give code 0x8, as the FP8 conversions do). The comparisons
+// against the midpoints 0.25, 0.75, ... are exact in fp32.
+__device__ __forceinline__ uint32_t fp4_code(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 31) << 3;
+  const float a = fabsf(y);
+  uint32_t c;
+  if (a <= 0.25f) c = 0;         // tie 0.25 -> 0
+  else if (a < 0.75f) c = 1;     // tie 0.75 -> 2
+  else if (a <= 1.25f) c = 2;    // tie 1.25 -> 2
+  else if (a < 1.75f) c = 3;     // tie 1.75 -> 4
+  else if (a <= 2.5f) c = 4;     // tie 2.5 -> 4
+  else if (a < 3.5f) c = 5;      // tie 3.5 -> 6
+  else if (a <= 5.0f) c = 6;     // tie 5 -> 6
+  else c = 7;                    // 6 and above (saturated)
+  return sign | c;
+}
 
 // E8M0 scale byte of an MX group (MegaMoE A8W8-FP stage 1 takes one shared exponent
 // per 32 elements; the OCP MX rule gives it): clamp(floor(log2(amax)) - emax + 127, 0, 254).

@@ -36,6 +36,9 @@ struct RouteParams {
   int topk_w_bf16 = 0;
 };
 hipError_t launch_routing(const RouteParams& p, hipStream_t stream);
+// key_value counts from the active offsets [active + 1] of a routing pass: int64
+// out[rows][2] = (s + a, count) for the experts with count > 0, ascending, then zeros.
+hipError_t launch_key_value(const int* offsets, int active, int s, int rows, int64_t* out, hipStream_t stream);
 
 // Chunks of up to `tm` rows (tm a multiple of 16) over groups given by int32 offsets
 // [groups + 1] (clamped into [0, rows], non-decreasing):

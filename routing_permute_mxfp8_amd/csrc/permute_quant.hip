@@ -103,16 +103,27 @@ __global__ __launch_bounds__(256) void permute_mx_kernel(
       const int b = mx_scale_byte<FMT>(__int_as_float(m));
       const float inv = mx_inv_scale(b);
       uint2 q;
-      q.x = pack4<FMT>(f[u][0] * inv, f[u][1] * inv, f[u][2] * inv, f[u][3] * inv);
-      q.y = pack4<FMT>(f[u][4] * inv, f[u][5] * inv, f[u][6] * inv, f[u][7] * inv);
+      if constexpr (FMT == 2) {   // MXFP4: 8 nibbles, element 2j in the low nibble of byte j
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w |= fp4_code(f[u][i] * inv) << (4 * i);
+        q.x = w;
+        q.y = 0;
+      } else {
+        q.x = pack4<FMT>(f[u][0] * inv, f[u][1] * inv, f[u][2] * inv, f[u][3] * inv);
+        q.y = pack4<FMT>(f[u][4] * inv, f[u][5] * inv, f[u][6] * inv, f[u][7] * inv);
+      }
       if (v < nvec) {
         const bool scale_lane = (lane & 3) == 0;
         for (uint64_t dm = dmask; dm; dm &= dm - 1) {
           const int k = __builtin_ctzll(dm);
           const int64_t d = __builtin_amdgcn_readlane(dest, k);
           // the permuted rows are written once and not read back here: non-temporal
-          __builtin_nontemporal_store(((uint64_t)q.y << 32) | q.x,
-                                      reinterpret_cast<uint64_t*>(out + d * hidden + (int64_t)v * 8));
+          if constexpr (FMT == 2)
+            __builtin_nontemporal_store(q.x, reinterpret_cast<uint32_t*>(out + d * (hidden >> 1) + (int64_t)v * 4));
+          else
+            __builtin_nontemporal_store(((uint64_t)q.y << 32) | q.x,
+                                        reinterpret_cast<uint64_t*>(out + d * hidden + (int64_t)v * 8));
           if (scale_lane) out_scales[d * scale_cols + (v >> 2)] = (uint8_t)b;
         }
         if (tok_out) {
@@ -171,9 +182,12 @@ hipError_t launch_mx_typed(const PermuteParams& p, hipStream_t stream) {
   if (p.quant == 0)
     permute_mx_kernel<InT, 0><<<grid, block, 0, stream>>>(x, p.n, (int)p.hidden, p.topk, p.scat, p.m_limit, out,
                                                           p.out_scales, (int)p.scale_cols, p.tok_out, p.tok_scales);
-  else
+  else if (p.quant == 1)
     permute_mx_kernel<InT, 1><<<grid, block, 0, stream>>>(x, p.n, (int)p.hidden, p.topk, p.scat, p.m_limit, out,
                                                           p.out_scales, (int)p.scale_cols, p.tok_out, p.tok_scales);
+  else   // MXFP4 rows of hidden / 2 bytes (no token-order copy)
+    permute_mx_kernel<InT, 2><<<grid, block, 0, stream>>>(x, p.n, (int)p.hidden, p.topk, p.scat, p.m_limit, out,
+                                                          p.out_scales, (int)p.scale_cols, nullptr, nullptr);
   return hipGetLastError();
 }
 

@@ -456,6 +456,34 @@ hipError_t routing_block_path(const RouteParams& p, int A, int nbits, hipStream_
   return hipGetLastError();
 }
 
+// key_value form of the per-expert counts (MoeInitRoutingV3 README, expertTokensNumType
+// 2): rows (expert id, count) of the active experts with a non-zero count, ascending,
+// then zero rows up to `rows` (one workgroup; thread t takes a contiguous share of the
+// experts, a block scan of the non-zero flags gives each row's place).
+__global__ __launch_bounds__(1024) void route_key_value(const int* __restrict__ offsets, int A, int s, int rows,
+                                                        int64_t* __restrict__ out) {
+  __shared__ int part[1024];
+  const int t = threadIdx.x;
+  const int P = (A + 1023) / 1024;
+  const int a0 = min(A, t * P), a1 = min(A, a0 + P);
+  int nz = 0;
+  for (int a = a0; a < a1; ++a) nz += offsets[a + 1] > offsets[a];
+  const int incl = block_inclusive_scan_1024(nz, part);
+  int row = incl - nz;
+  for (int a = a0; a < a1; ++a) {
+    const int cnt = offsets[a + 1] - offsets[a];
+    if (cnt > 0 && row < rows) {
+      out[2 * (int64_t)row] = s + a;
+      out[2 * (int64_t)row + 1] = cnt;
+      ++row;
+    }
+  }
+  for (int r = part[1023] + t; r < rows; r += 1024) {
+    out[2 * (int64_t)r] = 0;
+    out[2 * (int64_t)r + 1] = 0;
+  }
+}
+
 // Offsets are clamped into [0, rows] and made non-decreasing, and at most max_tiles
 // tiles are written, so caller-given offsets can never send a GEMM out of bounds.
 // Each group is padded to whole 16-row tiles in the tiled token layout: its padded
@@ -535,6 +563,11 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
     route_scatter<int32_t><<<p.nch, 64, lds_a, stream>>>(
         (const int32_t*)p.keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.base, p.offsets, p.scat, p.gath,
         p.gath_fill, p.row_token, p.row_weight, p.topk_w, p.topk_w_bf16);
+  return hipGetLastError();
+}
+
+hipError_t launch_key_value(const int* offsets, int active, int s, int rows, int64_t* out, hipStream_t stream) {
+  route_key_value<<<1, 1024, 0, stream>>>(offsets, active, s, rows, out);
   return hipGetLastError();
 }
 

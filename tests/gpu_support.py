@@ -15,7 +15,7 @@ import routing_permute_mxfp8_amd as rp
 from oracle import moe, mxfp
 
 DEV = "cuda"
-QMODE = {"e4m3": rp.QUANT_E4M3, "e5m2": rp.QUANT_E5M2}
+QMODE = {"e4m3": rp.QUANT_E4M3, "e5m2": rp.QUANT_E5M2, "e2m1": rp.QUANT_MXFP4}
 FP8 = {"e4m3": rp.FP8_E4M3, "e5m2": rp.FP8_E5M2}
 
 

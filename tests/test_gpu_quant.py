@@ -1,5 +1,5 @@
 """MX quantization on the GPU against the oracle, bit for bit: every finite bf16 value,
-both FP8 formats, in two arrangements (random groups; groups of neighbouring
+both FP8 formats and MXFP4 (E2M1), in two arrangements (random groups; groups of neighbouring
 magnitudes, which sweeps every scale byte, saturation, subnormal elements and
 subnormal amax). Plus fp16 / fp32 inputs and a ragged row count."""
 import numpy as np
@@ -25,10 +25,12 @@ def run(bits_2d, fmt):
     torch.cuda.synchronize()
     vals = mxfp.bf16_from_bits(bits_2d)
     oc, os_ = mxfp.quantize(vals, fmt)
+    if fmt == "e2m1":   # MXFP4: two codes a byte, element 2j in the low nibble
+        oc = mxfp.pack_fp4(oc)
     return codes.cpu().numpy(), scales.cpu().numpy(), oc, os_
 
 
-@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2", "e2m1"])
 @pytest.mark.parametrize("arrangement", ["random", "sorted"])
 def test_all_bf16_values(fmt, arrangement):
     say(f"mx_quantize all bf16 fmt={fmt} arrangement={arrangement}")

@@ -50,6 +50,8 @@ def check_init_routing(x_cpu, ids, e_num, active, quant_mode, row_idx_type=1, to
         assert np.array_equal(ex[pos].astype(np.float64), x64)
     else:
         codes, scales = mxfp.quantize(x64, routing.quant_mode_format(quant_mode))
+        if quant_mode == rp.QUANT_MXFP4:
+            codes = mxfp.pack_fp4(codes)
         assert np.array_equal(ex[pos], codes)
         assert np.array_equal(sc[pos], scales)
     return ref
@@ -67,7 +69,7 @@ def test_named_workloads(name):
 
 
 @pytest.mark.parametrize("active", [(0, 8), (3, 3), (0, 1), (7, 8), (2, 6)])
-@pytest.mark.parametrize("row_idx_type,tokens_type", [(1, 1), (0, 0), (0, 1), (1, 0)])
+@pytest.mark.parametrize("row_idx_type,tokens_type", [(1, 1), (0, 0), (0, 1), (1, 0), (1, 2), (0, 2)])
 def test_ranges_and_index_types(active, row_idx_type, tokens_type):
     cfg = moe_inputs.config("tiny", tokens=203, hidden=96, topk=3, seed=77)
     say(f"init_routing active={active} row_idx_type={row_idx_type} tokens_type={tokens_type}")
@@ -77,7 +79,8 @@ def test_ranges_and_index_types(active, row_idx_type, tokens_type):
 
 
 @pytest.mark.parametrize("quant_mode,dtype", [(-1, torch.bfloat16), (-1, torch.float32), (-1, torch.float16),
-                                              (2, torch.float16), (3, torch.float32), (2, torch.bfloat16)])
+                                              (2, torch.float16), (3, torch.float32), (2, torch.bfloat16),
+                                              (9, torch.bfloat16), (9, torch.float16), (9, torch.float32)])
 def test_dtypes_and_modes(quant_mode, dtype):
     cfg = moe_inputs.config("tiny", tokens=77, hidden=160, topk=4, experts=16, seed=5)
     say(f"init_routing quant_mode={quant_mode} dtype={dtype}")
@@ -98,8 +101,9 @@ def test_many_experts_and_chunks():
 @pytest.mark.parametrize("tokens,topk,experts,active,row_idx_type,tokens_type,quant",
                          [(10000, 8, 600, (50, 550), 0, 0, 2),     # 1024-row chunks, 500 buckets, gather index
                           (9000, 4, 64, (0, 64), 1, 1, 3),         # 256-row chunks, every expert active
-                          (1111, 16, 300, (17, 290), 0, 1, 3),     # ragged last chunk, K = 16
-                          (5000, 5, 40, (3, 37), 1, 0, 2)])        # K = 5: tokens straddle chunks
+                          (1111, 16, 300, (17, 290), 0, 2, 3),     # ragged last chunk, K = 16, key_value
+                          (5000, 5, 40, (3, 37), 1, 0, 2),         # K = 5: tokens straddle chunks
+                          (3000, 8, 256, (32, 64), 1, 1, 9)])      # MXFP4 output
 def test_chunked_routing_shapes(tokens, topk, experts, active, row_idx_type, tokens_type, quant):
     # several hundred chunks, hundreds of buckets, ragged last chunk, K = 16 and odd K
     cfg = moe_inputs.config("tiny", tokens=tokens, hidden=256, topk=topk, experts=experts, seed=tokens)
@@ -143,6 +147,9 @@ def test_permute_worked_example_shapes():
     assert tuple(out.shape) == (8, 128) and tuple(sc.shape) == (8, 4)
     check_permute(tokens, idx, 6, -1, 2)
     check_permute(tokens, idx, None, 2, 2)
+    out, srt, sc = rp.token_permute(tokens.to(DEV), torch.from_numpy(idx).to(DEV), quant_mode=9, num_experts=2)
+    assert tuple(out.shape) == (8, 64) and tuple(sc.shape) == (8, 4)   # MXFP4: H / 2 bytes a row
+    check_permute(tokens, idx, 5, 9, 2)
 
 
 @pytest.mark.parametrize("num_out", [None, 0, 1000, 311, -5, -100000])
@@ -163,3 +170,4 @@ def test_permute_one_dimensional_indices():
     tokens = torch.from_numpy(rng.standard_normal((99, 32)).astype(np.float32)).to(torch.bfloat16)
     say("token_permute 1-D indices")
     check_permute(tokens, idx, None, 2, 5)
+    check_permute(tokens, idx, -7, 9, 5)

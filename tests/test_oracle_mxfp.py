@@ -160,3 +160,72 @@ def test_bf16_round():
     assert mxfp.bf16_round(np.array([1.0 + 3 * 2.0 ** -8]))[0] == 1.0 + 2.0 ** -6
     bits = mxfp.bf16_bits(np.array([1.0, -2.0, 0.0]))
     assert list(bits) == [0x3F80, 0xC000, 0x0000]
+
+
+# ---- MXFP4 (FLOAT4_E2M1), quantMode 9 -------------------------------------------
+
+def test_e2m1_table_and_closed_forms():
+    """E2M1: sign bit 0x8, 2 exponent bits (bias 1), 1 mantissa bit, every code finite;
+    the eight magnitudes 0, 0.5 (subnormal), 1, 1.5, 2, 3, 4, 6."""
+    t = mxfp.decode_table("e2m1")
+    assert t.tolist()[:8] == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert np.array_equal(t[8:], -t[:8])
+    assert mxfp.max_finite("e2m1") == 6.0 and mxfp.EMAX["e2m1"] == 2
+    # hand-derived groups: all 1.0 -> X = 2^(0 - 2) -> scale 125, 1.0 / X = 4 -> code 6
+    c, s = mxfp.quantize(np.ones((1, 32)), "e2m1")
+    assert np.all(c == 6) and s.tolist() == [[125, 0]]
+    # amax 7.9 -> X = 2^(2 - 2) = 1: 6 -> 7, 3 -> 5, 1.5 -> 3, 0.75 (tie 0.5 / 1.0) -> 2,
+    # -2.5 (tie 2 / 3) -> 0x8 | 4, 7.9 -> saturated 6 (7), 0.25 (tie 0 / 0.5) -> 0, -0.1 -> -0 (8)
+    v = np.zeros((1, 32))
+    v[0, :8] = [6, 3, 1.5, 0.75, -2.5, 7.9, 0.25, -0.1]
+    c, s = mxfp.quantize(v, "e2m1")
+    assert c[0, :8].tolist() == [7, 5, 3, 2, 12, 7, 0, 8] and s[0, 0] == 127
+    # powers of two: 2^p -> scale p - 2 + 127, element 4 (code 6)
+    for p in (-20, -3, 0, 5, 40):
+        c, s = mxfp.quantize(np.full((1, 32), 2.0 ** p), "e2m1")
+        assert s[0, 0] == p + 125 and np.all(c == 6)
+
+
+def test_e2m1_rounding_is_nearest_by_brute_force():
+    rng = np.random.default_rng(8)
+    t = mxfp.decode_table("e2m1")
+    pos = t[:8]
+    mids = (pos[1:] + pos[:-1]) / 2
+    y = np.concatenate([rng.uniform(-7, 7, 5000), mids, -mids, [6.5, -9.0, 1e9, 0.0, -0.0]])
+    codes = mxfp.round_to_format(y, "e2m1")
+    assert codes.max() < 16
+    got = t[codes]
+    tgt = np.clip(y, -6, 6)
+    d = np.abs(t[None, :] - tgt[:, None])
+    best = d.min(axis=1)
+    assert np.all(np.abs(got - tgt) == best)
+    tie = (d == best[:, None]).sum(axis=1) > 2      # +-0 always tie with each other
+    mag = codes[tie] & 0x7
+    assert np.all(mag % 2 == 0)
+    assert np.array_equal(codes >> 3, np.signbit(y).astype(np.uint8))
+
+
+def test_e2m1_round_trip_bound_and_scale_rule():
+    """Half an E2M1 ulp (relative 2^-2 for normals, 2^-2 absolute below 1) or clamped to
+    6; amax / X in [4, 8) unless the E8M0 byte is clamped."""
+    v = all_bf16_finite()
+    for b in (110, 125, 127, 140):
+        x = 2.0 ** (b - 127)
+        y = v / x
+        back = mxfp.decode_table("e2m1")[mxfp.round_to_format(y, "e2m1")]
+        inside = np.abs(y) <= 6
+        bound = np.maximum(0.25 * np.abs(y), 0.25)
+        assert np.all(np.abs(back - y)[inside] <= bound[inside])
+        assert np.all(back[~inside] == np.sign(y[~inside]) * 6)
+    rng = np.random.default_rng(9)
+    v = rng.standard_normal((300, 64)) * np.exp(rng.uniform(-20, 20, size=(300, 1)))
+    _, s = mxfp.quantize(v, "e2m1")
+    ratio = np.abs(v.reshape(300, 2, 32)).max(axis=2) / mxfp.e8m0_value(s[:, :2])
+    assert np.all((ratio >= 4) & (ratio < 8))
+
+
+def test_fp4_packing():
+    c = np.array([[1, 2, 3, 15, 0, 8]], np.uint8)
+    p = mxfp.pack_fp4(c)
+    assert p.tolist() == [[0x21, 0xF3, 0x80]]
+    assert np.array_equal(mxfp.unpack_fp4(p), c)

@@ -96,3 +96,21 @@ def test_gather_rows_quant_is_row_local():
     allq, alls = mxfp.quantize(x, "e4m3")
     src = r["sorted_row_idx"] // 2
     assert np.array_equal(codes, allq[src]) and np.array_equal(scales, alls[src])
+
+
+def test_key_value_counts():
+    """expertTokensNumType 2: (expert, count) rows of the active experts with rows, ascending,
+    zero rows after them; hand-derived for the moe_token_permute example ids and checked
+    against a brute-force count on random ids."""
+    ids = np.array([[1, 0], [0, 1], [1, 0], [0, 1]])
+    r = routing.init_routing(ids, 4, (0, 4), 1, 2)
+    assert r["expert_tokens"].tolist() == [[0, 4], [1, 4], [0, 0], [0, 0]]
+    r = routing.init_routing(ids, 4, (1, 3), 1, 2)
+    assert r["expert_tokens"].tolist() == [[1, 4], [0, 0], [0, 0], [0, 0]]
+    rng = np.random.default_rng(11)
+    ids = rng.integers(0, 50, (300, 3))
+    kv = routing.init_routing(ids, 50, (7, 41), 1, 2)["expert_tokens"]
+    want = [(e, int((ids == e).sum())) for e in range(7, 41) if (ids == e).sum() > 0]
+    assert kv.shape == (50, 2)
+    assert [tuple(v) for v in kv[:len(want)].tolist()] == want
+    assert np.all(kv[len(want):] == 0)

@@ -41,13 +41,16 @@ def log(msg):
     print(msg, file=sys.stderr, flush=True)
 
 
-def library_weights(torch, rp, moe_inputs, cfg, n_experts, shared):
+def library_weights(torch, rp, moe_inputs, cfg, n_experts, shared, fp4=False):
+    """Expert weights made on the GPU from the bf16 masters and MX-quantized by the library:
+    FP8 of the layer's format, or MXFP4 (codes two a byte) with fp4."""
     t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
     h, i = cfg.hidden, cfg.inter
-    q = rp.QUANT_E4M3 if cfg.fmt == "e4m3" else rp.QUANT_E5M2
-    w1q = torch.empty((n_experts, 2 * i, h), dtype=torch.uint8, device="cuda")
+    q = rp.QUANT_MXFP4 if fp4 else rp.QUANT_E4M3 if cfg.fmt == "e4m3" else rp.QUANT_E5M2
+    cb = 2 if fp4 else 1   # elements per code byte
+    w1q = torch.empty((n_experts, 2 * i, h // cb), dtype=torch.uint8, device="cuda")
     w1s = torch.empty((n_experts, 2 * i, h // 32), dtype=torch.uint8, device="cuda")
-    w2q = torch.empty((n_experts, h, i), dtype=torch.uint8, device="cuda")
+    w2q = torch.empty((n_experts, h, i // cb), dtype=torch.uint8, device="cuda")
     w2s = torch.empty((n_experts, h, i // 32), dtype=torch.uint8, device="cuda")
     for e in range(n_experts):
         c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t1, e, device="cuda"), q)
@@ -57,16 +60,18 @@ def library_weights(torch, rp, moe_inputs, cfg, n_experts, shared):
     return w1q, w1s, w2q, w2s
 
 
-def layer_work(cfg, ids):
+def layer_work(cfg, ids, fp4=False):
     """Algorithmic bytes and flops per launch of the two grouped GEMMs and the combine:
-    GMM1 reads the touched experts' W1 (codes + 1/32 scales) and the quantized rows, and
-    writes the requantized rows; GMM2 reads W2 and those rows and writes fp32 O; the
-    combine reads fp32 O (and the shared experts' O) and writes bf16 Y."""
+    GMM1 reads the touched experts' W1 (codes + 1/32 scales; half a byte a code for MXFP4
+    weights) and the quantized rows, and writes the requantized rows; GMM2 reads W2 and
+    those rows and writes fp32 O; the combine reads fp32 O (and the shared experts' O) and
+    writes bf16 Y."""
     h, i, f = cfg.hidden, cfg.inter, cfg.flat
     touched = int(np.unique(ids).size)
     sc = 1.0 + 1.0 / 32.0
-    gmm1_bytes = touched * 2 * i * h * sc + f * h * sc + f * i * sc
-    gmm2_bytes = touched * h * i * sc + f * i * sc + f * h * 4
+    wsc = (0.5 if fp4 else 1.0) + 1.0 / 32.0
+    gmm1_bytes = touched * 2 * i * h * wsc + f * h * sc + f * i * sc
+    gmm2_bytes = touched * h * i * wsc + f * i * sc + f * h * 4
     combine_bytes = f * h * 4 + cfg.shared * cfg.tokens * h * 4 + cfg.tokens * h * 2
     gmm1_flops = 2.0 * f * h * 2 * i
     gmm2_flops = 2.0 * f * i * h
@@ -201,9 +206,15 @@ def roofline_entry(name, ms, work):
                 avg_launch_ms=round(ms, 5))
 
 
-def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs):
-    """The oracle (CPU, float64) on a bounded token sample: tokens/s of the per-token layer."""
+def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs, fp4=False):
+    """The oracle (CPU, float64) on a bounded token sample: tokens/s of the per-token layer
+    (MXFP4 weights with fp4)."""
     from oracle import moe, mxfp
+    wfmt = "e2m1" if fp4 else cfg.fmt
+
+    def q(m):
+        c, sc = mxfp.quantize(m, wfmt)
+        return (mxfp.pack_fp4(c) if fp4 else c), sc
     rng = np.random.default_rng(123)
     tokens = rng.choice(cfg.tokens, size=sample_tokens, replace=False)
     experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
@@ -211,15 +222,15 @@ def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs):
     for e in experts:  # inputs of the oracle: the sampled experts' weights, quantized by the oracle (untimed)
         m1 = moe_inputs.weight_master(cfg, "w1", e, device="cuda").cpu().double().numpy()
         m2 = moe_inputs.weight_master(cfg, "w2", e, device="cuda").cpu().double().numpy()
-        cache[e] = (*mxfp.quantize(m1, cfg.fmt), *mxfp.quantize(m2, cfg.fmt))
+        cache[e] = (*q(m1), *q(m2))
     shared = []
     for s in range(cfg.shared):
         m1 = moe_inputs.weight_master(cfg, "sw1", s, device="cuda").cpu().double().numpy()
         m2 = moe_inputs.weight_master(cfg, "sw2", s, device="cuda").cpu().double().numpy()
-        shared.append((*mxfp.quantize(m1, cfg.fmt), *mxfp.quantize(m2, cfg.fmt)))
+        shared.append((*q(m1), *q(m2)))
     x = x_cpu.double().numpy()
     t0 = time.perf_counter()
-    moe.per_token(x, ids, w, lambda e: cache[e], cfg.fmt, tokens, shared=shared)
+    moe.per_token(x, ids, w, lambda e: cache[e], cfg.fmt, tokens, shared=shared, wfmt=wfmt)
     dt = time.perf_counter() - t0
     try:
         from threadpoolctl import threadpool_info
@@ -238,23 +249,29 @@ def bench_mega(args, torch, rp, moe_inputs):
     x_cpu = moe_inputs.activations(cfg)
     w = moe_inputs.gate_weights(cfg)
     log(f"[bench] {cfg.name}: generating weights on the GPU")
-    weights = library_weights(torch, rp, moe_inputs, cfg, cfg.experts, shared=False)
-    shared = library_weights(torch, rp, moe_inputs, cfg, cfg.shared, shared=True) if cfg.shared else None
+    fp4 = args.weight_dtype == "mxfp4"
+    weights = library_weights(torch, rp, moe_inputs, cfg, cfg.experts, shared=False, fp4=fp4)
+    shared = library_weights(torch, rp, moe_inputs, cfg, cfg.shared, shared=True, fp4=fp4) if cfg.shared else None
     wf = rp.WEIGHTS_PACKED if args.weights == "packed" else rp.WEIGHTS_ND
     if wf == rp.WEIGHTS_PACKED:   # one-time conversion to the MFMA-native layout, untimed
-        weights = (*rp.pack_weights(weights[0], weights[1]), *rp.pack_weights(weights[2], weights[3]))
+        weights = (*rp.pack_weights(weights[0], weights[1], fp4), *rp.pack_weights(weights[2], weights[3], fp4))
         if shared is not None:
-            shared = (*rp.pack_weights(shared[0], shared[1]), *rp.pack_weights(shared[2], shared[3]))
+            shared = (*rp.pack_weights(shared[0], shared[1], fp4), *rp.pack_weights(shared[2], shared[3], fp4))
+    wd = rp.FP4_E2M1 if fp4 else 0
     x = x_cpu.cuda()
     ids_d = torch.from_numpy(ids).cuda()
     w_d = torch.from_numpy(w).cuda()
     fmt = rp.FP8_E4M3 if cfg.fmt == "e4m3" else rp.FP8_E5M2
-    nbytes = rp.mega_moe_workspace_bytes(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, weight_format=wf)
+    if fp4 and fmt != rp.FP8_E4M3:
+        raise SystemExit("MXFP4 weights (A8W4-FP) take E4M3 activations")
+    nbytes = rp.mega_moe_workspace_bytes(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, weight_format=wf,
+                                         weight_dtype=wd)
     ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
     torch.cuda.synchronize()
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):
-        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, weight_format=wf)
+        rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, weight_format=wf,
+                    weight_dtype=wd)
     torch.cuda.synchronize()
     # Stage events only where the stage times are read (GMM1, GMM2, shared experts +
     # combine): a timed event record costs a few microseconds of GPU time, inside the
@@ -273,7 +290,7 @@ def bench_mega(args, torch, rp, moe_inputs):
     start.record()
     for k in range(args.steps):
         rp.mega_moe(x, ids_d, w_d, *weights, shared=shared, quant_out_dtype=fmt, workspace=ws, stage_events=evs[k],
-                    weight_format=wf)
+                    weight_format=wf, weight_dtype=wd)
     end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
@@ -283,12 +300,12 @@ def bench_mega(args, torch, rp, moe_inputs):
     stage_ms = {"gmm1_swiglu_quant": between(2, 3), "gmm2": between(3, 4), "shared_experts_and_combine": between(4, 6)}
     stage_ms["routing_and_permute"] = between(0, 2)
     step_ms = [evs[k][0].elapsed_time(evs[k][6]) for k in range(args.steps)]
-    work = layer_work(cfg, ids)
+    work = layer_work(cfg, ids, fp4)
     roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], work["gmm1"]),
             "gmm2": roofline_entry("gmm2_kernel", stage_ms["gmm2"], work["gmm2"])}
     dominant = max(roof, key=lambda k: stage_ms[k])
     roofline = dict(roof[dominant])
-    roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name)
+    roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name + ("-mxfp4" if fp4 else ""))
     peaks = measure_peaks(torch, rp)
     ref = peaks["mfma_fp8_tflops"] if roofline["bound"] == "mfma" else peaks["read_gbs"]
     roofline["measured_peak"] = ref
@@ -298,10 +315,15 @@ def bench_mega(args, torch, rp, moe_inputs):
     total_flops = work["gmm1"]["flops"] + work["gmm2"]["flops"] + work["shared"]["flops"]
     out = dict(metric="MoE layer tokens/s", value=round(cfg.tokens / (ms * 1e-3), 1), unit="tokens/s", n_gpus=1,
                steps=args.steps, warmup=args.warmup, ms_per_step=round(ms, 5), higher_is_better=True,
-               scaling="weak", vs_baseline=None, dtype="mxfp8 (fp8 e4m3/e5m2 x e8m0 scales, fp32 accumulate)",
-               data="synthetic (seeded; weights N(0,1/sqrt(fan_in)) quantized to MXFP8 on the GPU)",
+               scaling="weak", vs_baseline=None,
+               dtype=("mxfp8 activations x mxfp4 e2m1 weights (e8m0 scales, fp32 accumulate)" if fp4 else
+                      "mxfp8 (fp8 e4m3/e5m2 x e8m0 scales, fp32 accumulate)"),
+               data=f"synthetic (seeded; weights N(0,1/sqrt(fan_in)) quantized to {'MXFP4' if fp4 else 'MXFP8'} "
+                    "on the GPU)",
                config=dict(workload=f"{cfg.name}: {cfg.tokens} tokens, hidden {cfg.hidden}, inter {cfg.inter}, "
-                                    f"{cfg.experts} experts, topK {cfg.topk}, shared {cfg.shared}, {cfg.fmt}",
+                                    f"{cfg.experts} experts, topK {cfg.topk}, shared {cfg.shared}, {cfg.fmt}"
+                                    + (", A8W4-FP (MXFP4 weights)" if fp4 else ""),
+                           weight_dtype=args.weight_dtype,
                            tokens=cfg.tokens, hidden=cfg.hidden, inter=cfg.inter, experts=cfg.experts,
                            topk=cfg.topk, shared=cfg.shared, fmt=cfg.fmt, touched_experts=work["touched"],
                            weight_layout=args.weights),
@@ -316,7 +338,7 @@ def bench_mega(args, torch, rp, moe_inputs):
     if not args.no_cpu_baseline:
         log("[bench] cpu baseline (oracle)")
         out["cpu_baseline"] = cpu_baseline_mega(cfg, ids, x_cpu, w, args.cpu_sample or (1 if cfg.shared else 2),
-                                                torch, moe_inputs)
+                                                torch, moe_inputs, fp4)
     else:
         out["cpu_baseline"] = None
     return out
@@ -382,6 +404,8 @@ def main():
     ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "routing"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU oracle sample")
+    ap.add_argument("--weight-dtype", default="fp8", choices=["fp8", "mxfp4"],
+                    help="expert weights: MXFP8 (A8W8-FP, the default) or MXFP4 (A8W4-FP)")
     ap.add_argument("--weights", default="packed", choices=["packed", "nd"],
                     help="weight layout: the library's MFMA-native packed layout or the pages' ND layout")
     ap.add_argument("--calibrate-copy", action="store_true",

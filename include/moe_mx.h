@@ -64,8 +64,9 @@ enum { MOE_DTYPE_FP32 = 0, MOE_DTYPE_FP16 = 1, MOE_DTYPE_BF16 = 2,
 /* has magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6 (sign bit 0x8, no inf or NaN), emax 2.       */
 enum { MOE_QUANT_NONE = -1, MOE_QUANT_MXFP8_E5M2 = 2, MOE_QUANT_MXFP8_E4M3 = 3, MOE_QUANT_MXFP4_E2M1 = 9 };
 
-/* dispatchQuantOutDtype values of [MM]: 23 FLOAT8_E5M2, 24 FLOAT8_E4M3FN. */
-enum { MOE_FP8_E5M2 = 23, MOE_FP8_E4M3 = 24 };
+/* dispatchQuantOutDtype values of [MM]: 23 FLOAT8_E5M2, 24 FLOAT8_E4M3FN; weight type */
+/* 296 FLOAT4_E2M1 (MXFP4 weights of the A8W4-FP scenario).                         */
+enum { MOE_FP8_E5M2 = 23, MOE_FP8_E4M3 = 24, MOE_FP4_E2M1 = 296 };
 
 /* rowIdxType of [V3]: 0 gather-type index, 1 scatter-type index. */
 enum { MOE_ROW_IDX_GATHER = 0, MOE_ROW_IDX_SCATTER = 1 };
@@ -118,6 +119,10 @@ moe_status moe_mx_quantize(const void* x, int dtype, int64_t rows, int64_t cols,
 /* K % 128 == 0 are required.                                                        */
 /* ------------------------------------------------------------------------ */
 enum { MOE_WEIGHTS_ND = 0, MOE_WEIGHTS_PACKED = 1 };
+/* MXFP4 weights (A8W4-FP): codes [groups, n, k/2] (two a byte) -> packed codes        */
+/* [groups, n/16, k/128, 64, 16 B] (the same byte count) and packed scales as above.   */
+moe_status moe_mx_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n,
+                                   int64_t k, uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
 int64_t moe_mx_packed_scale_bytes(int64_t groups, int64_t n, int64_t k);
 moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n,
                                int64_t k, uint8_t* packed_codes, uint8_t* packed_scales, void* stream);
@@ -280,8 +285,18 @@ typedef struct {
   void** stage_events;            /* nullable, see above */
   int num_activation_params;      /* 0..3, see the activations above */
   float activation_params[3];
+  int weight_dtype;               /* routed w1/w2: 0 or quant_out_dtype = FP8 (A8W8-FP),      */
+                                  /* MOE_FP4_E2M1 = MXFP4 (A8W4-FP; needs FLOAT8_E4M3FN x)  */
+  int shared_weight_dtype;        /* shared experts: 0 = as weight_dtype, or as above        */
 } moe_mega_args;
 
+/* A8W4-FP ([MM] "A8W4-FP quantization scenario"): with weight_dtype MOE_FP4_E2M1 the  */
+/* routed w1 / w2 hold MXFP4 codes two a byte (element 2j in the low nibble): w1      */
+/* uint8 [num_experts, 2*inter, hidden/2], w2 [num_experts, hidden, A/2] (A = inter,   */
+/* or 2*inter for gelu), scales as for FP8 (E8M0, one per 32 along K); in the packed  */
+/* weight format they come from moe_mx_pack_weights_fp4. X^ and A^ stay MXFP8 E4M3,   */
+/* so both GEMMs multiply FP8 activations by FP4 weights on the matrix cores.          */
+/* The shared experts may use the other weight type (shared_weight_dtype).             */
 moe_status mega_moe_workspace_size(const moe_mega_args* args /* host */, size_t* bytes /* host out */);
 moe_status mega_moe(const moe_mega_args* args /* host */, void* workspace, size_t workspace_bytes,
                     void* stream);

@@ -105,21 +105,26 @@ def activate(h1, kind="swiglu", params=()):
     raise ValueError(kind)
 
 
-def gmm(aq, sa, wq, ws, fmt):
-    """DQ_MX(A) . DQ_MX(W)^T for W stored (out, in): float64 [m, out]."""
+def gmm(aq, sa, wq, ws, fmt, wfmt=None):
+    """DQ_MX(A) . DQ_MX(W)^T for W stored (out, in): float64 [m, out]. wfmt: the weights'
+    element format when it differs from the activations' (A8W4-FP: "e2m1", codes two a
+    byte as stored, element 2j in the low nibble)."""
+    wfmt = fmt if wfmt is None else wfmt
     ad = mxfp.dequantize(aq, sa, fmt)
-    wd = mxfp.dequantize(wq, ws, fmt)
+    wcodes = mxfp.unpack_fp4(wq) if wfmt == "e2m1" else wq
+    wd = mxfp.dequantize(wcodes, ws, wfmt)
     return ad @ wd.T
 
 
-def expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt, act=("swiglu", ())):
+def expert_ffn(xq, sx, w1q, w1s, w2q, w2s, fmt, act=("swiglu", ()), wfmt=None):
     """Stages 2-3 for the rows of one expert. xq/sx: [m, H] codes/scales;
-    act = (activation kind, parameter list)."""
-    h1 = gmm(xq, sx, w1q, w1s, fmt)
+    act = (activation kind, parameter list); wfmt = the weights' format (A8W4-FP: "e2m1",
+    MegaMoE "A8W4-FP quantization scenario": X^ and A^ stay MXFP8, W1 and W2 MXFP4)."""
+    h1 = gmm(xq, sx, w1q, w1s, fmt, wfmt)
     a = mxfp.fp32_round(activate(h1, *act))
-    assert a.shape[1] == w2q.shape[1], "weight2's input width must equal A's"
+    assert a.shape[1] == w2q.shape[1] * (2 if wfmt == "e2m1" else 1), "weight2's input width must equal A's"
     aq, sa = mxfp.quantize(a, fmt)
-    o = gmm(aq, sa, w2q, w2s, fmt)
+    o = gmm(aq, sa, w2q, w2s, fmt, wfmt)
     return dict(h1=h1, a=a, aq=aq, sa=sa, o=o)
 
 
@@ -145,7 +150,8 @@ def combine(o_rows, expanded_row_idx, topk_weights, shared_o=()):
     return mxfp.bf16_round(y)
 
 
-def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), act=("swiglu", ())) -> dict:
+def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), act=("swiglu", ()), wfmt=None,
+             shared_wfmt=None) -> dict:
     """The whole layer on all tokens, in the permuted (expert-contiguous) order.
 
     x: [N, H] values (bf16 as float64); topk_ids int [N, K]; topk_weights [N, K];
@@ -163,10 +169,10 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
     for e in range(num_experts):
         lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
         if hi > lo:
-            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt, act)
+            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt, act, wfmt)
     hidden = x.shape[1]
     two_i = get(0)[0].shape[0]
-    aw = get(0)[2].shape[1]            # width of A: I (gated) or 2I (gelu)
+    aw = get(0)[2].shape[1] * (2 if wfmt == "e2m1" else 1)   # width of A: I (gated) or 2I (gelu)
     out = dict(routing=r, xq=xq, sx=sx,
                h1=np.zeros((flat, two_i)), a=np.zeros((flat, aw)),
                aq=np.zeros((flat, aw), np.uint8),
@@ -181,7 +187,8 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
         xq_tok, sx_tok = mxfp.quantize(x, fmt)
         out["xq_tok"], out["sx_tok"] = xq_tok, sx_tok
         for sw in shared:
-            shared_o.append(expert_ffn(xq_tok, sx_tok, *sw, fmt, act)["o"])
+            shared_o.append(expert_ffn(xq_tok, sx_tok, *sw, fmt, act,
+                                       wfmt if shared_wfmt is None else shared_wfmt)["o"])
     out["shared_o"] = shared_o
     full_scatter = routing.inverse(r["sorted_row_idx"])
     out["y"] = combine(out["o"], full_scatter, topk_weights, shared_o)
@@ -189,7 +196,8 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
     return out
 
 
-def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("swiglu", ())) -> dict:
+def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("swiglu", ()), wfmt=None,
+              shared_wfmt=None) -> dict:
     """The layer for selected tokens, one (token, k) at a time, with no permutation
     (the "brute force" form of stage 1-4: each expert receives a copy of x_t).
 
@@ -216,12 +224,12 @@ def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("
         acc = np.zeros((1, x.shape[1]))
         h1_t, o_t = [], []
         for j in range(k):
-            r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt, act)
+            r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt, act, wfmt)
             acc = acc + w[t, j] * r["o"]
             h1_t.append(r["h1"][0])
             o_t.append(r["o"][0])
         for sw in shared:
-            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt, act)["o"]
+            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt, act, wfmt if shared_wfmt is None else shared_wfmt)["o"]
         ys.append(mxfp.bf16_round(acc)[0])
         h1s.append(h1_t)
         os_.append(o_t)

@@ -58,11 +58,13 @@ class MegaArgs(ctypes.Structure):
         ("sorted_row_idx", ctypes.c_void_p),
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
         ("num_activation_params", ctypes.c_int), ("activation_params", ctypes.c_float * 3),
+        ("weight_dtype", ctypes.c_int), ("shared_weight_dtype", ctypes.c_int),
     ]
 
 MEGA_STAGE_EVENTS = 7
 # activation kinds of mega_moe (MegaMoE "Activation function formulas")
 ACT_SWIGLU, ACT_SWIGLUSTEP, ACT_SWIGLUOAI, ACT_SITUGLU, ACT_GELU = 0, 1, 2, 3, 4
+FP4_E2M1 = 296   # MXFP4 weights (A8W4-FP)
 MEGA_STAGES = ["routing", "permute_quant", "gmm1_swiglu_quant", "gmm2", "shared_experts", "combine"]
 
 
@@ -77,6 +79,7 @@ _SIGS = {
     "moe_mx_quantize": ([_VP, _INT, _I64, _I64, _INT, _VP, _VP, _VP], _INT),
     "moe_mx_packed_scale_bytes": ([_I64, _I64, _I64], _I64),
     "moe_mx_pack_weights": ([_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP], _INT),
+    "moe_mx_pack_weights_fp4": ([_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP], _INT),
     "moe_init_routing_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_init_routing": ([_VP, _INT, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
                           _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
@@ -166,16 +169,19 @@ def mx_quantize(x: torch.Tensor, quant_mode: int = QUANT_E4M3):
     return codes, scales
 
 
-def pack_weights(codes, scales):
+def pack_weights(codes, scales, fp4: bool = False):
     """MX weights [G, N, K] codes + [G, N, K/32] scales (the pages' layout) -> the library's
-    MFMA-native packed layout: (codes uint8 [G, N, K] in packed order, scales uint8 1-D)."""
+    MFMA-native packed layout: (codes uint8 [G, N, K] in packed order, scales uint8 1-D).
+    fp4: MXFP4 codes [G, N, K/2] (two a byte; K = 2 * the last dimension)."""
     lib = load()
     codes, scales = _u8(codes), _u8(scales)
     _need_gpu(codes, scales)
-    g, n, k = codes.shape
+    g, n, kb = codes.shape
+    k = 2 * kb if fp4 else kb
     pc = torch.empty_like(codes)
     ps = torch.empty((int(lib.moe_mx_packed_scale_bytes(g, n, k)),), dtype=torch.uint8, device=codes.device)
-    _check(lib.moe_mx_pack_weights(_ptr(codes), _ptr(scales), g, n, k, _ptr(pc), _ptr(ps), _stream(codes.device)))
+    fn = lib.moe_mx_pack_weights_fp4 if fp4 else lib.moe_mx_pack_weights
+    _check(fn(_ptr(codes), _ptr(scales), g, n, k, _ptr(pc), _ptr(ps), _stream(codes.device)))
     return pc, ps
 
 
@@ -238,7 +244,8 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
 
 
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
-                 debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=()):
+                 debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=(), weight_dtype=0,
+                 shared_weight_dtype=0):
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -257,6 +264,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
     if len(activation_params) > 3:
         raise ValueError("activation_params holds at most 3 values")
     a.num_activation_params = len(activation_params)
+    a.weight_dtype, a.shared_weight_dtype = weight_dtype, shared_weight_dtype
     for j, v in enumerate(activation_params):
         a.activation_params[j] = float(v)
     a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
@@ -267,7 +275,8 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
 
 def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
              quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None,
-             weight_format: int = WEIGHTS_ND, activation: int = ACT_SWIGLU, activation_params=()):
+             weight_format: int = WEIGHTS_ND, activation: int = ACT_SWIGLU, activation_params=(),
+             weight_dtype: int = 0, shared_weight_dtype: int = 0):
     """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
     debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
 
@@ -279,7 +288,9 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     None entries, recorded by the library on the stream at the boundaries of MEGA_STAGES
     (a None entry is skipped; each record costs a few microseconds of GPU time).
     activation / activation_params: ACT_* and its parameter list as in the C header (gelu
-    makes A, and w2's input width, 2 * inter)."""
+    makes A, and w2's input width, 2 * inter).
+    weight_dtype / shared_weight_dtype: 0 (FP8 as the activations) or FP4_E2M1 (MXFP4 codes
+    two a byte, e.g. from mx_quantize(..., QUANT_MXFP4); pack_weights(..., fp4=True))."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
     n, h = x.shape
@@ -301,7 +312,7 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
                    o=torch.empty((f, h), dtype=torch.float32, device=dev),
                    sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg,
-                     weight_format, activation, activation_params)
+                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} entries (events or None)")
@@ -322,10 +333,11 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
 
 def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
                              quant_out_dtype: int = FP8_E4M3, weight_format: int = WEIGHTS_ND,
-                             activation: int = ACT_SWIGLU, activation_params=()) -> int:
+                             activation: int = ACT_SWIGLU, activation_params=(), weight_dtype: int = 0,
+                             shared_weight_dtype: int = 0) -> int:
     lib = load()
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None,
-                     weight_format, activation, activation_params)
+                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype)
     nbytes = ctypes.c_size_t()
     _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     return nbytes.value

@@ -258,6 +258,15 @@ moe_status check_mega(const moe_mega_args* a) {
     return fail(MOE_ERR_DTYPE, "mega_moe: quant_out_dtype %d must be 23 (FLOAT8_E5M2) or 24 (FLOAT8_E4M3FN)",
                 a->quant_out_dtype);
   if (moe_status st = act_params(a, nullptr)) return st;
+  for (int wd : {a->weight_dtype, a->shared_weight_dtype}) {
+    if (wd != 0 && wd != MOE_FP8_E5M2 && wd != MOE_FP8_E4M3 && wd != MOE_FP4_E2M1)
+      return fail(MOE_ERR_DTYPE, "mega_moe: weight dtype %d not 0, 23, 24 or 296", wd);
+    if ((wd == MOE_FP8_E5M2 || wd == MOE_FP8_E4M3) && wd != a->quant_out_dtype)
+      return fail(MOE_ERR_UNSUPPORTED, "mega_moe: FP8 weights must have the activations' FP8 type %d",
+                  a->quant_out_dtype);
+    if (wd == MOE_FP4_E2M1 && a->quant_out_dtype != MOE_FP8_E4M3)
+      return fail(MOE_ERR_UNSUPPORTED, "mega_moe: MXFP4 weights (A8W4-FP) take FLOAT8_E4M3FN activations");
+  }
   if (a->topk_weights_dtype != MOE_DTYPE_FP32 && a->topk_weights_dtype != MOE_DTYPE_BF16)
     return fail(MOE_ERR_DTYPE, "mega_moe: topk_weights_dtype must be FP32 or BF16");
   if (a->weight_format != MOE_WEIGHTS_ND && a->weight_format != MOE_WEIGHTS_PACKED)
@@ -370,6 +379,19 @@ moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
     return fail(MOE_ERR_INVALID_ARG, "moe_mx_pack_weights: NULL buffer");
   hipError_t e = moe::launch_pack_weights(codes, scales, groups, n, k, packed_codes, packed_scales, (hipStream_t)stream);
   if (e != hipSuccess) return hip_fail(e, "moe_mx_pack_weights launch");
+  return ok();
+}
+
+moe_status moe_mx_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                                   uint8_t* packed_codes, uint8_t* packed_scales, void* stream) {
+  if (groups < 0 || n <= 0 || k <= 0 || n % 16 != 0 || k % 128 != 0)
+    return fail(MOE_ERR_SHAPE, "moe_mx_pack_weights_fp4: groups >= 0, n %% 16 == 0 and k %% 128 == 0 required");
+  if (groups == 0) return ok();
+  if (!codes || !scales || !packed_codes || !packed_scales)
+    return fail(MOE_ERR_INVALID_ARG, "moe_mx_pack_weights_fp4: NULL buffer");
+  hipError_t e =
+      moe::launch_pack_weights_fp4(codes, scales, groups, n, k, packed_codes, packed_scales, (hipStream_t)stream);
+  if (e != hipSuccess) return hip_fail(e, "moe_mx_pack_weights_fp4 launch");
   return ok();
 }
 
@@ -577,8 +599,10 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if ((e = mark(2)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 2: GMM1 + SwiGLU + MX requantization
   const int packed = a->weight_format == MOE_WEIGHTS_PACKED;
+  const int wfp4 = a->weight_dtype == MOE_FP4_E2M1;
+  const int swfp4 = (a->shared_weight_dtype ? a->shared_weight_dtype : a->weight_dtype) == MOE_FP4_E2M1;
   moe::Gmm1Params g1{w.xq, w.sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed, act};
+                     (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed, act, wfp4};
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
   if (a->aq || a->sa) {
@@ -589,21 +613,23 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   // stage 3: GMM2, O rows in fp32
   float* o = a->o ? a->o : w.o;
   moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
-                     (int)h, (int)aw, fmt, w.tt, o, packed};
+                     (int)h, (int)aw, fmt, w.tt, o, packed, wfp4};
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // shared experts: the same FFN over all tokens in token order
   for (int64_t s = 0; s < a->num_shared; ++s) {
-    moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + s * 2 * inter * h,
+    // bytes of one shared expert's codes: halved for MXFP4 (two codes a byte)
+    moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + (s * 2 * inter * h >> swfp4),
                        a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,
                        w.sh_count, w.sh_max_tiles, (int)h, (int)inter, fmt, w.sh_tt, w.aq_sh, w.sa_sh, nullptr,
-                       packed, act};
+                       packed, act, swfp4};
     e = moe::launch_gmm1(s1, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
-    moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + s * h * aw,
+    moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + (s * h * aw >> swfp4),
                        a->shared_w2_scales + s * group_scale_bytes(h, aw, a->weight_format), w.sh_tiles,
-                       w.sh_count, w.sh_max_tiles, (int)h, (int)aw, fmt, w.sh_tt, w.o_sh + s * n * h, packed};
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)aw, fmt, w.sh_tt, w.o_sh + s * n * h, packed,
+                       swfp4};
     e = moe::launch_gmm2(s2, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
   }

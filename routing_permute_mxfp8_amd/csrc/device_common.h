@@ -115,6 +115,17 @@ __device__ __forceinline__ v4f mfma_mx16(const v8i& a, const v8i& b, v4f c, int 
   return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FMT, FMT, 0, sa, 0, sb);
 }
 
+// Operand format codes of the block-scaled MFMA: 0 FP8 E4M3FN, 1 FP8 E5M2, 4 FP4 E2M1.
+// An FP4 operand (measured on gfx950) uses register bytes 0..15 only: lane l holds
+// K [32g, 32g + 32) of row r, element 2j in the low nibble of byte j, i.e. the 16
+// bytes at byte offset 16g of the row's packed K step; the scale byte is as for FP8.
+constexpr int kFmtFp4 = 4;
+
+template <int FA, int FB>
+__device__ __forceinline__ v4f mfma_mx16_ab(const v8i& a, const v8i& b, v4f c, int sa, int sb) {
+  return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, FA, FB, 0, sa, 0, sb);
+}
+
 __device__ __forceinline__ v8i join_operand(u32x4 lo, u32x4 hi) {
   v8i r;
   r[0] = (int)lo[0]; r[1] = (int)lo[1]; r[2] = (int)lo[2]; r[3] = (int)lo[3];

@@ -49,6 +49,15 @@ constexpr int kTileBytes = 2048;   // one 16-row x 128-K MX operand tile
 constexpr int kTileScaleBytes = 256;
 
 // ---- weight operand loads --------------------------------------------------------
+// WF: the weights' MFMA operand format, the tokens' FP8 format or kFmtFp4 (MXFP4 E2M1,
+// two codes a byte: a 16-channel x 128-K tile is 1 KB, one 16-byte load per lane).
+template <int WF>
+struct WeightFmt {
+  static constexpr bool kFp4 = WF == kFmtFp4;
+  static constexpr int kStepBytes = kFp4 ? 1024 : 2048;   // one 16-channel x 128-K tile
+  static constexpr int kParts = kFp4 ? 2 : 3;             // loads per tile and K step (data..., scale)
+};
+
 // ND: row pointer of channel (tile*16 + r) and its scale row.
 // PACKED: tile base (group, 16-channel tile, K step 0) and its scale base + lane*4.
 template <bool PACKED>
@@ -57,7 +66,7 @@ struct WPtr {
   const uint8_t* s;
 };
 
-template <bool PACKED>
+template <bool PACKED, int WF>
 __device__ __forceinline__ WPtr<PACKED> weight_tile(const uint8_t* w, const uint8_t* ws, int64_t tile_index, int K,
                                                     int lane) {
   // tile_index = group * (N / 16) + channel_tile
@@ -65,11 +74,11 @@ __device__ __forceinline__ WPtr<PACKED> weight_tile(const uint8_t* w, const uint
   const int ks = K >> 7;
   if constexpr (PACKED) {
     const int kq = (ks + 3) >> 2;
-    p.d = w + tile_index * ks * kTileBytes;
+    p.d = w + tile_index * ks * WeightFmt<WF>::kStepBytes;
     p.s = ws + tile_index * kq * kTileScaleBytes + lane * 4;
   } else {
     const int64_t row = tile_index * 16 + (lane & 15);
-    p.d = w + row * K;
+    p.d = w + row * (WeightFmt<WF>::kFp4 ? K >> 1 : K);
     p.s = ws + row * (K >> 5);
   }
   return p;
@@ -164,23 +173,24 @@ __device__ __forceinline__ void block_barrier() {
 // with WPF = 1 the token tiles issued after step s's weights may: one fixed vmcnt.
 template <int NT> struct WeightPrefetch { static constexpr int value = NT >= 16 ? 1 : 2; };
 
-template <int NT>
+template <int NT, int WF>
 struct Batch {
-  static constexpr int kWeights = 12;
+  static constexpr int kWeights = 4 * WeightFmt<WF>::kParts;
   static constexpr int kTokens = 3 * StageLayout<NT>::kPerWave;
   static constexpr int kLoads = kWeights + kTokens;
   static constexpr int kInFlight = WeightPrefetch<NT>::value == 2 ? kLoads : kTokens;
 };
 
-template <int NT, bool PACKED, int K_SLOT>
+template <int NT, bool PACKED, int WF, int K_SLOT>
 __device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], const WPtr<PACKED> (&wp)[4], int wstep,
                                           const uint8_t* tok, const uint8_t* toks, int ks, int row0, int ntt,
                                           int tstep, uint8_t* slot, int wave, int lane) {
-  constexpr int kW = Batch<NT>::kWeights;
+  constexpr int kW = Batch<NT, WF>::kWeights;
   if constexpr (K_SLOT < kW) {
-    constexpr int q = K_SLOT / 3, part = K_SLOT % 3;
+    constexpr int kParts = WeightFmt<WF>::kParts;
+    constexpr int q = K_SLOT / kParts, part = K_SLOT % kParts;
     const int g = lane >> 4;
-    if constexpr (part == 2) {
+    if constexpr (part == kParts - 1) {
       if constexpr (PACKED)
         sload[q] = (int)*reinterpret_cast<const uint32_t*>(wp[q].s + (wstep >> 2) * kTileScaleBytes);
       else
@@ -188,7 +198,9 @@ __device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], cons
     } else {
       const uint8_t* src;
       if constexpr (PACKED)
-        src = wp[q].d + (int64_t)wstep * kTileBytes + part * 1024 + lane * 16;
+        src = wp[q].d + (int64_t)wstep * WeightFmt<WF>::kStepBytes + part * 1024 + lane * 16;
+      else if constexpr (WeightFmt<WF>::kFp4)
+        src = wp[q].d + 64 * wstep + 16 * g;
       else
         src = wp[q].d + 128 * wstep + part * 64 + 16 * g;
       const u32x4 v = *reinterpret_cast<const u32x4*>(src);
@@ -208,12 +220,12 @@ __device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], cons
   }
 }
 
-template <int NT, bool PACKED, int K0, int... I>
+template <int NT, bool PACKED, int WF, int K0, int... I>
 __device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i (&aload)[4], int (&sload)[4],
                                            const WPtr<PACKED> (&wp)[4], int wstep, const uint8_t* tok,
                                            const uint8_t* toks, int ks, int row0, int ntt, int tstep, uint8_t* slot,
                                            int wave, int lane) {
-  (load_slot<NT, PACKED, K0 + I>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane), ...);
+  (load_slot<NT, PACKED, WF, K0 + I>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane), ...);
 }
 
 // One K step s, with its weights in (acur, scur) and its token tiles in ring slot
@@ -235,20 +247,20 @@ __device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i
 // fences keep them there); loads that do not fit, and all loads of small chunks, go
 // first.
 // WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
 __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4],
                                        const v8i (&acur)[4], const int (&scur)[4], v8i (&aload)[4],
                                        int (&sload)[4], const uint8_t* tok, const uint8_t* toks, int row0, int ntt,
                                        uint8_t* lds, int wave, int lane) {
-  constexpr int kLoads = Batch<NT>::kLoads;
+  constexpr int kLoads = Batch<NT, WF>::kLoads;
   constexpr int kTop = NT < 4 ? kLoads : (kLoads > 4 * NT ? kLoads - 4 * NT : 0);
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
-  wait_vmcnt<Batch<NT>::kInFlight>();
+  wait_vmcnt<Batch<NT, WF>::kInFlight>();
   block_barrier<NT>();
   const int wstep = min(s + WeightPrefetch<NT>::value, ks - 1), tstep = min(s + 2, ks - 1);
   uint8_t* slot = lds + (cur == 0 ? 2 : cur - 1) * kBuf;   // (cur + 2) % 3
   const uint8_t* buf = lds + cur * kBuf;
-  load_slots<NT, PACKED, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
+  load_slots<NT, PACKED, WF, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
                             ntt, tstep, slot, wave, lane);
   int sw[4];
 #pragma unroll
@@ -264,12 +276,12 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT]
         ([&] {
           constexpr int q = Q;
           if constexpr (WEIGHTS_A)
-            acc[q][t] = mfma_mx16<FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
+            acc[q][t] = mfma_mx16_ab<WF, FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
           else
-            acc[q][t] = mfma_mx16<FMT>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
+            acc[q][t] = mfma_mx16_ab<FMT, WF>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
           constexpr int k = kTop + 4 * t + q;
           if constexpr (k < kLoads) {
-            load_slot<NT, PACKED, k>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane);
+            load_slot<NT, PACKED, WF, k>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane);
             __builtin_amdgcn_sched_barrier(0);
           }
         }(), ...);
@@ -287,43 +299,43 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT]
 // register allocator permutes the accumulators across the loop body instead.) At the
 // end every load has landed and every wave is past its last LDS read, so the next
 // chunk may reuse the ring.
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
 __device__ __forceinline__ void k_loop_pf2(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                        int lane) {
-  constexpr int kL = Batch<NT>::kLoads;
+  constexpr int kL = Batch<NT, WF>::kLoads;
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   const int ks = K >> 7, r = ks % 3, s1 = min(1, ks - 1);
   v8i a0[4], a1[4], a2[4];
   int c0[4], c1[4], c2[4];
   auto seq = std::make_integer_sequence<int, kL>{};
   if (r == 0) {
-    load_slots<NT, PACKED, 0>(seq, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, 0>(seq, a1, c1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a1, c1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   } else if (r == 1) {
-    load_slots<NT, PACKED, 0>(seq, a2, c2, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, 0>(seq, a0, c0, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a2, c2, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a0, c0, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   } else {
-    load_slots<NT, PACKED, 0>(seq, a1, c1, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, 0>(seq, a2, c2, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a1, c1, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, 0>(seq, a2, c2, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   }
   int s = 0, cur = 0;
   if (r == 1) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     s = 1;
     cur = 1;
   } else if (r == 2) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     s = 2;
     cur = 2;
   }
   for (; s < ks; s += 3) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(s, ks, cur, acc, wp, a0, c0, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s, ks, cur, acc, wp, a0, c0, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   wait_vmcnt<0>();
@@ -334,22 +346,22 @@ __device__ __forceinline__ void k_loop_pf2(v4f (&acc)[4][NT], const WPtr<PACKED>
 // 1 first; if ks is odd, step 0 alone (its weight buffers then swap by copies); then
 // the steps two at a time (the two weight buffers alternate, roles fixed in the
 // unrolled body). Then as above.
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
 __device__ __forceinline__ void k_loop_pf1(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
                                            const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                            int lane) {
-  constexpr int kW = Batch<NT>::kWeights, kT = Batch<NT>::kTokens;
+  constexpr int kW = Batch<NT, WF>::kWeights, kT = Batch<NT, WF>::kTokens;
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   const int ks = K >> 7;
   v8i a0[4], a1[4];
   int c0[4], c1[4];
-  load_slots<NT, PACKED, 0>(std::make_integer_sequence<int, kW + kT>{}, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0,
+  load_slots<NT, PACKED, WF, 0>(std::make_integer_sequence<int, kW + kT>{}, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0,
                             lds, wave, lane);
-  load_slots<NT, PACKED, kW>(std::make_integer_sequence<int, kT>{}, a1, c1, wp, 0, tok, toks, ks, row0, ntt,
+  load_slots<NT, PACKED, WF, kW>(std::make_integer_sequence<int, kT>{}, a1, c1, wp, 0, tok, toks, ks, row0, ntt,
                              min(1, ks - 1), lds + kBuf, wave, lane);
   int s = 0, cur = 0;
   if (ks & 1) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(0, ks, 0, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       a0[q] = a1[q];
@@ -359,23 +371,23 @@ __device__ __forceinline__ void k_loop_pf1(v4f (&acc)[4][NT], const WPtr<PACKED>
     cur = 1;
   }
   for (; s < ks; s += 2) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(s, ks, cur, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s, ks, cur, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   wait_vmcnt<0>();
   __syncthreads();
 }
 
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A>
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
 __device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                        int lane) {
   if constexpr (WeightPrefetch<NT>::value == 2)
-    k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+    k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A, WF>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
   else
-    k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+    k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A, WF>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
 }
 
 // Occupancy targets: small token chunks (decode) want several waves per SIMD to keep
@@ -447,7 +459,7 @@ __device__ __forceinline__ void store_group(const float (&act)[2][4], uint8_t* _
 }
 
 // ---- GMM1 + activation + MX requantization --------------------------------------
-template <int FMT, int NT, bool PACKED, int EPI>
+template <int FMT, int NT, bool PACKED, int EPI, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
 void gmm1_swiglu_kernel(
     const uint8_t* __restrict__ xq, const uint8_t* __restrict__ sx, const uint8_t* __restrict__ w,
@@ -471,14 +483,14 @@ void gmm1_swiglu_kernel(
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int ct = (q < 2 ? n0 : inter + n0 - 32) / 16 + q;   // q = 0,1 gate; 2,3 up
-      wp[q] = weight_tile<PACKED>(w, ws, (int64_t)e * n16 + ct, hidden, lane);
+      wp[q] = weight_tile<PACKED, WF>(w, ws, (int64_t)e * n16 + ct, hidden, lane);
     }
     v4f acc[4][NT];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, true>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, true, WF>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
 
     // A^ goes out in the tiled layout with K = inter (2 inter for gelu), where this
     // block's 128 gate channels are exactly K step cb: the wave's 32 channels are half
@@ -532,7 +544,7 @@ void gmm1_swiglu_kernel(
 // them back per token (combine.hip). Combining here with fp32 atomics would send every
 // add to memory: a token's K rows are computed on different XCDs, whose L2s are not
 // coherent, so device-scope atomics are not resolved in L2.
-template <int FMT, int NT, bool PACKED>
+template <int FMT, int NT, bool PACKED, int WF>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
 void gmm2_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
@@ -558,13 +570,13 @@ void gmm2_kernel(
     const int c0w = wave_on ? c0 : 0;
     WPtr<PACKED> wp[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wp[q] = weight_tile<PACKED>(w, ws, (int64_t)e * n16 + (c0w >> 4) + q, inter, lane);
+    for (int q = 0; q < 4; ++q) wp[q] = weight_tile<PACKED, WF>(w, ws, (int64_t)e * n16 + (c0w >> 4) + q, inter, lane);
     v4f acc[4][NT];
 #pragma unroll
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, false>(acc, wp, aq, sa, inter, row0, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, false, WF>(acc, wp, aq, sa, inter, row0, ntt, lds, wave, lane);
 
     // acc[q][t][i] = O[token row 16t + 4g + i][channel c0 + 16q + r]
 #pragma unroll
@@ -598,6 +610,22 @@ __global__ void pack_codes_kernel(const uint8_t* __restrict__ codes, uint8_t* __
     const int64_t tile = blk / ks;              // g * N/16 + n16
     const int64_t row = tile * 16 + (l & 15);   // flat row over [G * N]
     const u32x4 v = *reinterpret_cast<const u32x4*>(codes + row * K + 128 * s + 64 * h + 16 * (l >> 4));
+    reinterpret_cast<u32x4*>(packed)[p] = v;
+  }
+}
+
+// MXFP4 codes [G, N, K/2] (two a byte) -> packed [G][N/16][K/128][64][16 B]: tile (g, n16, s),
+// lane l holds row n16*16 + l%16, bytes [64 s + 16 (l/16), +16) of the row (K [128 s + 32 (l/16), +32)).
+__global__ void pack_codes_fp4_kernel(const uint8_t* __restrict__ codes, uint8_t* __restrict__ packed,
+                                      int64_t pieces, int K) {
+  const int ks = K >> 7;
+  for (int64_t p = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; p < pieces; p += (int64_t)gridDim.x * blockDim.x) {
+    const int l = (int)(p & 63);
+    const int64_t blk = p >> 6;                 // (g * N/16 + n16) * ks + s
+    const int s = (int)(blk % ks);
+    const int64_t tile = blk / ks;
+    const int64_t row = tile * 16 + (l & 15);
+    const u32x4 v = *reinterpret_cast<const u32x4*>(codes + row * (K >> 1) + 64 * s + 16 * (l >> 4));
     reinterpret_cast<u32x4*>(packed)[p] = v;
   }
 }
@@ -661,9 +689,9 @@ hipError_t persistent_shape(K kernel, size_t lds, LaunchShape* out) {
   return hipSuccess;
 }
 
-template <int FMT, int NT, bool PACKED, int EPI>
+template <int FMT, int NT, bool PACKED, int EPI, int WF>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
-  auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI>;
+  auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI, WF>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
@@ -672,9 +700,9 @@ hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int FMT, int NT, bool PACKED>
+template <int FMT, int NT, bool PACKED, int WF>
 hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
-  auto kern = gmm2_kernel<FMT, NT, PACKED>;
+  auto kern = gmm2_kernel<FMT, NT, PACKED, WF>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
@@ -682,36 +710,36 @@ hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int FMT, bool PACKED, int EPI>
+template <int FMT, bool PACKED, int EPI, int WF>
 hipError_t gmm1_epi(const Gmm1Params& p, hipStream_t st) {
   switch (p.tt) {
-    case 1: return gmm1_go<FMT, 1, PACKED, EPI>(p, st);
-    case 2: return gmm1_go<FMT, 2, PACKED, EPI>(p, st);
-    case 4: return gmm1_go<FMT, 4, PACKED, EPI>(p, st);
-    case 8: return gmm1_go<FMT, 8, PACKED, EPI>(p, st);
-    default: return gmm1_go<FMT, 16, PACKED, EPI>(p, st);
+    case 1: return gmm1_go<FMT, 1, PACKED, EPI, WF>(p, st);
+    case 2: return gmm1_go<FMT, 2, PACKED, EPI, WF>(p, st);
+    case 4: return gmm1_go<FMT, 4, PACKED, EPI, WF>(p, st);
+    case 8: return gmm1_go<FMT, 8, PACKED, EPI, WF>(p, st);
+    default: return gmm1_go<FMT, 16, PACKED, EPI, WF>(p, st);
   }
 }
 
-template <int FMT, bool PACKED>
+template <int FMT, bool PACKED, int WF>
 hipError_t gmm1_nt(const Gmm1Params& p, hipStream_t st) {
   switch (p.act.kind) {
-    case 1: return gmm1_epi<FMT, PACKED, 1>(p, st);
-    case 2: return gmm1_epi<FMT, PACKED, 2>(p, st);
-    case 3: return gmm1_epi<FMT, PACKED, 3>(p, st);
-    case kActGelu: return gmm1_epi<FMT, PACKED, kActGelu>(p, st);
-    default: return gmm1_epi<FMT, PACKED, 0>(p, st);
+    case 1: return gmm1_epi<FMT, PACKED, 1, WF>(p, st);
+    case 2: return gmm1_epi<FMT, PACKED, 2, WF>(p, st);
+    case 3: return gmm1_epi<FMT, PACKED, 3, WF>(p, st);
+    case kActGelu: return gmm1_epi<FMT, PACKED, kActGelu, WF>(p, st);
+    default: return gmm1_epi<FMT, PACKED, 0, WF>(p, st);
   }
 }
 
-template <int FMT, bool PACKED>
+template <int FMT, bool PACKED, int WF>
 hipError_t gmm2_nt(const Gmm2Params& p, hipStream_t st) {
   switch (p.tt) {
-    case 1: return gmm2_go<FMT, 1, PACKED>(p, st);
-    case 2: return gmm2_go<FMT, 2, PACKED>(p, st);
-    case 4: return gmm2_go<FMT, 4, PACKED>(p, st);
-    case 8: return gmm2_go<FMT, 8, PACKED>(p, st);
-    default: return gmm2_go<FMT, 16, PACKED>(p, st);
+    case 1: return gmm2_go<FMT, 1, PACKED, WF>(p, st);
+    case 2: return gmm2_go<FMT, 2, PACKED, WF>(p, st);
+    case 4: return gmm2_go<FMT, 4, PACKED, WF>(p, st);
+    case 8: return gmm2_go<FMT, 8, PACKED, WF>(p, st);
+    default: return gmm2_go<FMT, 16, PACKED, WF>(p, st);
   }
 }
 
@@ -726,14 +754,23 @@ int gmm_token_tiles(int64_t rows, int64_t groups) {
   return 16;
 }
 
+// MXFP4 weights (the pages' A8W4-FP scenario) pair with E4M3 tokens only.
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t st) {
-  if (p.fmt == 0) return p.packed ? gmm1_nt<0, true>(p, st) : gmm1_nt<0, false>(p, st);
-  return p.packed ? gmm1_nt<1, true>(p, st) : gmm1_nt<1, false>(p, st);
+  if (p.wfp4) {
+    if (p.fmt != 0) return hipErrorInvalidValue;
+    return p.packed ? gmm1_nt<0, true, kFmtFp4>(p, st) : gmm1_nt<0, false, kFmtFp4>(p, st);
+  }
+  if (p.fmt == 0) return p.packed ? gmm1_nt<0, true, 0>(p, st) : gmm1_nt<0, false, 0>(p, st);
+  return p.packed ? gmm1_nt<1, true, 1>(p, st) : gmm1_nt<1, false, 1>(p, st);
 }
 
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t st) {
-  if (p.fmt == 0) return p.packed ? gmm2_nt<0, true>(p, st) : gmm2_nt<0, false>(p, st);
-  return p.packed ? gmm2_nt<1, true>(p, st) : gmm2_nt<1, false>(p, st);
+  if (p.wfp4) {
+    if (p.fmt != 0) return hipErrorInvalidValue;
+    return p.packed ? gmm2_nt<0, true, kFmtFp4>(p, st) : gmm2_nt<0, false, kFmtFp4>(p, st);
+  }
+  if (p.fmt == 0) return p.packed ? gmm2_nt<0, true, 0>(p, st) : gmm2_nt<0, false, 0>(p, st);
+  return p.packed ? gmm2_nt<1, true, 1>(p, st) : gmm2_nt<1, false, 1>(p, st);
 }
 
 hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
@@ -744,6 +781,19 @@ hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
   if (b1 < 1) b1 = 1;
   if (b2 < 1) b2 = 1;
   pack_codes_kernel<<<(unsigned)b1, 256, 0, st>>>(codes, packed, pieces, (int)n, (int)k);
+  pack_scales_kernel<<<(unsigned)b2, 256, 0, st>>>(scales, reinterpret_cast<uint32_t*>(packed_scales), words, (int)n,
+                                                   (int)k);
+  return hipGetLastError();
+}
+
+hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                                   uint8_t* packed, uint8_t* packed_scales, hipStream_t st) {
+  const int64_t pieces = groups * n * k / 32;   // 16-byte pieces of the [G, N, K/2] codes
+  const int64_t words = groups * (n / 16) * (((k >> 7) + 3) >> 2) * 64;
+  int64_t b1 = std::min<int64_t>((pieces + 255) / 256, 65536), b2 = std::min<int64_t>((words + 255) / 256, 65536);
+  if (b1 < 1) b1 = 1;
+  if (b2 < 1) b2 = 1;
+  pack_codes_fp4_kernel<<<(unsigned)b1, 256, 0, st>>>(codes, packed, pieces, (int)k);
   pack_scales_kernel<<<(unsigned)b2, 256, 0, st>>>(scales, reinterpret_cast<uint32_t*>(packed_scales), words, (int)n,
                                                    (int)k);
   return hipGetLastError();

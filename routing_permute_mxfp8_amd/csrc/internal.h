@@ -119,6 +119,7 @@ struct Gmm1Params {
   float* h1;                                   // nullable [rows, 2I]
   int packed;                                  // weights in the MFMA-native packed layout
   ActParams act;                               // A = act(G, U) [rows, I], or gelu(Z) [rows, 2I]
+  int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, 2I, H/2]; fmt must be E4M3)
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 
@@ -129,6 +130,7 @@ struct Gmm2Params {
   int hidden, inter, fmt, tt;
   float* o;                                    // [rows, H] fp32, sorted rows
   int packed;
+  int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, H, I/2]; fmt must be E4M3)
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 
@@ -139,6 +141,11 @@ int gmm_token_tiles(int64_t rows, int64_t groups);
 // packed scales [G, N/16, ceil(K/512), 64, 4].
 hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
                                uint8_t* packed, uint8_t* packed_scales, hipStream_t stream);
+
+// MXFP4 codes [G, N, K/2] + scales [G, N, K/32] -> packed codes [G, N/16, K/128, 64, 16 B]
+// (1 KB tiles) and the same packed scales.
+hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
+                                   uint8_t* packed, uint8_t* packed_scales, hipStream_t stream);
 
 // Chunks of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), i*tm}.
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);

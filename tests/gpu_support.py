@@ -46,19 +46,22 @@ def oracle_weights(cfg, n_experts=None, shared=False, gelu=False):
     return tuple(np.stack(v) for v in out)
 
 
-def library_weights(cfg, n_experts=None, shared=False):
-    """Weights generated on the GPU and quantized by the library (the benchmark's recipe)."""
+def library_weights(cfg, n_experts=None, shared=False, fp4=False):
+    """Weights generated on the GPU and quantized by the library (the benchmark's recipe);
+    MXFP4 codes two a byte with fp4."""
     n_experts = cfg.experts if n_experts is None else n_experts
     t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
     h, i = cfg.hidden, cfg.inter
-    w1q = torch.empty((n_experts, 2 * i, h), dtype=torch.uint8, device=DEV)
+    cb = 2 if fp4 else 1
+    q = rp.QUANT_MXFP4 if fp4 else QMODE[cfg.fmt]
+    w1q = torch.empty((n_experts, 2 * i, h // cb), dtype=torch.uint8, device=DEV)
     w1s = torch.empty((n_experts, 2 * i, h // 32), dtype=torch.uint8, device=DEV)
-    w2q = torch.empty((n_experts, h, i), dtype=torch.uint8, device=DEV)
+    w2q = torch.empty((n_experts, h, i // cb), dtype=torch.uint8, device=DEV)
     w2s = torch.empty((n_experts, h, i // 32), dtype=torch.uint8, device=DEV)
     for e in range(n_experts):
-        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t1, e, device=DEV), QMODE[cfg.fmt])
+        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t1, e, device=DEV), q)
         w1q[e].copy_(c); w1s[e].copy_(s)
-        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t2, e, device=DEV), QMODE[cfg.fmt])
+        c, s = rp.mx_quantize(moe_inputs.weight_master(cfg, t2, e, device=DEV), q)
         w2q[e].copy_(c); w2s[e].copy_(s)
     return w1q, w1s, w2q, w2s
 
@@ -178,9 +181,10 @@ def check_requant(aq_gpu, sa_gpu, a_ref, delta, fmt, max_code_diff=0.02, max_sca
     return code_diff, scale_diff
 
 
-def oracle_experts_parallel(cfg, experts, shared=False, workers=8):
+def oracle_experts_parallel(cfg, experts, shared=False, workers=8, fp4=False):
     """oracle_expert_from_gpu_masters for several experts: masters regenerated on the GPU
-    one after the other, the oracle quantizations run in a thread pool."""
+    one after the other, the oracle quantizations run in a thread pool (MXFP4, codes
+    packed two a byte, with fp4)."""
     from concurrent.futures import ThreadPoolExecutor
     t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
     masters = {}
@@ -190,8 +194,10 @@ def oracle_experts_parallel(cfg, experts, shared=False, workers=8):
 
     def work(e):
         m1, m2 = masters[e]
-        q1, s1 = mxfp.quantize(m1.double().numpy(), cfg.fmt)
-        q2, s2 = mxfp.quantize(m2.double().numpy(), cfg.fmt)
+        q1, s1 = mxfp.quantize(m1.double().numpy(), "e2m1" if fp4 else cfg.fmt)
+        q2, s2 = mxfp.quantize(m2.double().numpy(), "e2m1" if fp4 else cfg.fmt)
+        if fp4:
+            q1, q2 = mxfp.pack_fp4(q1), mxfp.pack_fp4(q2)
         return e, (q1, s1, q2, s2)
 
     with ThreadPoolExecutor(max_workers=workers) as ex:

@@ -134,6 +134,77 @@ def test_activations(kind, params, tt):
     assert mx <= 2e-2 and mean <= 5e-3
 
 
+def fp4_weights(cfg, n_experts=None, shared=False):
+    """MXFP4 (E2M1) weights quantized by the oracle from the bf16 masters, codes two a byte."""
+    n_experts = cfg.experts if n_experts is None else n_experts
+    t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
+    out = [[], [], [], []]
+    for e in range(n_experts):
+        q1, s1 = mxfp.quantize(moe_inputs.weight_master(cfg, t1, e).double().numpy(), "e2m1")
+        q2, s2 = mxfp.quantize(moe_inputs.weight_master(cfg, t2, e).double().numpy(), "e2m1")
+        for lst, v in zip(out, (mxfp.pack_fp4(q1), s1, mxfp.pack_fp4(q2), s2)):
+            lst.append(v)
+    return tuple(np.stack(v) for v in out)
+
+
+def device_weights_fp4(arrays, wf):
+    d = [to_dev(a) for a in arrays]
+    if wf == rp.WEIGHTS_PACKED:
+        return [*rp.pack_weights(d[0], d[1], fp4=True), *rp.pack_weights(d[2], d[3], fp4=True)]
+    return d
+
+
+@pytest.mark.parametrize("wf", [rp.WEIGHTS_ND, rp.WEIGHTS_PACKED], ids=["nd", "packed"])
+@pytest.mark.parametrize("case", [dict(tokens=96, inter=256, experts=8, topk=2, seed=51, shared="fp8"),
+                                  dict(tokens=600, inter=128, experts=4, topk=2, seed=52, shared="fp4"),
+                                  dict(tokens=333, inter=256, experts=16, topk=4, seed=53, shared=None)],
+                         ids=["2tile-shared8", "16tile-shared4", "4tile"])
+def test_a8w4(case, wf):
+    """A8W4-FP: E4M3 activations, MXFP4 routed weights (and MXFP4 or FP8 shared weights),
+    A requantized to E4M3; h1 and O from FP8 x FP4 products on the matrix cores."""
+    case = dict(case)
+    sh_kind = case.pop("shared")
+    cfg = moe_inputs.config("tiny", hidden=256, shared=0 if sh_kind is None else 1, **case)
+    say(f"mega_moe A8W4 N={cfg.tokens} I={cfg.inter} E={cfg.experts} K={cfg.topk} shared={sh_kind} wf={wf}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    x = x_t.double().numpy()
+    w = moe_inputs.gate_weights(cfg)
+    weights = fp4_weights(cfg)
+    shared_dev, shared_np, swd = None, (), 0
+    if sh_kind == "fp4":
+        sh = fp4_weights(cfg, 1, shared=True)
+        shared_dev, swd = tuple(device_weights_fp4(sh, wf)), rp.FP4_E2M1
+    elif sh_kind == "fp8":
+        sh = oracle_weights(cfg, 1, shared=True)
+        shared_dev, swd = tuple(device_weights(sh, wf)), rp.FP8_E4M3
+    if sh_kind:
+        shared_np = [tuple(a[0] for a in sh)]
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights_fp4(weights, wf),
+                              shared=shared_dev, quant_out_dtype=rp.FP8_E4M3, debug=True, weight_format=wf,
+                              weight_dtype=rp.FP4_E2M1, shared_weight_dtype=swd)
+    torch.cuda.synchronize()
+    ref = moe.mega_moe(x, ids, w, weights, "e4m3", cfg.experts, shared=shared_np, wfmt="e2m1",
+                       shared_wfmt="e4m3" if sh_kind == "fp8" else "e2m1")
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    h1_got = dbg["h1"].cpu().numpy()
+    err = normwise_err(h1_got, ref["h1"])
+    assert err <= 2e-3, err
+    offs = ref["routing"]["offsets"]
+    h1_abs = np.zeros_like(ref["h1"])
+    for e in range(cfg.experts):
+        if offs[e + 1] > offs[e]:
+            h1_abs[offs[e]:offs[e + 1]] = np.abs(mxfp.dequantize(ref["xq"][offs[e]:offs[e + 1]],
+                                                                 ref["sx"][offs[e]:offs[e + 1]], "e4m3")) @ \
+                np.abs(mxfp.dequantize(mxfp.unpack_fp4(weights[0][e]), weights[1][e], "e2m1")).T
+    check_gemm_elementwise(h1_got, ref["h1"], h1_abs, cfg.hidden)
+    delta = swiglu_delta(ref["h1"], h1_abs, cfg.hidden, cfg.inter)
+    codes, scales = check_requant(dbg["aq"].cpu().numpy(), dbg["sa"].cpu().numpy(), ref["a"], delta, "e4m3")
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  h1 err {err:.3g} requant codes differing {codes:.3g} scales {scales:.3g} Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
 @pytest.mark.parametrize("tokens,hidden,inter", [(64, 256, 128), (200, 512, 256), (40, 7168, 2048)])
 def test_shared_expert_alone(tokens, hidden, inter):
     """All gate weights 0: Y is the shared expert's dense FFN over every token."""
@@ -244,6 +315,45 @@ def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True, wf=rp.WEIG
         say(f"  expert {e} ({hi - lo} rows): h1 err {err_e:.3g}, requant codes differing {codes:.3g} "
             f"scales {scales:.3g}")
         assert err_e <= 2e-3
+
+
+@pytest.mark.timeout(900)
+def test_full_size_decode_a8w4():
+    """The decode-shaped layer with MXFP4 weights (A8W4-FP) in the benchmark's configuration
+    (library-quantized, packed): routing exact, the library's MXFP4 weight bytes equal the
+    oracle's, sampled tokens' Y and h1 within the layer tolerances."""
+    cfg = moe_inputs.config("decode")
+    say(f"mega_moe full size decode A8W4: N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    weights = library_weights(cfg, fp4=True)
+    dev_w = [*rp.pack_weights(weights[0], weights[1], fp4=True), *rp.pack_weights(weights[2], weights[3], fp4=True)]
+    say("  weights ready")
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w,
+                              quant_out_dtype=rp.FP8_E4M3, debug=True, weight_format=rp.WEIGHTS_PACKED,
+                              weight_dtype=rp.FP4_E2M1)
+    torch.cuda.synchronize()
+    r = routing.init_routing(ids, cfg.experts)
+    assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), r["sorted_row_idx"])
+    rng = np.random.default_rng(8)
+    tokens = rng.choice(cfg.tokens, size=4, replace=False)
+    needed = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
+    cache = oracle_experts_parallel(cfg, needed, fp4=True)
+    for e in needed:
+        for j in range(4):
+            assert np.array_equal(weights[j][e].cpu().numpy(), cache[e][j]), (e, j)
+    x = x_t.double().numpy()
+    ref = moe.per_token(x, ids, w, lambda e: cache[e], "e4m3", tokens, wfmt="e2m1")
+    y_got = y[torch.from_numpy(tokens).to(DEV)].cpu().double().numpy()
+    mx, mean = y_errors(y_got, ref["y"])
+    inv = routing.inverse(r["sorted_row_idx"]).reshape(cfg.tokens, cfg.topk)
+    pos = inv[tokens].reshape(-1)
+    h1_got = dbg["h1"][torch.from_numpy(pos).to(DEV)].cpu().numpy()
+    err = normwise_err(h1_got, ref["h1"].reshape(len(pos), -1))
+    say(f"  sampled tokens {tokens.tolist()}: Y max {mx:.3g} mean {mean:.3g}, h1 err {err:.3g}")
+    assert err <= 2e-3
+    assert mx <= 2e-2 and mean <= 5e-3
 
 
 @pytest.mark.timeout(900)

@@ -208,3 +208,26 @@ def test_zero_gate_weights_leave_the_shared_expert():
     xq, sx = mxfp.quantize(x, cfg.fmt)
     dense = moe.expert_ffn(xq, sx, *shared[0], cfg.fmt)["o"]
     assert np.array_equal(full["y"], mxfp.bf16_round(dense))
+
+
+def test_a8w4_gemm_equals_the_same_weights_in_fp8():
+    """A8W4-FP (MegaMoE "A8W4-FP quantization scenario"): FP8 activations times MXFP4
+    weights. Every E2M1 value is exact in E4M3, so the same dequantized weights written
+    as E4M3 codes under the same E8M0 scales must give the identical float64 product;
+    this pins the nibble order and the FP4 dequantization against the FP8 path."""
+    rng = np.random.default_rng(12)
+    m, n, k = 5, 48, 256
+    xq, sx = mxfp.quantize(rng.normal(size=(m, k)), "e4m3")
+    w4, ws = mxfp.quantize(rng.normal(size=(n, k)) / 16, "e2m1")
+    w4p = mxfp.pack_fp4(w4)
+    w8 = mxfp.round_to_format(mxfp.decode_table("e2m1")[w4], "e4m3")
+    assert np.array_equal(mxfp.decode_table("e4m3")[w8], mxfp.decode_table("e2m1")[w4])
+    got = moe.gmm(xq, sx, w4p, ws, "e4m3", "e2m1")
+    assert np.array_equal(got, moe.gmm(xq, sx, w8, ws, "e4m3"))
+    # one-hot: x = 1.0 at k = 3 (scale 2^0), weight row 7 = 6.0 at k = 3 (code 7, scale 2^-1)
+    xq = np.zeros((1, 64), np.uint8); xq[0, 3] = 0x38
+    sx = np.full((1, 2), 127, np.uint8)
+    w = np.zeros((16, 64), np.uint8); w[7, 3] = 7
+    ws = np.full((16, 2), 126, np.uint8)
+    h = moe.gmm(xq, sx, mxfp.pack_fp4(w), ws, "e4m3", "e2m1")
+    assert h[0, 7] == 3.0 and np.count_nonzero(h) == 1

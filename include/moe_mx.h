@@ -288,6 +288,12 @@ typedef struct {
   int weight_dtype;               /* routed w1/w2: 0 or quant_out_dtype = FP8 (A8W8-FP),      */
                                   /* MOE_FP4_E2M1 = MXFP4 (A8W4-FP; needs FLOAT8_E4M3FN x)  */
   int shared_weight_dtype;        /* shared experts: 0 = as weight_dtype, or as above        */
+  int x_is_quantized;             /* 0: x is bf16, quantized inside ([MM] dispatchQuantMode 4); */
+                                  /* 1: pre-quantized pass-through (dispatchQuantMode 0): x   */
+                                  /* holds FP8 codes of quant_out_dtype [num_tokens, hidden]  */
+                                  /* and x_scales their E8M0 scales [num_tokens, hidden/32];  */
+                                  /* stage 1 only gathers them                                */
+  const uint8_t* x_scales;        /* device, with x_is_quantized; else NULL                 */
 } moe_mega_args;
 
 /* A8W4-FP ([MM] "A8W4-FP quantization scenario"): with weight_dtype MOE_FP4_E2M1 the  */

@@ -59,6 +59,7 @@ class MegaArgs(ctypes.Structure):
         ("stage_events", ctypes.POINTER(ctypes.c_void_p)),
         ("num_activation_params", ctypes.c_int), ("activation_params", ctypes.c_float * 3),
         ("weight_dtype", ctypes.c_int), ("shared_weight_dtype", ctypes.c_int),
+        ("x_is_quantized", ctypes.c_int), ("x_scales", ctypes.c_void_p),
     ]
 
 MEGA_STAGE_EVENTS = 7
@@ -245,7 +246,7 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
 
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
                  debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=(), weight_dtype=0,
-                 shared_weight_dtype=0):
+                 shared_weight_dtype=0, x_scales=None):
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -265,6 +266,8 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
         raise ValueError("activation_params holds at most 3 values")
     a.num_activation_params = len(activation_params)
     a.weight_dtype, a.shared_weight_dtype = weight_dtype, shared_weight_dtype
+    if x_scales is not None:   # pre-quantized pass-through: x holds FP8 codes
+        a.x_is_quantized, a.x_scales = 1, _ptr(_u8(x_scales))
     for j, v in enumerate(activation_params):
         a.activation_params[j] = float(v)
     a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
@@ -276,7 +279,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
 def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
              quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None,
              weight_format: int = WEIGHTS_ND, activation: int = ACT_SWIGLU, activation_params=(),
-             weight_dtype: int = 0, shared_weight_dtype: int = 0):
+             weight_dtype: int = 0, shared_weight_dtype: int = 0, x_scales=None):
     """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
     debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
 
@@ -290,9 +293,13 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     activation / activation_params: ACT_* and its parameter list as in the C header (gelu
     makes A, and w2's input width, 2 * inter).
     weight_dtype / shared_weight_dtype: 0 (FP8 as the activations) or FP4_E2M1 (MXFP4 codes
-    two a byte, e.g. from mx_quantize(..., QUANT_MXFP4); pack_weights(..., fp4=True))."""
+    two a byte, e.g. from mx_quantize(..., QUANT_MXFP4); pack_weights(..., fp4=True)).
+    x_scales: pre-quantized pass-through: x holds FP8 codes of quant_out_dtype (uint8
+    [N, H], e.g. from mx_quantize) and x_scales their E8M0 scales [N, H/32]."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
+    if x_scales is not None and x_scales.shape[1] != x.shape[1] // 32:
+        x_scales = x_scales[:, :x.shape[1] // 32].contiguous()   # drop the AlignUp(.., 2) padding column
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -312,7 +319,7 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
                    o=torch.empty((f, h), dtype=torch.float32, device=dev),
                    sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg,
-                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype)
+                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype, x_scales)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} entries (events or None)")

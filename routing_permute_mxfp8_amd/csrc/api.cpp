@@ -273,6 +273,12 @@ moe_status check_mega(const moe_mega_args* a) {
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: weight_format %d not 0 (ND) or 1 (packed)", a->weight_format);
   if (a->num_tokens > 0 && (!a->x || !a->topk_ids || !a->topk_weights || !a->y))
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: x, topk_ids, topk_weights and y must be non-NULL");
+  if (a->x_is_quantized != 0 && a->x_is_quantized != 1)
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: x_is_quantized must be 0 or 1");
+  if (a->x_is_quantized && a->num_tokens > 0 && !a->x_scales)
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: pre-quantized x needs x_scales");
+  if (!a->x_is_quantized && a->x_scales)
+    return fail(MOE_ERR_INVALID_ARG, "mega_moe: x_scales is only taken with pre-quantized x");
   if (!a->w1 || !a->w1_scales || !a->w2 || !a->w2_scales)
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: w1, w1_scales, w2, w2_scales must be non-NULL");
   if (a->num_shared > 0 && (!a->shared_w1 || !a->shared_w1_scales || !a->shared_w2 || !a->shared_w2_scales))
@@ -577,19 +583,32 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
   // of the shared experts)
-  moe::PermuteTilesParams pt;
-  pt.x = a->x; pt.in_dtype = MOE_DTYPE_BF16; pt.hidden = (int)h; pt.row_token = w.row_token;
-  pt.chunks = w.tiles; pt.chunk_count = w.tile_count; pt.max_chunks = w.max_tiles; pt.tt = w.tt; pt.fmt = fmt;
-  pt.out = w.xq; pt.out_scales = w.sx;
-  e = moe::launch_permute_tiles(pt, st);
+  // (pre-quantized x: the codes and scales are gathered as they are, [MM] dispatchQuantMode 0)
+  const uint8_t* xcodes = static_cast<const uint8_t*>(a->x);
+  if (a->x_is_quantized) {
+    e = moe::launch_pack_tokens(xcodes, a->x_scales, (int)h, w.tiles, w.tile_count, w.max_tiles, w.tt, w.xq, w.sx,
+                                st, w.row_token);
+  } else {
+    moe::PermuteTilesParams pt;
+    pt.x = a->x; pt.in_dtype = MOE_DTYPE_BF16; pt.hidden = (int)h; pt.row_token = w.row_token;
+    pt.chunks = w.tiles; pt.chunk_count = w.tile_count; pt.max_chunks = w.max_tiles; pt.tt = w.tt; pt.fmt = fmt;
+    pt.out = w.xq; pt.out_scales = w.sx;
+    e = moe::launch_permute_tiles(pt, st);
+  }
   if (e != hipSuccess) return hip_fail(e, "mega_moe permute launch");
   if (a->num_shared > 0) {
     e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
-    moe::PermuteTilesParams ps = pt;
-    ps.row_token = nullptr; ps.chunks = w.sh_tiles; ps.chunk_count = w.sh_count; ps.max_chunks = w.sh_max_tiles;
-    ps.tt = w.sh_tt; ps.out = w.xq_sh; ps.out_scales = w.sx_sh;
-    e = moe::launch_permute_tiles(ps, st);
+    if (a->x_is_quantized) {
+      e = moe::launch_pack_tokens(xcodes, a->x_scales, (int)h, w.sh_tiles, w.sh_count, w.sh_max_tiles, w.sh_tt,
+                                  w.xq_sh, w.sx_sh, st);
+    } else {
+      moe::PermuteTilesParams ps;
+      ps.x = a->x; ps.in_dtype = MOE_DTYPE_BF16; ps.hidden = (int)h; ps.row_token = nullptr;
+      ps.chunks = w.sh_tiles; ps.chunk_count = w.sh_count; ps.max_chunks = w.sh_max_tiles; ps.tt = w.sh_tt;
+      ps.fmt = fmt; ps.out = w.xq_sh; ps.out_scales = w.sx_sh;
+      e = moe::launch_permute_tiles(ps, st);
+    }
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared permute launch");
   }
   if (a->xq || a->sx) {

@@ -72,10 +72,11 @@ struct PermuteTilesParams {
   uint8_t* out_scales = nullptr; // tiled scales
 };
 hipError_t launch_permute_tiles(const PermuteTilesParams& p, hipStream_t stream);
-// Row-major codes [rows, K] / scales [rows, K/32] (sorted rows) <-> tiled layout.
+// Row-major codes [rows, K] / scales [rows, K/32] (sorted rows) <-> tiled layout; the pack
+// may gather (sorted row i <- source row row_token[i]).
 hipError_t launch_pack_tokens(const uint8_t* codes, const uint8_t* scales, int K, const int4* chunks,
                               const int* chunk_count, int max_chunks, int tt, uint8_t* out, uint8_t* out_scales,
-                              hipStream_t stream);
+                              hipStream_t stream, const int32_t* row_token = nullptr);
 hipError_t launch_unpack_tokens(const uint8_t* in, const uint8_t* in_scales, int K, const int4* chunks,
                                 const int* chunk_count, int max_chunks, int tt, uint8_t* codes, uint8_t* scales,
                                 hipStream_t stream);

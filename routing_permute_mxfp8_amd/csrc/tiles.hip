@@ -152,9 +152,12 @@ __global__ __launch_bounds__(256) void permute_tiles_kernel(const InT* __restric
   }
 }
 
-// Row-major FP8 codes [rows, K] and scales [rows, K/32] (sorted rows) -> tiled layout.
+// Row-major FP8 codes [rows, K] and scales [rows, K/32] -> tiled layout. Sorted row i
+// takes source row row_token[i] (a gather of already quantized tokens), or row i itself
+// when row_token is null.
 __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint8_t* __restrict__ codes,
                                                           const uint8_t* __restrict__ scales, int K,
+                                                          const int32_t* __restrict__ row_token,
                                                           const int4* __restrict__ chunks,
                                                           const int* __restrict__ chunk_count, int max_chunks, int tt,
                                                           uint8_t* __restrict__ out, uint8_t* __restrict__ out_scales) {
@@ -165,7 +168,7 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint8_t* __restr
     TileItem ti;
     if (!tile_item(it, tt, kq, chunks, &ti)) continue;
     const bool valid = r < ti.nvalid;
-    const int64_t row = ti.srow + r;
+    const int64_t row = valid && row_token ? (int64_t)row_token[ti.srow + r] : ti.srow + r;
     uint32_t sword = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -250,10 +253,10 @@ hipError_t launch_permute_tiles(const PermuteTilesParams& p, hipStream_t stream)
 
 hipError_t launch_pack_tokens(const uint8_t* codes, const uint8_t* scales, int K, const int4* chunks,
                               const int* chunk_count, int max_chunks, int tt, uint8_t* out, uint8_t* out_scales,
-                              hipStream_t stream) {
+                              hipStream_t stream, const int32_t* row_token) {
   if (max_chunks <= 0) return hipSuccess;
-  pack_tokens_kernel<<<tile_grid(max_chunks, tt, K), 256, 0, stream>>>(codes, scales, K, chunks, chunk_count,
-                                                                        max_chunks, tt, out, out_scales);
+  pack_tokens_kernel<<<tile_grid(max_chunks, tt, K), 256, 0, stream>>>(codes, scales, K, row_token, chunks,
+                                                                        chunk_count, max_chunks, tt, out, out_scales);
   return hipGetLastError();
 }
 

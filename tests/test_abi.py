@@ -153,6 +153,12 @@ def test_mega_moe_validation(lib):
     assert act(3) == 0 and act(3, 2.0) == 0 and act(3, 2.0, 4.0) == 0   # situglu
     assert act(3, 0.0) == 1 and act(3, 2.0, -1.0) == 1
     assert act(4) == 0 and act(4, flt_max) == 0 and act(4, 5.0) == 1     # gelu: no clamp
+    assert status(x_is_quantized=1) == 1                       # pre-quantized x needs x_scales
+    assert status(x_scales=FAKE) == 1                          # scales only with pre-quantized x
+    assert status(x_is_quantized=1, x_scales=FAKE) == 0
+    assert status(x_is_quantized=2, x_scales=FAKE) == 1
+    assert status(weight_dtype=296) == 0 and status(weight_dtype=296, quant_out_dtype=23) == 4
+    assert status(weight_dtype=23) == 4 and status(weight_dtype=7) == 3 and status(shared_weight_dtype=296) == 0
     assert status(topk_weights_dtype=1) == 3
     assert status(num_shared=5) == 2
     assert status(num_shared=1) == 1   # shared weights missing

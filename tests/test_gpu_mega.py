@@ -14,7 +14,7 @@ import torch
 import moe_inputs
 import routing_permute_mxfp8_amd as rp
 from oracle import moe, mxfp, routing
-from gpu_support import (DEV, FP8, abs_gmm, act_delta, check_gemm_elementwise, check_requant, library_weights,
+from gpu_support import (DEV, FP8, QMODE, abs_gmm, act_delta, check_gemm_elementwise, check_requant, library_weights,
                          normwise_err,
                          oracle_expert_from_gpu_masters, oracle_experts_parallel, oracle_weights, say, swiglu_delta,
                          to_dev, y_errors)
@@ -202,6 +202,36 @@ def test_a8w4(case, wf):
     codes, scales = check_requant(dbg["aq"].cpu().numpy(), dbg["sa"].cpu().numpy(), ref["a"], delta, "e4m3")
     mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
     say(f"  h1 err {err:.3g} requant codes differing {codes:.3g} scales {scales:.3g} Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
+@pytest.mark.parametrize("fmt", ["e4m3", "e5m2"])
+def test_prequantized_passthrough(fmt):
+    """MegaMoE dispatchQuantMode 0: x already MX-quantized (codes + E8M0 scales) skips the
+    stage-1 quantization. Given the library's own quantization of x the layer must be the
+    same bit for bit as with bf16 x quantized inside (routed and shared experts)."""
+    cfg = moe_inputs.config("tiny", tokens=200, hidden=512, inter=256, experts=16, topk=4, shared=1, seed=61,
+                            fmt=fmt)
+    say(f"mega_moe pre-quantized x fmt={fmt}")
+    ids = to_dev(moe_inputs.expert_ids(cfg).astype(np.int32))
+    x = moe_inputs.activations(cfg).to(DEV)
+    w = to_dev(moe_inputs.gate_weights(cfg))
+    wts = device_weights(oracle_weights(cfg), rp.WEIGHTS_PACKED)
+    sh = tuple(device_weights(oracle_weights(cfg, 1, shared=True), rp.WEIGHTS_PACKED))
+    q = FP8[cfg.fmt]
+    y0, e0, d0 = rp.mega_moe(x, ids, w, *wts, shared=sh, quant_out_dtype=q, debug=True,
+                             weight_format=rp.WEIGHTS_PACKED)
+    codes, scales = rp.mx_quantize(x, QMODE[cfg.fmt])
+    y1, e1, d1 = rp.mega_moe(codes, ids, w, *wts, shared=sh, quant_out_dtype=q, debug=True,
+                             weight_format=rp.WEIGHTS_PACKED, x_scales=scales)
+    torch.cuda.synchronize()
+    assert torch.equal(d0["xq"], d1["xq"]) and torch.equal(d0["sx"], d1["sx"])
+    assert torch.equal(y0, y1) and torch.equal(e0, e1)
+    ref = moe.mega_moe(x.cpu().double().numpy(), moe_inputs.expert_ids(cfg), moe_inputs.gate_weights(cfg),
+                       oracle_weights(cfg), cfg.fmt, cfg.experts,
+                       shared=[tuple(a[0] for a in oracle_weights(cfg, 1, shared=True))])
+    assert np.array_equal(d1["xq"].cpu().numpy(), ref["xq"])
+    mx, mean = y_errors(y1.cpu().double().numpy(), ref["y"])
     assert mx <= 2e-2 and mean <= 5e-3
 
 

@@ -717,6 +717,7 @@ hipError_t gmm1_epi(const Gmm1Params& p, hipStream_t st) {
     case 2: return gmm1_go<FMT, 2, PACKED, EPI, WF>(p, st);
     case 4: return gmm1_go<FMT, 4, PACKED, EPI, WF>(p, st);
     case 8: return gmm1_go<FMT, 8, PACKED, EPI, WF>(p, st);
+    case 18: return gmm1_go<FMT, 18, PACKED, EPI, WF>(p, st);
     default: return gmm1_go<FMT, 16, PACKED, EPI, WF>(p, st);
   }
 }
@@ -752,6 +753,17 @@ int gmm_token_tiles(int64_t rows, int64_t groups) {
   if (avg <= 64.0) return 4;
   if (avg <= 128.0) return 8;
   return 16;
+}
+
+// GMM1 over many groups of 240-288 rows (a prefill-shaped layer: 256 +- 16 rows per
+// expert) takes 288-row chunks: almost every expert is then one chunk, so its weights
+// are streamed once instead of twice for the experts just above 256 rows (the 288
+// accumulators per lane cost some moves between accumulation and vector registers,
+// which GMM1 hides behind its weight stream and GMM2 does not).
+int gmm1_token_tiles(int64_t rows, int64_t groups) {
+  const double avg = groups > 0 ? (double)rows / (double)groups : (double)rows;
+  if (groups > 1 && avg > 240.0 && avg <= 288.0) return 18;
+  return gmm_token_tiles(rows, groups);
 }
 
 // MXFP4 weights (the pages' A8W4-FP scenario) pair with E4M3 tokens only.

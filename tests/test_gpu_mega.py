@@ -27,6 +27,8 @@ SMALL = [
     dict(name="tiny", tokens=333, hidden=512, inter=256, experts=16, topk=4, shared=2, seed=42),
     dict(name="skewed", tokens=500, hidden=384, inter=384, experts=20, topk=5, seed=43),
     dict(name="tiny", tokens=5, hidden=256, inter=128, experts=32, topk=8, seed=44),
+    # ~256 rows per expert: GMM1 in 288-row chunks, GMM2 in 256-row chunks of a second list
+    dict(name="tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, shared=1, seed=45),
 ]
 
 
@@ -92,14 +94,17 @@ ACT_KIND = {"swiglu": rp.ACT_SWIGLU, "swiglustep": rp.ACT_SWIGLUSTEP, "swigluoai
 
 
 @pytest.mark.parametrize("kind,params", ACTS, ids=lambda v: str(v))
-@pytest.mark.parametrize("tt", ["small", "wide"])
+@pytest.mark.parametrize("tt", ["small", "wide", "long"])
 def test_activations(kind, params, tt):
     """MegaMoE "Activation function formulas": every activation and parameter list, routed
-    and shared experts, in 1-tile (small) and 16-tile (wide) chunks; clamps that bite."""
+    and shared experts, in 1-tile (small), 16-tile (wide) and GMM1's 18-tile (long) chunks;
+    clamps that bite."""
     if tt == "small":
         cfg = moe_inputs.config("tiny", tokens=96, hidden=256, inter=256, experts=8, topk=2, shared=1, seed=47)
-    else:
+    elif tt == "wide":
         cfg = moe_inputs.config("tiny", tokens=600, hidden=256, inter=128, experts=4, topk=2, shared=1, seed=48)
+    else:
+        cfg = moe_inputs.config("tiny", tokens=520, hidden=256, inter=256, experts=4, topk=2, shared=1, seed=49)
     say(f"mega_moe activation {kind} {params} N={cfg.tokens} I={cfg.inter} E={cfg.experts}")
     gelu = kind == "gelu"
     ids = moe_inputs.expert_ids(cfg)
@@ -157,8 +162,9 @@ def device_weights_fp4(arrays, wf):
 @pytest.mark.parametrize("wf", [rp.WEIGHTS_ND, rp.WEIGHTS_PACKED], ids=["nd", "packed"])
 @pytest.mark.parametrize("case", [dict(tokens=96, inter=256, experts=8, topk=2, seed=51, shared="fp8"),
                                   dict(tokens=600, inter=128, experts=4, topk=2, seed=52, shared="fp4"),
-                                  dict(tokens=333, inter=256, experts=16, topk=4, seed=53, shared=None)],
-                         ids=["2tile-shared8", "16tile-shared4", "4tile"])
+                                  dict(tokens=333, inter=256, experts=16, topk=4, seed=53, shared=None),
+                                  dict(tokens=512, inter=256, experts=4, topk=2, seed=54, shared="fp4")],
+                         ids=["2tile-shared8", "16tile-shared4", "4tile", "18tile-shared4"])
 def test_a8w4(case, wf):
     """A8W4-FP: E4M3 activations, MXFP4 routed weights (and MXFP4 or FP8 shared weights),
     A requantized to E4M3; h1 and O from FP8 x FP4 products on the matrix cores."""

@@ -64,21 +64,22 @@ def layer_work(cfg, ids, fp4=False):
     """Algorithmic bytes and flops per launch of the two grouped GEMMs and the combine:
     GMM1 reads the touched experts' W1 (codes + 1/32 scales; half a byte a code for MXFP4
     weights) and the quantized rows, and writes the requantized rows; GMM2 reads W2 and
-    those rows and writes fp32 O; the combine reads fp32 O (and the shared experts' O) and
+    those rows and writes O, bf16 rows (the default combine mode: each expert's output
+    reaches the combine as BF16); the combine reads O (and the shared experts' O) and
     writes bf16 Y."""
     h, i, f = cfg.hidden, cfg.inter, cfg.flat
     touched = int(np.unique(ids).size)
     sc = 1.0 + 1.0 / 32.0
     wsc = (0.5 if fp4 else 1.0) + 1.0 / 32.0
     gmm1_bytes = touched * 2 * i * h * wsc + f * h * sc + f * i * sc
-    gmm2_bytes = touched * h * i * wsc + f * i * sc + f * h * 4
-    combine_bytes = f * h * 4 + cfg.shared * cfg.tokens * h * 4 + cfg.tokens * h * 2
+    gmm2_bytes = touched * h * i * wsc + f * i * sc + f * h * 2
+    combine_bytes = f * h * 2 + cfg.shared * cfg.tokens * h * 2 + cfg.tokens * h * 2
     gmm1_flops = 2.0 * f * h * 2 * i
     gmm2_flops = 2.0 * f * i * h
     if cfg.shared:
         n = cfg.tokens
         gmm1_bytes_s = cfg.shared * (2 * i * h * sc + n * h * sc + n * i * sc)
-        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc + n * h * 4)
+        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc + n * h * 2)
         shared = dict(bytes=gmm1_bytes_s + gmm2_bytes_s, flops=cfg.shared * 6.0 * n * h * i)
     else:
         shared = dict(bytes=0.0, flops=0.0)
@@ -326,7 +327,7 @@ def bench_mega(args, torch, rp, moe_inputs):
                            weight_dtype=args.weight_dtype,
                            tokens=cfg.tokens, hidden=cfg.hidden, inter=cfg.inter, experts=cfg.experts,
                            topk=cfg.topk, shared=cfg.shared, fmt=cfg.fmt, touched_experts=work["touched"],
-                           weight_layout=args.weights),
+                           weight_layout=args.weights, combine_comm_mode=0),
                roofline=roofline,
                layer=dict(algorithmic_bytes=total_bytes, flops=total_flops,
                           hbm_frac=round(total_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

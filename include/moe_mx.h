@@ -203,6 +203,8 @@ moe_status moe_token_permute(const void* tokens, int dtype, int64_t n, int64_t h
 /*            A = SiLU(G) * U (fp32),  A^, S_A = Q_MX(A) with the same FP8 type */
 /*   stage 3  O = DQ(A^).DQ(W2)                                                 */
 /*   stage 4  y[t] = bf16( sum_k w[t,k] O[row(t,k)] + sum_s O_shared_s[t] )    */
+/*            with every O row first rounded to bf16 (combine_comm_mode 0) or    */
+/*            kept fp32 (combine_comm_mode 1), the sum in fp32                  */
 /* Shapes ([MM] "MXFP quantization scenario constraints"):                     */
 /*   x            bf16 [num_tokens, hidden]                                      */
 /*   topk_ids     int32 [num_tokens, topk], values in [0, num_experts), distinct */
@@ -294,6 +296,14 @@ typedef struct {
                                   /* and x_scales their E8M0 scales [num_tokens, hidden/32];  */
                                   /* stage 1 only gathers them                                */
   const uint8_t* x_scales;        /* device, with x_is_quantized; else NULL                 */
+  int combine_comm_mode;          /* [MM] combineCommMode with every expert on this card:   */
+                                  /* 0 (the pages' default, no deduplication): each expert's */
+                                  /* output row, routed or shared, reaches the combine as   */
+                                  /* BF16 and the weighted sum of those rows (fp32) is      */
+                                  /* rounded to bf16 y; 1 (intra-card deduplication): a     */
+                                  /* token's expert outputs are summed in fp32 and rounded  */
+                                  /* once. The o parity output stays fp32 either way. Other */
+                                  /* values: MOE_ERR_UNSUPPORTED (2 is a multi-server mode) */
 } moe_mega_args;
 
 /* A8W4-FP ([MM] "A8W4-FP quantization scenario"): with weight_dtype MOE_FP4_E2M1 the  */

@@ -137,21 +137,30 @@ def _getter(weights):
     return lambda e: (w1q[e], w1s[e], w2q[e], w2s[e])
 
 
-def combine(o_rows, expanded_row_idx, topk_weights, shared_o=()):
-    """Stage 4: Y[t] = bf16( sum_k w[t,k] O[row(t,k)] + sum_s O_s[t] ), float64 sum."""
+def combine(o_rows, expanded_row_idx, topk_weights, shared_o=(), combine_comm_mode=0):
+    """Stage 4: Y[t] = bf16( sum_k w[t,k] O[row(t,k)] + sum_s O_s[t] ), float64 sum.
+
+    MegaMoE combineCommMode: with 0 (no deduplication, the default) each expert's output
+    row is sent back as BF16, so every O row (routed and shared) is rounded to bf16
+    before the weighted sum; with 1 a token's expert outputs on the card are summed in
+    FP32 and converted to BF16 once, so the rows enter the sum unrounded."""
+    if combine_comm_mode not in (0, 1):
+        raise ValueError("combine_comm_mode must be 0 or 1 on one card")
+    rows = mxfp.bf16_round if combine_comm_mode == 0 else (lambda v: np.asarray(v, dtype=np.float64))
     w = np.asarray(topk_weights, dtype=np.float64)
     n, k = w.shape
     idx = np.asarray(expanded_row_idx).reshape(n, k)
+    o_rows = rows(o_rows)
     y = np.zeros((n, o_rows.shape[1]), dtype=np.float64)
     for j in range(k):
         y += w[:, j:j + 1] * o_rows[idx[:, j]]
     for o_s in shared_o:
-        y += o_s
+        y += rows(o_s)
     return mxfp.bf16_round(y)
 
 
 def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), act=("swiglu", ()), wfmt=None,
-             shared_wfmt=None) -> dict:
+             shared_wfmt=None, combine_comm_mode=0) -> dict:
     """The whole layer on all tokens, in the permuted (expert-contiguous) order.
 
     x: [N, H] values (bf16 as float64); topk_ids int [N, K]; topk_weights [N, K];
@@ -191,13 +200,13 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
                                        wfmt if shared_wfmt is None else shared_wfmt)["o"])
     out["shared_o"] = shared_o
     full_scatter = routing.inverse(r["sorted_row_idx"])
-    out["y"] = combine(out["o"], full_scatter, topk_weights, shared_o)
+    out["y"] = combine(out["o"], full_scatter, topk_weights, shared_o, combine_comm_mode)
     out["expert_token_nums"] = r["counts"].astype(np.int32)
     return out
 
 
 def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("swiglu", ()), wfmt=None,
-              shared_wfmt=None) -> dict:
+              shared_wfmt=None, combine_comm_mode=0) -> dict:
     """The layer for selected tokens, one (token, k) at a time, with no permutation
     (the "brute force" form of stage 1-4: each expert receives a copy of x_t).
 
@@ -218,6 +227,8 @@ def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("
             cache[e] = get(e)
         return cache[e]
 
+    # combineCommMode 0: each expert's output row arrives at the combine as BF16
+    rows = mxfp.bf16_round if combine_comm_mode == 0 else (lambda v: v)
     ys, h1s, os_ = [], [], []
     for t in tokens:
         xq_t, sx_t = mxfp.quantize(x[t:t + 1], fmt)
@@ -225,11 +236,11 @@ def per_token(x, topk_ids, topk_weights, weights, fmt, tokens, shared=(), act=("
         h1_t, o_t = [], []
         for j in range(k):
             r = expert_ffn(xq_t, sx_t, *expert(int(ids[t, j])), fmt, act, wfmt)
-            acc = acc + w[t, j] * r["o"]
+            acc = acc + w[t, j] * rows(r["o"])
             h1_t.append(r["h1"][0])
             o_t.append(r["o"][0])
         for sw in shared:
-            acc = acc + expert_ffn(xq_t, sx_t, *sw, fmt, act, wfmt if shared_wfmt is None else shared_wfmt)["o"]
+            acc = acc + rows(expert_ffn(xq_t, sx_t, *sw, fmt, act, wfmt if shared_wfmt is None else shared_wfmt)["o"])
         ys.append(mxfp.bf16_round(acc)[0])
         h1s.append(h1_t)
         os_.append(o_t)

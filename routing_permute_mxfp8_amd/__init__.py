@@ -60,6 +60,7 @@ class MegaArgs(ctypes.Structure):
         ("num_activation_params", ctypes.c_int), ("activation_params", ctypes.c_float * 3),
         ("weight_dtype", ctypes.c_int), ("shared_weight_dtype", ctypes.c_int),
         ("x_is_quantized", ctypes.c_int), ("x_scales", ctypes.c_void_p),
+        ("combine_comm_mode", ctypes.c_int),
     ]
 
 MEGA_STAGE_EVENTS = 7
@@ -246,7 +247,7 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
 
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
                  debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=(), weight_dtype=0,
-                 shared_weight_dtype=0, x_scales=None):
+                 shared_weight_dtype=0, x_scales=None, combine_comm_mode=0):
     n, h = x.shape
     k = topk_ids.shape[1]
     e, two_i, _ = w1.shape
@@ -268,6 +269,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
     a.weight_dtype, a.shared_weight_dtype = weight_dtype, shared_weight_dtype
     if x_scales is not None:   # pre-quantized pass-through: x holds FP8 codes
         a.x_is_quantized, a.x_scales = 1, _ptr(_u8(x_scales))
+    a.combine_comm_mode = combine_comm_mode
     for j, v in enumerate(activation_params):
         a.activation_params[j] = float(v)
     a.y, a.expert_token_nums = _ptr(y), _ptr(etn)
@@ -279,7 +281,7 @@ def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared
 def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
              quant_out_dtype: int = FP8_E4M3, debug: bool = False, workspace=None, stage_events=None,
              weight_format: int = WEIGHTS_ND, activation: int = ACT_SWIGLU, activation_params=(),
-             weight_dtype: int = 0, shared_weight_dtype: int = 0, x_scales=None):
+             weight_dtype: int = 0, shared_weight_dtype: int = 0, x_scales=None, combine_comm_mode: int = 0):
     """The MX MoE layer. Returns (y bf16 [N, H], expert_token_nums int32 [E]) and, with
     debug=True, a dict of the stage intermediates (xq, sx, h1, aq, sa, o, sorted_row_idx).
 
@@ -295,7 +297,9 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     weight_dtype / shared_weight_dtype: 0 (FP8 as the activations) or FP4_E2M1 (MXFP4 codes
     two a byte, e.g. from mx_quantize(..., QUANT_MXFP4); pack_weights(..., fp4=True)).
     x_scales: pre-quantized pass-through: x holds FP8 codes of quant_out_dtype (uint8
-    [N, H], e.g. from mx_quantize) and x_scales their E8M0 scales [N, H/32]."""
+    [N, H], e.g. from mx_quantize) and x_scales their E8M0 scales [N, H/32].
+    combine_comm_mode: 0 (each expert output row rounded to bf16 before the weighted sum,
+    MegaMoE's default) or 1 (a token's expert outputs summed in fp32, rounded once)."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
     if x_scales is not None and x_scales.shape[1] != x.shape[1] // 32:
@@ -319,7 +323,8 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
                    o=torch.empty((f, h), dtype=torch.float32, device=dev),
                    sorted_row_idx=torch.empty((f,), dtype=torch.int32, device=dev))
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn, dbg,
-                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype, x_scales)
+                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype, x_scales,
+                     combine_comm_mode)
     if stage_events is not None:
         if len(stage_events) != MEGA_STAGE_EVENTS:
             raise ValueError(f"stage_events needs {MEGA_STAGE_EVENTS} entries (events or None)")
@@ -341,10 +346,11 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
 def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=None,
                              quant_out_dtype: int = FP8_E4M3, weight_format: int = WEIGHTS_ND,
                              activation: int = ACT_SWIGLU, activation_params=(), weight_dtype: int = 0,
-                             shared_weight_dtype: int = 0) -> int:
+                             shared_weight_dtype: int = 0, combine_comm_mode: int = 0) -> int:
     lib = load()
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None,
-                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype)
+                     weight_format, activation, activation_params, weight_dtype, shared_weight_dtype,
+                     combine_comm_mode=combine_comm_mode)
     nbytes = ctypes.c_size_t()
     _check(lib.mega_moe_workspace_size(ctypes.byref(a), ctypes.byref(nbytes)))
     return nbytes.value

@@ -149,8 +149,12 @@ struct MegaWs {
   uint8_t* sx_sh;
   uint8_t* aq_sh;
   uint8_t* sa_sh;
-  float* o;       // fp32 [F, hidden] expert outputs (sorted rows) unless the caller's o
-  float* o_sh;    // fp32 [num_shared, tokens, hidden]
+  // expert outputs: fp32 (combine_comm_mode 1) or bf16 (mode 0) [F, hidden] in sorted
+  // rows unless the caller's o (fp32) is given, and [num_shared, tokens, hidden]
+  float* o;
+  uint16_t* o16;
+  float* o_sh;
+  uint16_t* o16_sh;
 };
 
 // Width of GMM1's activation output A (= GMM2's K): inter for the gated activations,
@@ -196,8 +200,12 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
     w.aq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, i));
     w.sa_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, i));
   }
-  w.o = a->o ? nullptr : cv.take<float>((size_t)flat * h);
-  w.o_sh = a->num_shared > 0 ? cv.take<float>((size_t)a->num_shared * n * h) : nullptr;
+  const bool rows16 = a->combine_comm_mode == 0;
+  w.o = (a->o || rows16) ? nullptr : cv.take<float>((size_t)flat * h);
+  w.o16 = (a->o || !rows16) ? nullptr : cv.take<uint16_t>((size_t)flat * h);
+  const size_t nsh = (size_t)a->num_shared * n * h;
+  w.o_sh = a->num_shared > 0 && !rows16 ? cv.take<float>(nsh) : nullptr;
+  w.o16_sh = a->num_shared > 0 && rows16 ? cv.take<uint16_t>(nsh) : nullptr;
   return w;
 }
 
@@ -289,6 +297,8 @@ moe_status check_mega(const moe_mega_args* a) {
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: x, topk_ids, topk_weights and y must be non-NULL");
   if (a->x_is_quantized != 0 && a->x_is_quantized != 1)
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: x_is_quantized must be 0 or 1");
+  if (a->combine_comm_mode != 0 && a->combine_comm_mode != 1)
+    return fail(MOE_ERR_UNSUPPORTED, "mega_moe: combine_comm_mode %d not 0 or 1 (one card)", a->combine_comm_mode);
   if (a->x_is_quantized && a->num_tokens > 0 && !a->x_scales)
     return fail(MOE_ERR_INVALID_ARG, "mega_moe: pre-quantized x needs x_scales");
   if (!a->x_is_quantized && a->x_scales)
@@ -654,6 +664,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   float* o = a->o ? a->o : w.o;
   moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles2, w.tile_count2, w.max_tiles2,
                      (int)h, (int)aw, fmt, w.tt2, o, packed, wfp4};
+  g2.o16 = o ? nullptr : w.o16;
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
@@ -668,16 +679,21 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm1 launch");
     moe::Gmm2Params s2{w.aq_sh, w.sa_sh, a->shared_w2 + (s * h * aw >> swfp4),
                        a->shared_w2_scales + s * group_scale_bytes(h, aw, a->weight_format), w.sh_tiles,
-                       w.sh_count, w.sh_max_tiles, (int)h, (int)aw, fmt, w.sh_tt, w.o_sh + s * n * h, packed,
-                       swfp4};
+                       w.sh_count, w.sh_max_tiles, (int)h, (int)aw, fmt, w.sh_tt,
+                       w.o_sh ? w.o_sh + s * n * h : nullptr, packed, swfp4};
+    s2.o16 = w.o16_sh ? w.o16_sh + s * n * h : nullptr;
     e = moe::launch_gmm2(s2, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared gmm2 launch");
   }
   if ((e = mark(5)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 4: weighted combine into bf16 y (one rounding, after the sum)
   moe::CombineParams cp;
-  cp.o = o; cp.pos = w.scat; cp.w = a->topk_weights; cp.w_bf16 = a->topk_weights_dtype == MOE_DTYPE_BF16;
-  cp.topk = (int)a->topk; cp.o_shared = w.o_sh; cp.num_shared = (int)a->num_shared; cp.tokens = n;
+  // combine_comm_mode 0: bf16 rows (rounded as read from the caller's fp32 o)
+  cp.o = o ? (const void*)o : (const void*)w.o16;
+  cp.o_fmt = a->combine_comm_mode == 0 ? (o ? 1 : 2) : 0;
+  cp.sh_bf16 = a->combine_comm_mode == 0;
+  cp.pos = w.scat; cp.w = a->topk_weights; cp.w_bf16 = a->topk_weights_dtype == MOE_DTYPE_BF16;
+  cp.topk = (int)a->topk; cp.o_shared = w.o_sh ? (const void*)w.o_sh : (const void*)w.o16_sh; cp.num_shared = (int)a->num_shared; cp.tokens = n;
   cp.hidden = (int)h; cp.y = reinterpret_cast<uint16_t*>(a->y);
   e = moe::launch_combine(cp, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe combine launch");

@@ -3,12 +3,16 @@
 // MegaMoE README, "A8W8-FP quantization scenario", stage 4: Y[i] = sum_k W[i, k] *
 // O[pi(i, k)], with pi the permutation of the routing (token i's k-th expert row), plus
 // the outputs of the shared experts, which see every token, unweighted; the
-// moe_token_permute article's unpermute direction is the same gather. The expert outputs
-// O are kept in fp32 and Y is rounded to bf16 once, after the sum.
+// moe_token_permute article's unpermute direction is the same gather. The sum is fp32
+// and Y is rounded to bf16 once, after it. MegaMoE's combineCommMode decides what the
+// combine receives: with mode 0 (no deduplication, the default) every expert's output
+// row arrives as BF16, so each O row is rounded to bf16 first (stored so by GMM2, or
+// rounded here as it is read); with mode 1 (a token's experts merged in FP32 on the
+// card) the rows stay fp32.
 //
-// Each thread owns 4 consecutive channels of one token (16-byte loads of the K expert
-// rows and the shared rows, summed in the order k = 0..K-1, then the shared experts in
-// order) and writes 8 bytes of bf16.
+// Each thread owns 4 consecutive channels of one token (16- or 8-byte loads of the K
+// expert rows and the shared rows, summed in the order k = 0..K-1, then the shared
+// experts in order) and writes 8 bytes of bf16.
 
 #include <algorithm>
 
@@ -22,12 +26,31 @@ __device__ __forceinline__ void fma4(float4& acc, float w, const float4& v) {
   acc.x += w * v.x; acc.y += w * v.y; acc.z += w * v.z; acc.w += w * v.w;
 }
 
+__device__ __forceinline__ float round_bf16(float v) { return bf16_to_f(f_to_bf16(v)); }
+
+// 4 consecutive channels (index c of 4) of a row: OF 0 fp32, 1 fp32 rounded to bf16,
+// 2 bf16.
+template <int OF>
+__device__ __forceinline__ float4 load4(const void* base, int64_t row, int hidden, int c) {
+  if constexpr (OF == 2) {
+    const uint2 u = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + row * hidden)[c];
+    return make_float4(bf16_to_f((uint16_t)u.x), bf16_to_f((uint16_t)(u.x >> 16)), bf16_to_f((uint16_t)u.y),
+                       bf16_to_f((uint16_t)(u.y >> 16)));
+  } else {
+    float4 v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + row * hidden)[c];
+    if constexpr (OF == 1) v = make_float4(round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w));
+    return v;
+  }
+}
+
 // Block b covers token b / slices and 1024 channels (256 threads x 4) of it, so that few
 // tokens still fill the chip. The K rows are loaded four at a time, all four loads in
 // flight before their products are added (in order k = 0..K-1).
-__global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ o, const int32_t* __restrict__ pos,
+// OF: format of the routed rows (see load4); SF: of the shared rows (0 fp32, 2 bf16).
+template <int OF, int SF>
+__global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o, const int32_t* __restrict__ pos,
                                                       const void* __restrict__ wts, int w_bf16, int topk,
-                                                      const float* __restrict__ o_shared, int num_shared,
+                                                      const void* __restrict__ o_shared, int num_shared,
                                                       int64_t tokens, int hidden, uint16_t* __restrict__ y) {
   const int h4 = hidden >> 2;
   const int slices = (h4 + 255) >> 8;
@@ -39,7 +62,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
     auto weight = [&](int64_t f) {
       return w_bf16 ? bf16_to_f(reinterpret_cast<const uint16_t*>(wts)[f]) : reinterpret_cast<const float*>(wts)[f];
     };
-    auto row = [&](int p) { return reinterpret_cast<const float4*>(o + (int64_t)p * hidden)[c]; };
+    auto row = [&](int p) { return load4<OF>(o, p, hidden, c); };
     float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
     int k = 0;
     for (; k + 4 <= topk; k += 4) {
@@ -60,7 +83,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ 
       if (p >= 0) fma4(acc, weight(f), row(p));
     }
     for (int s = 0; s < num_shared; ++s) {
-      const float4 v = reinterpret_cast<const float4*>(o_shared + ((int64_t)s * tokens + t) * hidden)[c];
+      const float4 v = load4<SF>(o_shared, (int64_t)s * tokens + t, hidden, c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
     uint2 out;
@@ -101,8 +124,10 @@ hipError_t launch_combine(const CombineParams& p, hipStream_t st) {
   if (p.tokens <= 0) return hipSuccess;
   const int64_t slices = ((p.hidden >> 2) + 255) >> 8;
   const unsigned grid = (unsigned)std::min<int64_t>(p.tokens * slices, 1 << 20);
-  combine_kernel<<<grid, 256, 0, st>>>(p.o, p.pos, p.w, p.w_bf16, p.topk, p.o_shared, p.num_shared, p.tokens,
-                                       p.hidden, p.y);
+  // routed rows fp32 (mode 1), fp32 rounded as read or bf16 (mode 0, shared rows bf16)
+  auto kern = p.o_fmt == 2 ? combine_kernel<2, 2> : p.o_fmt == 1 ? combine_kernel<1, 2> : combine_kernel<0, 0>;
+  if ((p.o_fmt != 0) != (p.sh_bf16 != 0)) return hipErrorInvalidValue;
+  kern<<<grid, 256, 0, st>>>(p.o, p.pos, p.w, p.w_bf16, p.topk, p.o_shared, p.num_shared, p.tokens, p.hidden, p.y);
   return hipGetLastError();
 }
 

@@ -540,16 +540,17 @@ void gmm1_swiglu_kernel(
 }
 
 // ---- GMM2 ---------------------------------------------------------------------------
-// O rows (fp32, sorted-row order) go out with plain stores; the weighted combine reads
-// them back per token (combine.hip). Combining here with fp32 atomics would send every
+// O rows (sorted-row order; fp32, or bf16 with OBF16: the rows the combine receives when
+// each expert's output is sent as BF16) go out with plain stores; the weighted combine
+// reads them back per token (combine.hip). Combining here with fp32 atomics would send every
 // add to memory: a token's K rows are computed on different XCDs, whose L2s are not
 // coherent, so device-scope atomics are not resolved in L2.
-template <int FMT, int NT, bool PACKED, int WF>
+template <int FMT, int NT, bool PACKED, int WF, bool OBF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
 void gmm2_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
-    int inter, float* __restrict__ o) {
+    int inter, float* __restrict__ o, uint16_t* __restrict__ o16) {
   extern __shared__ __align__(16) uint8_t lds[];
   // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -586,9 +587,14 @@ void gmm2_kernel(
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * t + 4 * g + i;
         if (rr >= nrows) continue;
-        float* orow = o + (int64_t)(srow0 + rr) * hidden + c0 + r;
+        const int64_t at = (int64_t)(srow0 + rr) * hidden + c0 + r;
+        if constexpr (OBF16) {
 #pragma unroll
-        for (int q = 0; q < 4; ++q) orow[16 * q] = acc[q][t][i];
+          for (int q = 0; q < 4; ++q) o16[at + 16 * q] = f_to_bf16(acc[q][t][i]);
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) o[at + 16 * q] = acc[q][t][i];
+        }
       }
     }
   }
@@ -700,13 +706,13 @@ hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   return hipGetLastError();
 }
 
-template <int FMT, int NT, bool PACKED, int WF>
+template <int FMT, int NT, bool PACKED, int WF, bool OBF16>
 hipError_t gmm2_go(const Gmm2Params& p, hipStream_t st) {
-  auto kern = gmm2_kernel<FMT, NT, PACKED, WF>;
+  auto kern = gmm2_kernel<FMT, NT, PACKED, WF, OBF16>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, kRing * StageLayout<NT>::kBufBytes, &ls);
   if (e != hipSuccess) return e;
-  kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.o);
+  kern<<<ls.grid, 256, ls.lds, st>>>(p.aq, p.sa, p.w, p.ws, p.tiles, p.tile_count, p.hidden, p.inter, p.o, p.o16);
   return hipGetLastError();
 }
 
@@ -733,15 +739,20 @@ hipError_t gmm1_nt(const Gmm1Params& p, hipStream_t st) {
   }
 }
 
+template <int FMT, bool PACKED, int WF, bool OBF16>
+hipError_t gmm2_tt(const Gmm2Params& p, hipStream_t st) {
+  switch (p.tt) {
+    case 1: return gmm2_go<FMT, 1, PACKED, WF, OBF16>(p, st);
+    case 2: return gmm2_go<FMT, 2, PACKED, WF, OBF16>(p, st);
+    case 4: return gmm2_go<FMT, 4, PACKED, WF, OBF16>(p, st);
+    case 8: return gmm2_go<FMT, 8, PACKED, WF, OBF16>(p, st);
+    default: return gmm2_go<FMT, 16, PACKED, WF, OBF16>(p, st);
+  }
+}
+
 template <int FMT, bool PACKED, int WF>
 hipError_t gmm2_nt(const Gmm2Params& p, hipStream_t st) {
-  switch (p.tt) {
-    case 1: return gmm2_go<FMT, 1, PACKED, WF>(p, st);
-    case 2: return gmm2_go<FMT, 2, PACKED, WF>(p, st);
-    case 4: return gmm2_go<FMT, 4, PACKED, WF>(p, st);
-    case 8: return gmm2_go<FMT, 8, PACKED, WF>(p, st);
-    default: return gmm2_go<FMT, 16, PACKED, WF>(p, st);
-  }
+  return p.o16 ? gmm2_tt<FMT, PACKED, WF, true>(p, st) : gmm2_tt<FMT, PACKED, WF, false>(p, st);
 }
 
 }  // namespace

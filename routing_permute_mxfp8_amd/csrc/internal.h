@@ -132,6 +132,7 @@ struct Gmm2Params {
   float* o;                                    // [rows, H] fp32, sorted rows
   int packed;
   int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, H, I/2]; fmt must be E4M3)
+  uint16_t* o16 = nullptr;                     // if set, O rows go here as bf16 (RNE) instead of o
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 
@@ -158,12 +159,14 @@ hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, 
 // O [rows, H] fp32 in sorted-row order, pos the scatter index (flat row -> sorted row,
 // -1 = none), w fp32 or bf16 [tokens * K], O_shared [num_shared][tokens, H] or null.
 struct CombineParams {
-  const float* o = nullptr;
+  const void* o = nullptr;         // expert output rows: fp32, or bf16 when o_fmt == 2
+  int o_fmt = 0;                   // 0 fp32, 1 fp32 rounded to bf16 as read, 2 bf16
+  int sh_bf16 = 0;                 // shared rows stored bf16 (else fp32)
   const int32_t* pos = nullptr;
   const void* w = nullptr;
   int w_bf16 = 0;
   int topk = 1;
-  const float* o_shared = nullptr;
+  const void* o_shared = nullptr;
   int num_shared = 0;
   int64_t tokens = 0;
   int hidden = 0;                  // multiple of 4

@@ -160,6 +160,14 @@ def test_mega_moe_validation(lib):
     assert status(weight_dtype=296) == 0 and status(weight_dtype=296, quant_out_dtype=23) == 4
     assert status(weight_dtype=23) == 4 and status(weight_dtype=7) == 3 and status(shared_weight_dtype=296) == 0
     assert status(topk_weights_dtype=1) == 3
+    assert status(combine_comm_mode=1) == 0 and status(combine_comm_mode=2) == 4 and status(combine_comm_mode=-1) == 4
+    # combineCommMode 0 keeps bf16 expert rows: half the O bytes of the fp32 merge (mode 1)
+    ws = {}
+    for mode in (0, 1):
+        b = ctypes.c_size_t()
+        assert lib.mega_moe_workspace_size(ctypes.byref(args(combine_comm_mode=mode)), ctypes.byref(b)) == 0
+        ws[mode] = b.value
+    assert ws[1] - ws[0] >= 8 * 2 * 256 * 2 - 256
     assert status(num_shared=5) == 2
     assert status(num_shared=1) == 1   # shared weights missing
     assert status(w2=None) == 1

@@ -86,6 +86,39 @@ def test_small_layers(case, wdtype, wf):
     assert mx <= 2e-2 and mean <= 5e-3
 
 
+@pytest.mark.parametrize("mode", [0, 1])
+def test_combine_comm_modes(mode):
+    """MegaMoE combineCommMode with every expert on the card: 0 rounds each expert output
+    row (routed and shared) to bf16 before the fp32 weighted sum, 1 sums fp32 rows; each
+    against the oracle's same mode. Y is the same bit for bit whether the fp32 o parity
+    output is requested (rows rounded as the combine reads them) or not (GMM2 stores
+    bf16 rows in mode 0)."""
+    cfg = moe_inputs.config("tiny", tokens=333, hidden=512, inter=256, experts=16, topk=4, shared=2, seed=46)
+    say(f"mega_moe combine_comm_mode {mode} N={cfg.tokens} H={cfg.hidden} E={cfg.experts} S={cfg.shared}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    weights = oracle_weights(cfg)
+    sh = oracle_weights(cfg, cfg.shared, shared=True)
+    wf = rp.WEIGHTS_PACKED
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf))
+    kw = dict(shared=tuple(device_weights(sh, wf)), quant_out_dtype=FP8[cfg.fmt], weight_format=wf,
+              combine_comm_mode=mode)
+    y_dbg, _, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y, etn = rp.mega_moe(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_dbg)
+    shared_np = [tuple(a[s] for a in sh) for s in range(cfg.shared)]
+    ref = moe.mega_moe(x_t.double().numpy(), ids, w, weights, cfg.fmt, cfg.experts, shared=shared_np,
+                       combine_comm_mode=mode)
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+    with pytest.raises(rp.MoeError):
+        rp.mega_moe(*args, **dict(kw, combine_comm_mode=2))
+
+
 ACTS = [("swiglu", (0.8,)), ("swiglustep", (0.6,)), ("swiglustep", ()), ("swigluoai", ()),
         ("swigluoai", (0.9, 1.2, 0.5)), ("situglu", (2.0,)), ("situglu", (1.5, 0.7)), ("situglu", ()),
         ("gelu", ()), ("gelu", (float(np.finfo(np.float32).max),))]

@@ -5,7 +5,9 @@ the same MX operands, a dense special case (one-hot input reproduces a weight
 row), and the per-token brute force (no permutation) which must equal the
 permuted layer bit for bit when the float64 GEMMs are exact.
 """
+import json
 import math
+import os
 
 import numpy as np
 import pytest
@@ -171,13 +173,14 @@ def test_float64_gemm_is_exact_on_small_shapes():
             assert got[i, n] == float(ints[i, n]) * scale
 
 
-def test_brute_force_equals_permuted_layer_bitwise():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_brute_force_equals_permuted_layer_bitwise(mode):
     cfg = moe_inputs.config("tiny", shared=1)
     x, ids, w = layer_inputs(cfg)
     weights = quantized_weights(cfg)
     shared = [tuple(a[0] for a in quantized_weights(cfg, 1, shared=True))]
-    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared)
-    bf = moe.per_token(x, ids, w, weights, cfg.fmt, range(cfg.tokens), shared=shared)
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared, combine_comm_mode=mode)
+    bf = moe.per_token(x, ids, w, weights, cfg.fmt, range(cfg.tokens), shared=shared, combine_comm_mode=mode)
     assert np.array_equal(full["y"], bf["y"])
     inv = routing.inverse(full["routing"]["sorted_row_idx"]).reshape(cfg.tokens, cfg.topk)
     for t in range(cfg.tokens):
@@ -188,14 +191,30 @@ def test_brute_force_equals_permuted_layer_bitwise():
     assert np.array_equal(full["y"], mxfp.bf16_round(full["y"]))
 
 
-def test_topk_one_unit_weight_is_plain_unpermute():
+@pytest.mark.parametrize("mode", [0, 1])
+def test_topk_one_unit_weight_is_plain_unpermute(mode):
+    """K = 1, w = 1, no shared expert: Y is the unpermuted O rounded to bf16 in both
+    combine modes (rounding a row to bf16 twice changes nothing)."""
     cfg = moe_inputs.config("tiny", topk=1)
     x, ids, _ = layer_inputs(cfg)
     weights = quantized_weights(cfg)
     w = np.ones((cfg.tokens, 1), np.float32)
-    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts)
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, combine_comm_mode=mode)
     inv = routing.inverse(full["routing"]["sorted_row_idx"])
     assert np.array_equal(full["y"], mxfp.bf16_round(full["o"][inv]))
+
+
+def test_combine_comm_mode_worked_example():
+    """MegaMoE combineCommMode: BF16 rows per expert (0) against one FP32 merge (1), on a
+    hand-derived two-expert example (tests/golden/combine_comm_mode.json)."""
+    g = json.load(open(os.path.join(os.path.dirname(__file__), "golden", "combine_comm_mode.json")))
+    o = np.array(g["expert_rows"], np.float64)[:, None]
+    w = np.array(g["topk_weights"], np.float64)
+    for mode, want in g["y"].items():
+        y = moe.combine(o, np.array([0, 1]), w, combine_comm_mode=int(mode))
+        assert y.shape == (1, 1) and y[0, 0] == want, (mode, y)
+    with pytest.raises(ValueError):
+        moe.combine(o, np.array([0, 1]), w, combine_comm_mode=2)
 
 
 def test_zero_gate_weights_leave_the_shared_expert():

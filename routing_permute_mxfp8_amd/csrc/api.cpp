@@ -100,7 +100,6 @@ bool valid_quant_mode(int q) {
 bool valid_x_dtype(int d) { return d == MOE_DTYPE_FP32 || d == MOE_DTYPE_FP16 || d == MOE_DTYPE_BF16; }
 
 int token_tile_tt(int64_t rows, int64_t groups) { return moe::gmm_token_tiles(rows, groups); }
-int gmm1_tile_tt(int64_t rows, int64_t groups) { return moe::gmm1_token_tiles(rows, groups); }
 
 // Scale bytes of one weight group (N output channels, K inputs) in a weight format.
 int64_t group_scale_bytes(int64_t n, int64_t k, int format) {
@@ -130,12 +129,9 @@ struct MegaWs {
   int32_t* gath;
   int32_t* row_token;
   float* row_weight;
-  int4* tiles;          // chunk list of GMM1 (and of the token tiling)
+  int4* tiles;
   int* tile_count;
   int max_tiles, tt;
-  int4* tiles2;         // chunk list of GMM2: the same list unless GMM1 takes longer chunks
-  int* tile_count2;
-  int max_tiles2, tt2;
   int4* sh_tiles;
   int* sh_count;
   int sh_max_tiles, sh_tt;
@@ -170,20 +166,10 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.gath = a->sorted_row_idx ? nullptr : cv.take<int32_t>(flat);
   w.row_token = cv.take<int32_t>(flat);
   w.row_weight = cv.take<float>(flat);
-  w.tt = gmm1_tile_tt(flat, e);
+  w.tt = token_tile_tt(flat, e);
   w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.tile_count = cv.take<int>(1);
-  w.tt2 = token_tile_tt(flat, e);
-  if (w.tt2 != w.tt) {
-    w.max_tiles2 = (int)(flat / (16 * w.tt2) + e + 1);
-    w.tiles2 = cv.take<int4>(w.max_tiles2);
-    w.tile_count2 = cv.take<int>(1);
-  } else {
-    w.max_tiles2 = w.max_tiles;
-    w.tiles2 = w.tiles;
-    w.tile_count2 = w.tile_count;
-  }
   const int64_t padded = moe::t16_padded_rows(flat, e);
   w.xq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, h));
   w.sx = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, h));
@@ -338,12 +324,10 @@ struct GmmWs {
   float* o;   // fp32 [rows, hidden] GMM2 output when the caller passes no o
 };
 
-// gmm1: chunks for GMM1 (possibly longer); the chunk list is sized for the GEMMs'
-// common (shorter) chunks, so one workspace size serves both stage entry points.
-GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_t inter, bool gmm1) {
+GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_t inter) {
   GmmWs w;
-  w.tt = gmm1 ? gmm1_tile_tt(rows, groups) : token_tile_tt(rows, groups);
-  w.max_tiles = (int)(rows / (16 * token_tile_tt(rows, groups)) + groups + 1);
+  w.tt = token_tile_tt(rows, groups);
+  w.max_tiles = (int)(rows / (16 * w.tt) + groups + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.count = cv.take<int>(1);
   const int64_t padded = moe::t16_padded_rows(rows, groups), kin = std::max(hidden, inter);
@@ -606,11 +590,6 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if (n == 0) return ok();
   e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt, w.max_tiles, w.tiles, w.tile_count, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
-  if (w.tiles2 != w.tiles) {
-    e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt2, w.max_tiles2, w.tiles2, w.tile_count2,
-                                st);
-    if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
-  }
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
   // of the shared experts)
@@ -662,8 +641,8 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if ((e = mark(3)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 3: GMM2, O rows in fp32
   float* o = a->o ? a->o : w.o;
-  moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles2, w.tile_count2, w.max_tiles2,
-                     (int)h, (int)aw, fmt, w.tt2, o, packed, wfp4};
+  moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
+                     (int)h, (int)aw, fmt, w.tt, o, packed, wfp4};
   g2.o16 = o ? nullptr : w.o16;
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
@@ -706,7 +685,7 @@ moe_status moe_gmm_workspace_size(int64_t rows, int64_t num_groups, int64_t hidd
   if (moe_status s = check_gmm_common("moe_gmm_workspace_size", rows, hidden, inter, num_groups, MOE_FP8_E4M3))
     return s;
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups, hidden, inter, false);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   *bytes = cv.off;
   return ok();
 }
@@ -722,11 +701,11 @@ moe_status moe_gmm1_swiglu_quant(const uint8_t* xq, const uint8_t* sx, int64_t r
   if (!group_offsets || !w1 || !w1_scales || (rows > 0 && (!xq || !sx || !aq || !sa)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups, hidden, inter, true);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
   if (rows == 0) return ok();
   Carver wc(workspace);
-  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter, true);
+  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");
@@ -754,11 +733,11 @@ moe_status moe_gmm2_combine(const uint8_t* aq, const uint8_t* sa, int64_t rows, 
   if (!group_offsets || !w2 || !w2_scales || (rows > 0 && (!aq || !sa || !row_token || !row_weight || !y_accum)))
     return fail(MOE_ERR_INVALID_ARG, "%s: NULL buffer", who);
   Carver cv(nullptr);
-  carve_gmm(cv, rows, num_groups, hidden, inter, false);
+  carve_gmm(cv, rows, num_groups, hidden, inter);
   if (moe_status s = check_ws(who, cv.off, workspace, workspace_bytes)) return s;
   if (rows == 0) return ok();
   Carver wc(workspace);
-  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter, false);
+  GmmWs w = carve_gmm(wc, rows, num_groups, hidden, inter);
   hipStream_t st = (hipStream_t)stream;
   hipError_t e = moe::launch_build_tiles(group_offsets, (int)num_groups, (int)rows, 16 * w.tt, w.max_tiles, w.tiles, w.count, st);
   if (e != hipSuccess) return hip_fail(e, "tile list launch");

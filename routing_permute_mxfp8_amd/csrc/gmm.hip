@@ -13,9 +13,9 @@
 // Design (one kernel per GEMM, persistent):
 // * Work item = (token chunk of one expert, channel block). A chunk holds up to 16*NT
 //   rows of one expert (device-built tile list, no host readback of the counts).
-// * Each wave owns 64 output channels (GMM1: 32 gate + the matching 32 up channels)
-//   and streams their weights from HBM straight into VGPRs exactly once per chunk, with
-//   a two-step register prefetch. The chunk's token rows are staged per K step into LDS
+// * Each wave owns 64 output channels (GMM1: 32 gate + the matching 32 up channels;
+//   GMM2 over 288-row chunks: 48) and streams their weights from HBM straight into VGPRs
+//   exactly once per chunk, with a one- or two-step register prefetch. The chunk's token rows are staged per K step into LDS
 //   (double-buffered, laid out exactly as the MFMA operand so every ds_read_b128 is
 //   conflict-free) and shared by the block's waves.
 // * V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the E8M0 scales applied by the matrix core.
@@ -173,19 +173,19 @@ __device__ __forceinline__ void block_barrier() {
 // with WPF = 1 the token tiles issued after step s's weights may: one fixed vmcnt.
 template <int NT> struct WeightPrefetch { static constexpr int value = NT >= 16 ? 1 : 2; };
 
-template <int NT, int WF>
+template <int NT, int WF, int QW>
 struct Batch {
-  static constexpr int kWeights = 4 * WeightFmt<WF>::kParts;
+  static constexpr int kWeights = QW * WeightFmt<WF>::kParts;
   static constexpr int kTokens = 3 * StageLayout<NT>::kPerWave;
   static constexpr int kLoads = kWeights + kTokens;
   static constexpr int kInFlight = WeightPrefetch<NT>::value == 2 ? kLoads : kTokens;
 };
 
-template <int NT, bool PACKED, int WF, int K_SLOT>
-__device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], const WPtr<PACKED> (&wp)[4], int wstep,
+template <int NT, bool PACKED, int WF, int QW, int K_SLOT>
+__device__ __forceinline__ void load_slot(v8i (&aload)[QW], int (&sload)[QW], const WPtr<PACKED> (&wp)[QW], int wstep,
                                           const uint8_t* tok, const uint8_t* toks, int ks, int row0, int ntt,
                                           int tstep, uint8_t* slot, int wave, int lane) {
-  constexpr int kW = Batch<NT, WF>::kWeights;
+  constexpr int kW = Batch<NT, WF, QW>::kWeights;
   if constexpr (K_SLOT < kW) {
     constexpr int kParts = WeightFmt<WF>::kParts;
     constexpr int q = K_SLOT / kParts, part = K_SLOT % kParts;
@@ -220,12 +220,12 @@ __device__ __forceinline__ void load_slot(v8i (&aload)[4], int (&sload)[4], cons
   }
 }
 
-template <int NT, bool PACKED, int WF, int K0, int... I>
-__device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i (&aload)[4], int (&sload)[4],
-                                           const WPtr<PACKED> (&wp)[4], int wstep, const uint8_t* tok,
+template <int NT, bool PACKED, int WF, int QW, int K0, int... I>
+__device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i (&aload)[QW], int (&sload)[QW],
+                                           const WPtr<PACKED> (&wp)[QW], int wstep, const uint8_t* tok,
                                            const uint8_t* toks, int ks, int row0, int ntt, int tstep, uint8_t* slot,
                                            int wave, int lane) {
-  (load_slot<NT, PACKED, WF, K0 + I>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane), ...);
+  (load_slot<NT, PACKED, WF, QW, K0 + I>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane), ...);
 }
 
 // One K step s, with its weights in (acur, scur) and its token tiles in ring slot
@@ -247,24 +247,24 @@ __device__ __forceinline__ void load_slots(std::integer_sequence<int, I...>, v8i
 // fences keep them there); loads that do not fit, and all loads of small chunks, go
 // first.
 // WEIGHTS_A: weights in the MFMA A slot (GMM1), else tokens in the A slot (GMM2).
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
-__device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4],
-                                       const v8i (&acur)[4], const int (&scur)[4], v8i (&aload)[4],
-                                       int (&sload)[4], const uint8_t* tok, const uint8_t* toks, int row0, int ntt,
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
+__device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW],
+                                       const v8i (&acur)[QW], const int (&scur)[QW], v8i (&aload)[QW],
+                                       int (&sload)[QW], const uint8_t* tok, const uint8_t* toks, int row0, int ntt,
                                        uint8_t* lds, int wave, int lane) {
-  constexpr int kLoads = Batch<NT, WF>::kLoads;
-  constexpr int kTop = NT < 4 ? kLoads : (kLoads > 4 * NT ? kLoads - 4 * NT : 0);
+  constexpr int kLoads = Batch<NT, WF, QW>::kLoads;
+  constexpr int kTop = NT < 4 ? kLoads : (kLoads > QW * NT ? kLoads - QW * NT : 0);
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
-  wait_vmcnt<Batch<NT, WF>::kInFlight>();
+  wait_vmcnt<Batch<NT, WF, QW>::kInFlight>();
   block_barrier<NT>();
   const int wstep = min(s + WeightPrefetch<NT>::value, ks - 1), tstep = min(s + 2, ks - 1);
   uint8_t* slot = lds + (cur == 0 ? 2 : cur - 1) * kBuf;   // (cur + 2) % 3
   const uint8_t* buf = lds + cur * kBuf;
-  load_slots<NT, PACKED, WF, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
+  load_slots<NT, PACKED, WF, QW, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
                             ntt, tstep, slot, wave, lane);
-  int sw[4];
+  int sw[QW];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) sw[q] = weight_scale<PACKED>(scur[q], s, lane);
+  for (int q = 0; q < QW; ++q) sw[q] = weight_scale<PACKED>(scur[q], s, lane);
   v8i b[2];
   int sb[2];
   stage_read<NT>(buf, 0, s, lane, b[0], sb[0]);
@@ -279,13 +279,13 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT]
             acc[q][t] = mfma_mx16_ab<WF, FMT>(acur[q], b[t & 1], acc[q][t], sw[q], sb[t & 1]);
           else
             acc[q][t] = mfma_mx16_ab<FMT, WF>(b[t & 1], acur[q], acc[q][t], sb[t & 1], sw[q]);
-          constexpr int k = kTop + 4 * t + q;
+          constexpr int k = kTop + QW * t + q;
           if constexpr (k < kLoads) {
-            load_slot<NT, PACKED, WF, k>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane);
+            load_slot<NT, PACKED, WF, QW, k>(aload, sload, wp, wstep, tok, toks, ks, row0, ntt, tstep, slot, wave, lane);
             __builtin_amdgcn_sched_barrier(0);
           }
         }(), ...);
-      }(std::make_integer_sequence<int, 4>{});
+      }(std::make_integer_sequence<int, QW>{});
     }(), ...);
   }(std::make_integer_sequence<int, NT>{});
 }
@@ -299,43 +299,43 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[4][NT]
 // register allocator permutes the accumulators across the loop body instead.) At the
 // end every load has landed and every wave is past its last LDS read, so the next
 // chunk may reuse the ring.
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
-__device__ __forceinline__ void k_loop_pf2(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
+__device__ __forceinline__ void k_loop_pf2(v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                        int lane) {
-  constexpr int kL = Batch<NT, WF>::kLoads;
+  constexpr int kL = Batch<NT, WF, QW>::kLoads;
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   const int ks = K >> 7, r = ks % 3, s1 = min(1, ks - 1);
-  v8i a0[4], a1[4], a2[4];
-  int c0[4], c1[4], c2[4];
+  v8i a0[QW], a1[QW], a2[QW];
+  int c0[QW], c1[QW], c2[QW];
   auto seq = std::make_integer_sequence<int, kL>{};
   if (r == 0) {
-    load_slots<NT, PACKED, WF, 0>(seq, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, WF, 0>(seq, a1, c1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a1, c1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   } else if (r == 1) {
-    load_slots<NT, PACKED, WF, 0>(seq, a2, c2, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, WF, 0>(seq, a0, c0, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a2, c2, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a0, c0, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   } else {
-    load_slots<NT, PACKED, WF, 0>(seq, a1, c1, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
-    load_slots<NT, PACKED, WF, 0>(seq, a2, c2, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a1, c1, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, QW, 0>(seq, a2, c2, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave, lane);
   }
   int s = 0, cur = 0;
   if (r == 1) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     s = 1;
     cur = 1;
   } else if (r == 2) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     s = 2;
     cur = 2;
   }
   for (; s < ks; s += 3) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s, ks, cur, acc, wp, a0, c0, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s, ks, cur, acc, wp, a0, c0, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   wait_vmcnt<0>();
@@ -346,24 +346,24 @@ __device__ __forceinline__ void k_loop_pf2(v4f (&acc)[4][NT], const WPtr<PACKED>
 // 1 first; if ks is odd, step 0 alone (its weight buffers then swap by copies); then
 // the steps two at a time (the two weight buffers alternate, roles fixed in the
 // unrolled body). Then as above.
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
-__device__ __forceinline__ void k_loop_pf1(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
+__device__ __forceinline__ void k_loop_pf1(v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW], const uint8_t* tok,
                                            const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                            int lane) {
-  constexpr int kW = Batch<NT, WF>::kWeights, kT = Batch<NT, WF>::kTokens;
+  constexpr int kW = Batch<NT, WF, QW>::kWeights, kT = Batch<NT, WF, QW>::kTokens;
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   const int ks = K >> 7;
-  v8i a0[4], a1[4];
-  int c0[4], c1[4];
-  load_slots<NT, PACKED, WF, 0>(std::make_integer_sequence<int, kW + kT>{}, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0,
+  v8i a0[QW], a1[QW];
+  int c0[QW], c1[QW];
+  load_slots<NT, PACKED, WF, QW, 0>(std::make_integer_sequence<int, kW + kT>{}, a0, c0, wp, 0, tok, toks, ks, row0, ntt, 0,
                             lds, wave, lane);
-  load_slots<NT, PACKED, WF, kW>(std::make_integer_sequence<int, kT>{}, a1, c1, wp, 0, tok, toks, ks, row0, ntt,
+  load_slots<NT, PACKED, WF, QW, kW>(std::make_integer_sequence<int, kT>{}, a1, c1, wp, 0, tok, toks, ks, row0, ntt,
                              min(1, ks - 1), lds + kBuf, wave, lane);
   int s = 0, cur = 0;
   if (ks & 1) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(0, ks, 0, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < QW; ++q) {
       a0[q] = a1[q];
       c0[q] = c1[q];
     }
@@ -371,23 +371,23 @@ __device__ __forceinline__ void k_loop_pf1(v4f (&acc)[4][NT], const WPtr<PACKED>
     cur = 1;
   }
   for (; s < ks; s += 2) {
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s, ks, cur, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s, ks, cur, acc, wp, a0, c0, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
-    k_step<FMT, NT, PACKED, WEIGHTS_A, WF>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
     cur = cur == 2 ? 0 : cur + 1;
   }
   wait_vmcnt<0>();
   __syncthreads();
 }
 
-template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF>
-__device__ __forceinline__ void k_loop(v4f (&acc)[4][NT], const WPtr<PACKED> (&wp)[4], const uint8_t* tok,
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
+__device__ __forceinline__ void k_loop(v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                        int lane) {
   if constexpr (WeightPrefetch<NT>::value == 2)
-    k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A, WF>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+    k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
   else
-    k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A, WF>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+    k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
 }
 
 // Occupancy targets: small token chunks (decode) want several waves per SIMD to keep
@@ -490,7 +490,7 @@ void gmm1_swiglu_kernel(
     for (int q = 0; q < 4; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, true, WF>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, true, WF, 4>(acc, wp, xq, sx, hidden, row0, ntt, lds, wave, lane);
 
     // A^ goes out in the tiled layout with K = inter (2 inter for gelu), where this
     // block's 128 gate channels are exactly K step cb: the wave's 32 channels are half
@@ -545,18 +545,24 @@ void gmm1_swiglu_kernel(
 // reads them back per token (combine.hip). Combining here with fp32 atomics would send every
 // add to memory: a token's K rows are computed on different XCDs, whose L2s are not
 // coherent, so device-scope atomics are not resolved in L2.
+// QW 16-channel weight tiles per wave: 4 (256 channels a block), or 3 with 288-row
+// chunks (192 channels a block), whose 3 x 18 accumulator tiles fit the accumulation
+// registers (4 x 18 do not).
+template <int NT> struct Gmm2Tiles { static constexpr int value = NT == 18 ? 3 : 4; };
+
 template <int FMT, int NT, bool PACKED, int WF, bool OBF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))
 void gmm2_kernel(
     const uint8_t* __restrict__ aq, const uint8_t* __restrict__ sa, const uint8_t* __restrict__ w,
     const uint8_t* __restrict__ ws, const int4* __restrict__ tiles, const int* __restrict__ tile_count, int hidden,
     int inter, float* __restrict__ o, uint16_t* __restrict__ o16) {
+  constexpr int QW = Gmm2Tiles<NT>::value;
   extern __shared__ __align__(16) uint8_t lds[];
   // wave index as a scalar: every per-wave address (LDS slots, tiles) stays in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int g = lane >> 4, r = lane & 15;
-  const int ncb = (hidden + 255) >> 8;        // 256 channels per block (64 per wave)
   const int n16 = hidden >> 4;
+  const int ncb = (n16 + 4 * QW - 1) / (4 * QW);   // 64 QW channels per block (16 QW per wave)
   int it, stride, last;
   block_items(*tile_count * ncb, &it, &stride, &last);
   for (; it < last; it += stride) {
@@ -564,36 +570,40 @@ void gmm2_kernel(
     const int4 tile = tiles[j];
     const int e = tile.x, row0 = tile.y, nrows = tile.z, srow0 = tile.w;
     const int ntt = (nrows + 15) >> 4;
-    const int c0 = cb * 256 + wave * 64;
-    // hidden % 256 == 128: the last block's upper waves have no channels; they still
-    // stage tokens and meet the barriers, reading a valid tile, and skip the epilogue.
-    const bool wave_on = c0 < hidden;
-    const int c0w = wave_on ? c0 : 0;
-    WPtr<PACKED> wp[4];
+    // This wave's first 16-channel tile. In the last block, tiles past hidden take the
+    // last tile's weights (in bounds; the wave still stages tokens and meets the
+    // barriers) and are not stored; with QW = 4 (hidden % 256 == 128) a whole wave is off.
+    const int t0 = (cb * 4 + wave) * QW;
+    const int nq = min(QW, n16 - t0);            // tiles of this wave inside hidden (may be <= 0)
+    WPtr<PACKED> wp[QW];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) wp[q] = weight_tile<PACKED, WF>(w, ws, (int64_t)e * n16 + (c0w >> 4) + q, inter, lane);
-    v4f acc[4][NT];
+    for (int q = 0; q < QW; ++q) {
+      const int tq = QW == 4 ? (nq > 0 ? t0 : 0) + q : min(t0 + q, n16 - 1);
+      wp[q] = weight_tile<PACKED, WF>(w, ws, (int64_t)e * n16 + tq, inter, lane);
+    }
+    v4f acc[QW][NT];
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
+    for (int q = 0; q < QW; ++q)
 #pragma unroll
       for (int t = 0; t < NT; ++t) acc[q][t] = v4f{0.f, 0.f, 0.f, 0.f};
-    k_loop<FMT, NT, PACKED, false, WF>(acc, wp, aq, sa, inter, row0, ntt, lds, wave, lane);
+    k_loop<FMT, NT, PACKED, false, WF, QW>(acc, wp, aq, sa, inter, row0, ntt, lds, wave, lane);
 
-    // acc[q][t][i] = O[token row 16t + 4g + i][channel c0 + 16q + r]
+    // acc[q][t][i] = O[token row 16t + 4g + i][channel 16 (t0 + q) + r]
 #pragma unroll
     for (int t = 0; t < NT; ++t) {
-      if (t >= ntt || !wave_on) continue;
+      if (t >= ntt || nq <= 0) continue;
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int rr = 16 * t + 4 * g + i;
         if (rr >= nrows) continue;
-        const int64_t at = (int64_t)(srow0 + rr) * hidden + c0 + r;
-        if constexpr (OBF16) {
+        const int64_t at = (int64_t)(srow0 + rr) * hidden + 16 * t0 + r;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) o16[at + 16 * q] = f_to_bf16(acc[q][t][i]);
-        } else {
-#pragma unroll
-          for (int q = 0; q < 4; ++q) o[at + 16 * q] = acc[q][t][i];
+        for (int q = 0; q < QW; ++q) {
+          if (QW != 4 && q >= nq) continue;      // QW = 4: a wave is all on or all off
+          if constexpr (OBF16)
+            o16[at + 16 * q] = f_to_bf16(acc[q][t][i]);
+          else
+            o[at + 16 * q] = acc[q][t][i];
         }
       }
     }
@@ -746,6 +756,7 @@ hipError_t gmm2_tt(const Gmm2Params& p, hipStream_t st) {
     case 2: return gmm2_go<FMT, 2, PACKED, WF, OBF16>(p, st);
     case 4: return gmm2_go<FMT, 4, PACKED, WF, OBF16>(p, st);
     case 8: return gmm2_go<FMT, 8, PACKED, WF, OBF16>(p, st);
+    case 18: return gmm2_go<FMT, 18, PACKED, WF, OBF16>(p, st);
     default: return gmm2_go<FMT, 16, PACKED, WF, OBF16>(p, st);
   }
 }
@@ -763,18 +774,12 @@ int gmm_token_tiles(int64_t rows, int64_t groups) {
   if (avg <= 32.0) return 2;
   if (avg <= 64.0) return 4;
   if (avg <= 128.0) return 8;
-  return 16;
-}
-
-// GMM1 over many groups of 240-288 rows (a prefill-shaped layer: 256 +- 16 rows per
-// expert) takes 288-row chunks: almost every expert is then one chunk, so its weights
-// are streamed once instead of twice for the experts just above 256 rows (the 288
-// accumulators per lane cost some moves between accumulation and vector registers,
-// which GMM1 hides behind its weight stream and GMM2 does not).
-int gmm1_token_tiles(int64_t rows, int64_t groups) {
-  const double avg = groups > 0 ? (double)rows / (double)groups : (double)rows;
+  // Many groups of 240-288 rows (a prefill-shaped layer: 256 +- 16 rows per expert):
+  // 288-row chunks, so that almost every expert is one chunk and its weights are
+  // streamed once instead of twice for the experts just above 256 rows (GMM1 keeps 64
+  // channels a wave with 288 accumulators per lane, GMM2 takes 48 channels a wave).
   if (groups > 1 && avg > 240.0 && avg <= 288.0) return 18;
-  return gmm_token_tiles(rows, groups);
+  return 16;
 }
 
 // MXFP4 weights (the pages' A8W4-FP scenario) pair with E4M3 tokens only.

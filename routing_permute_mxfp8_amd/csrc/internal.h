@@ -115,7 +115,7 @@ struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
   const int4* tiles; const int* tile_count; int max_tiles;
-  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16; GMM1 also 18)
+  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16, 18)
   uint8_t* aq; uint8_t* sa;                    // tiled [padded rows, I] (2I for gelu)
   float* h1;                                   // nullable [rows, 2I]
   int packed;                                  // weights in the MFMA-native packed layout
@@ -138,8 +138,6 @@ hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 
 // Token tiles (16 rows each) per chunk for `rows` rows over `groups` groups.
 int gmm_token_tiles(int64_t rows, int64_t groups);
-// Token tiles per chunk of GMM1: gmm_token_tiles, or 18 for many groups of 240-288 rows.
-int gmm1_token_tiles(int64_t rows, int64_t groups);
 
 // codes [G, N, K] + scales [G, N, K/32] -> MFMA-native packed codes (same size) and
 // packed scales [G, N/16, ceil(K/512), 64, 4].

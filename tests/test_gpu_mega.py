@@ -27,7 +27,7 @@ SMALL = [
     dict(name="tiny", tokens=333, hidden=512, inter=256, experts=16, topk=4, shared=2, seed=42),
     dict(name="skewed", tokens=500, hidden=384, inter=384, experts=20, topk=5, seed=43),
     dict(name="tiny", tokens=5, hidden=256, inter=128, experts=32, topk=8, seed=44),
-    # ~256 rows per expert: GMM1 in 288-row chunks, GMM2 in 256-row chunks of a second list
+    # ~256 rows per expert: both GEMMs in 288-row chunks (GMM2 with 48 channels a wave, a partial last block)
     dict(name="tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, shared=1, seed=45),
 ]
 
@@ -130,7 +130,7 @@ ACT_KIND = {"swiglu": rp.ACT_SWIGLU, "swiglustep": rp.ACT_SWIGLUSTEP, "swigluoai
 @pytest.mark.parametrize("tt", ["small", "wide", "long"])
 def test_activations(kind, params, tt):
     """MegaMoE "Activation function formulas": every activation and parameter list, routed
-    and shared experts, in 1-tile (small), 16-tile (wide) and GMM1's 18-tile (long) chunks;
+    and shared experts, in 1-tile (small), 16-tile (wide) and 18-tile (long) chunks;
     clamps that bite."""
     if tt == "small":
         cfg = moe_inputs.config("tiny", tokens=96, hidden=256, inter=256, experts=8, topk=2, shared=1, seed=47)

@@ -135,6 +135,10 @@ struct MegaWs {
   int4* sh_tiles;
   int* sh_count;
   int sh_max_tiles, sh_tt;
+  // x quantized once in token order (row-major codes [tokens, hidden] and scales
+  // [tokens, hidden/32]) when the gather re-reads many x rows; else null
+  uint8_t* xrow;
+  uint8_t* xrow_s;
   // token operands in the tiled layout: routed rows (padded per expert) and the
   // token-order rows of the shared experts
   uint8_t* xq;
@@ -157,6 +161,15 @@ struct MegaWs {
 // 2 * inter for gelu ([MM] "Activation function formulas", gelu).
 int64_t act_width(const moe_mega_args* a) { return a->activation == MOE_ACT_GELU ? 2 * a->inter : a->inter; }
 
+// Stage 1 in two passes (MX-quantize every token once, then gather its codes into the
+// tiled layout) when topk >= 3 rows per token and x is large: the gather then reads one
+// byte per element of each destination row instead of the two of bf16 x, and the shared
+// experts' token-order operand is the same codes. Small layers keep the one-pass gather
+// (one launch fewer). Q_MX is row-local, so both give the same bytes.
+bool quantize_first(const moe_mega_args* a) {
+  return !a->x_is_quantized && a->topk >= 3 && a->num_tokens * a->hidden >= (int64_t)1 << 22;
+}
+
 MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   MegaWs w{};
   const int64_t n = a->num_tokens, h = a->hidden, i = act_width(a), e = a->num_experts;
@@ -170,6 +183,10 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.tile_count = cv.take<int>(1);
+  if (quantize_first(a)) {
+    w.xrow = cv.take<uint8_t>((size_t)(n * h));
+    w.xrow_s = cv.take<uint8_t>((size_t)(n * (h / 32)));
+  }
   const int64_t padded = moe::t16_padded_rows(flat, e);
   w.xq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, h));
   w.sx = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, h));
@@ -595,8 +612,20 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   // of the shared experts)
   // (pre-quantized x: the codes and scales are gathered as they are, [MM] dispatchQuantMode 0)
   const uint8_t* xcodes = static_cast<const uint8_t*>(a->x);
-  if (a->x_is_quantized) {
-    e = moe::launch_pack_tokens(xcodes, a->x_scales, (int)h, w.tiles, w.tile_count, w.max_tiles, w.tt, w.xq, w.sx,
+  const uint8_t* xscales = a->x_scales;
+  bool codes_in = a->x_is_quantized != 0;
+  if (w.xrow) {
+    moe::PermuteParams q;
+    q.x = a->x; q.in_dtype = MOE_DTYPE_BF16; q.n = n; q.hidden = h; q.topk = 1; q.scat = nullptr; q.m_limit = n;
+    q.quant = fmt; q.out = w.xrow; q.out_scales = w.xrow_s; q.scale_cols = h / 32;
+    e = moe::launch_permute(q, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe token quantization launch");
+    xcodes = w.xrow;
+    xscales = w.xrow_s;
+    codes_in = true;
+  }
+  if (codes_in) {
+    e = moe::launch_pack_tokens(xcodes, xscales, (int)h, w.tiles, w.tile_count, w.max_tiles, w.tt, w.xq, w.sx,
                                 st, w.row_token);
   } else {
     moe::PermuteTilesParams pt;
@@ -609,8 +638,8 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if (a->num_shared > 0) {
     e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
-    if (a->x_is_quantized) {
-      e = moe::launch_pack_tokens(xcodes, a->x_scales, (int)h, w.sh_tiles, w.sh_count, w.sh_max_tiles, w.sh_tt,
+    if (codes_in) {
+      e = moe::launch_pack_tokens(xcodes, xscales, (int)h, w.sh_tiles, w.sh_count, w.sh_max_tiles, w.sh_tt,
                                   w.xq_sh, w.sx_sh, st);
     } else {
       moe::PermuteTilesParams ps;

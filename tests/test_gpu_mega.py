@@ -119,6 +119,32 @@ def test_combine_comm_modes(mode):
         rp.mega_moe(*args, **dict(kw, combine_comm_mode=2))
 
 
+def test_stage1_quantize_then_gather():
+    """A layer large enough (topk >= 3, tokens x hidden >= 2^22) for stage 1 to quantize
+    each token once and then gather codes (routed rows and the shared expert's token-order
+    rows): the gathered X^ / S_X bit for bit and Y against the oracle."""
+    cfg = moe_inputs.config("tiny", tokens=1024, hidden=4096, inter=128, experts=16, topk=4, shared=1, seed=55)
+    say(f"mega_moe two-pass stage 1 N={cfg.tokens} H={cfg.hidden} E={cfg.experts} K={cfg.topk}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    weights = oracle_weights(cfg)
+    sh = oracle_weights(cfg, cfg.shared, shared=True)
+    wf = rp.WEIGHTS_PACKED
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf),
+                              shared=tuple(device_weights(sh, wf)), quant_out_dtype=FP8[cfg.fmt], debug=True,
+                              weight_format=wf)
+    torch.cuda.synchronize()
+    ref = moe.mega_moe(x_t.double().numpy(), ids, w, weights, cfg.fmt, cfg.experts,
+                       shared=[tuple(a[0] for a in sh)])
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    assert np.array_equal(dbg["sx"].cpu().numpy(), ref["sx"])
+    assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
 ACTS = [("swiglu", (0.8,)), ("swiglustep", (0.6,)), ("swiglustep", ()), ("swigluoai", ()),
         ("swigluoai", (0.9, 1.2, 0.5)), ("situglu", (2.0,)), ("situglu", (1.5, 0.7)), ("situglu", ()),
         ("gelu", ()), ("gelu", (float(np.finfo(np.float32).max),))]

@@ -413,8 +413,8 @@ def main():
                     help="only run a plain 1 GiB device copy --steps times (counter calibration)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}): this build has no multi-GPU path; "
-              "expert-parallel sharding is described in DESIGN.md", file=sys.stderr)
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}): the library has no multi-GPU "
+              "path (the layer would shard by experts, one expert range per GPU)", file=sys.stderr)
         sys.exit(2)
     import torch
     if args.calibrate_copy:

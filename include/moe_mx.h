@@ -56,7 +56,10 @@ typedef enum {
 
 /* Element dtypes of activation buffers. */
 enum { MOE_DTYPE_FP32 = 0, MOE_DTYPE_FP16 = 1, MOE_DTYPE_BF16 = 2,
-       MOE_DTYPE_INT32 = 3, MOE_DTYPE_INT64 = 4 };
+       MOE_DTYPE_INT32 = 3, MOE_DTYPE_INT64 = 4,
+       /* MX codes (moe_init_routing x only): one byte per FP8 element, two FP4    */
+       /* elements per byte (element 2j in the low nibble)                          */
+       MOE_DTYPE_FP8_E5M2 = 5, MOE_DTYPE_FP8_E4M3 = 6, MOE_DTYPE_FP4_E2M1 = 7 };
 
 /* quantMode values of [V3] / quant_mode of [TP]: -1 none, 2 MXFP8 E5M2, 3 MXFP8 E4M3FN, */
 /* 9 MXFP4 E2M1. MXFP4 codes are stored two per byte: element 2j in the low nibble,   */
@@ -130,7 +133,14 @@ moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 /* ------------------------------------------------------------------------ */
 /* moe_init_routing  ([V3] 计算公式 1-6, dropless mode).                      */
 /*   x            device, [num_rows, hidden] of x_dtype (BF16, FP16; FP32 too  */
-/*                when quant_mode = -1)                                        */
+/*                when quant_mode = -1), or MX codes (MOE_DTYPE_FP8_E5M2,       */
+/*                _FP8_E4M3: [num_rows, hidden] bytes; _FP4_E2M1: [num_rows,    */
+/*                hidden/2] bytes, hidden even) with quant_mode = -1: the rows  */
+/*                are gathered as they are ([V3] quantMode -1 with an FP8/FP4 x) */
+/*   scale        device or NULL ([V3] scaleOptional): only with x of MX codes,  */
+/*                their E8M0 scales [num_rows, moe_mx_scale_cols(hidden)]       */
+/*                (hidden % 32 == 0); expanded_scale then receives the gathered */
+/*                scale rows (expandedScaleOut). Any other use: an error.       */
 /*   expert_idx   device, int32 [num_rows, k]; flat row r = t*k + j            */
 /*   expert_num   number of experts E, 1..MOE_MAX_EXPERTS                      */
 /*   active_start, active_end  activeExpertRange [s, e), 0 <= s <= e <= E     */
@@ -142,8 +152,9 @@ moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 /*                     Q(x[src(i) / k]) where src(i) is the flat row at position */
 /*                     i of the stable expert-major order restricted to [s, e);  */
 /*                     FP8 codes in MX modes (packed MXFP4, hidden / 2 bytes a  */
-/*                     row, in mode 9), x_dtype values otherwise. Rows           */
-/*                     >= availableIdxNum are not written.                      */
+/*                     row, in mode 9), x_dtype values otherwise (x's code rows */
+/*                     when x holds MX codes). Rows >= availableIdxNum are not  */
+/*                     written.                                                 */
 /*   expanded_row_idx  int32 [num_rows*k]. Scatter type: entry r = position of   */
 /*                     flat row r in expanded_x, or -1 if its expert is outside  */
 /*                     [s, e). Gather type: entry i < availableIdxNum = src(i),  */
@@ -154,13 +165,13 @@ moe_status moe_mx_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 /*                     [s, e) with a non-zero count, ascending, then zero rows   */
 /*                     (the pages leave those rows open)                        */
 /*   expanded_scale    uint8 [num_rows*k, moe_mx_scale_cols(hidden)] in MX modes  */
-/*                     (NULL allowed when quant_mode = -1)                       */
+/*                     and with a scale input (NULL allowed otherwise)          */
 /*   available_idx_num int64 [1]: #{r : s <= expert_idx[r] < e}                 */
 /* Ties between equal experts keep ascending flat row (stable sort).            */
 /* ------------------------------------------------------------------------ */
 moe_status moe_init_routing_workspace_size(int64_t num_rows, int64_t k, int64_t expert_num,
                                            size_t* bytes /* host out */);
-moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_t hidden,
+moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows, int64_t hidden,
                             const int32_t* expert_idx, int64_t k, int64_t expert_num,
                             int64_t active_start, int64_t active_end, int quant_mode,
                             int row_idx_type, int expert_tokens_num_type, void* expanded_x,

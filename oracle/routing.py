@@ -145,6 +145,19 @@ def gather_rows(x, sorted_row_idx, topk: int, quant_mode: int, start: int = 0, c
     return codes, scales
 
 
+def gather_passthrough(codes, scales, sorted_row_idx, topk: int, start: int = 0, count=None):
+    """MoeInitRoutingV3 with quantMode -1 and an x already holding MX codes (FLOAT8_E4M3FN,
+    FLOAT8_E5M2 or FLOAT4_E2M1 bytes) and, optionally, their FLOAT8_E8M0 scales
+    (scaleOptional): expandedX[i] = codes[sortedRowIdx[start + i] // K] and
+    expandedScaleOut[i] = scales[sortedRowIdx[start + i] // K], the rows taken as they are.
+    Returns (code rows, scale rows or None)."""
+    codes = np.asarray(codes, dtype=np.uint8)
+    if count is None:
+        count = sorted_row_idx.size - start
+    src = sorted_row_idx[start:start + count] // topk
+    return codes[src], None if scales is None else np.asarray(scales, dtype=np.uint8)[src]
+
+
 def actual_num_out_tokens(flat: int, num_out_tokens) -> int:
     """moe_token_permute 参数说明: None or 0 -> F; > 0 -> min(n, F); < 0 -> max(F + n, 0)."""
     if num_out_tokens is None or num_out_tokens == 0:

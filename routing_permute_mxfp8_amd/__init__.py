@@ -24,13 +24,15 @@ __all__ = [
     "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "QUANT_MXFP4", "FP8_E5M2", "FP8_E4M3",
     "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "token_permute",
     "mega_moe", "mega_moe_workspace_bytes", "gmm1_swiglu_quant", "gmm2_combine", "combine_finalize",
-    "pack_weights", "WEIGHTS_ND", "WEIGHTS_PACKED",
+    "pack_weights", "WEIGHTS_ND", "WEIGHTS_PACKED", "DTYPE_FP8_E5M2", "DTYPE_FP8_E4M3", "DTYPE_FP4_E2M1",
 ]
 
 QUANT_NONE, QUANT_E5M2, QUANT_E4M3, QUANT_MXFP4 = -1, 2, 3, 9
 FP8_E5M2, FP8_E4M3 = 23, 24
 WEIGHTS_ND, WEIGHTS_PACKED = 0, 1
 _DT = {torch.float32: 0, torch.float16: 1, torch.bfloat16: 2, torch.int32: 3, torch.int64: 4}
+# x dtypes of MX codes for init_routing's pass-through (one FP8 code a byte, two FP4 codes a byte)
+DTYPE_FP8_E5M2, DTYPE_FP8_E4M3, DTYPE_FP4_E2M1 = 5, 6, 7
 _STATUS = {0: "OK", 1: "INVALID_ARG", 2: "SHAPE", 3: "DTYPE", 4: "UNSUPPORTED", 5: "WORKSPACE", 6: "HIP"}
 
 
@@ -83,7 +85,7 @@ _SIGS = {
     "moe_mx_pack_weights": ([_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP], _INT),
     "moe_mx_pack_weights_fp4": ([_VP, _VP, _I64, _I64, _I64, _VP, _VP, _VP], _INT),
     "moe_init_routing_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
-    "moe_init_routing": ([_VP, _INT, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
+    "moe_init_routing": ([_VP, _INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
                           _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
     "moe_token_permute_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_token_permute": ([_VP, _INT, _I64, _I64, _VP, _INT, _I64, _I64, _I64, _INT, _INT,
@@ -188,12 +190,19 @@ def pack_weights(codes, scales, fp4: bool = False):
 
 
 def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: int = QUANT_NONE,
-                 row_idx_type: int = 1, expert_tokens_num_type: int = 1):
+                 row_idx_type: int = 1, expert_tokens_num_type: int = 1, x_codes: int | None = None, scale=None):
     """MoeInitRoutingV3 (dropless). Returns (expanded_x, expanded_row_idx, expert_tokens,
-    expanded_scale or None, available_idx_num) with expanded_x of shape [N*K, H]."""
+    expanded_scale or None, available_idx_num) with expanded_x of shape [N*K, H].
+
+    x_codes: DTYPE_FP8_E5M2 / DTYPE_FP8_E4M3 / DTYPE_FP4_E2M1 when x holds MX codes (uint8
+    [N, H], or [N, H/2] for FP4, H the logical hidden size): the rows are gathered as they
+    are (quant_mode -1), with their E8M0 scales [N, mx_scale_cols(H)] when scale is given."""
     lib = load()
     _need_gpu(x, expert_idx)
     n, h = x.shape
+    if x_codes is not None:
+        return _init_routing_codes(lib, x, expert_idx, expert_num, active_range, row_idx_type,
+                                   expert_tokens_num_type, x_codes, scale)
     k = expert_idx.shape[1]
     s, e = (0, expert_num) if active_range is None else active_range
     flat = n * k
@@ -211,9 +220,40 @@ def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: 
     nbytes = ctypes.c_size_t()
     _check(lib.moe_init_routing_workspace_size(n, k, expert_num, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)
-    _check(lib.moe_init_routing(_ptr(x), _DT[x.dtype], n, h, _ptr(expert_idx), k, expert_num, s, e, quant_mode,
+    _check(lib.moe_init_routing(_ptr(x), _DT[x.dtype], None, n, h, _ptr(expert_idx), k, expert_num, s, e, quant_mode,
                                 row_idx_type, expert_tokens_num_type, _ptr(ex), _ptr(idx), _ptr(tok), _ptr(sc),
                                 _ptr(avail), _ptr(ws), ws.numel(), _stream(dev)))
+    return ex, idx, tok, sc, avail
+
+
+def _init_routing_codes(lib, x, expert_idx, expert_num, active_range, row_idx_type, expert_tokens_num_type,
+                        x_codes, scale):
+    n, row_bytes = x.shape
+    h = 2 * row_bytes if x_codes == DTYPE_FP4_E2M1 else row_bytes
+    k = expert_idx.shape[1]
+    s, e = (0, expert_num) if active_range is None else active_range
+    flat = n * k
+    dev = x.device
+    ex = torch.empty((flat, row_bytes), dtype=torch.uint8, device=dev)
+    idx = torch.empty((flat,), dtype=torch.int32, device=dev)
+    if expert_tokens_num_type == 2:
+        tok = torch.empty((expert_num, 2), dtype=torch.int64, device=dev)
+    else:
+        tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
+    sc = None
+    if scale is not None:
+        _need_gpu(scale)
+        scale = _u8(scale)
+        if tuple(scale.shape) != (n, mx_scale_cols(h)):
+            raise ValueError(f"scale must be [N, {mx_scale_cols(h)}] E8M0 bytes")
+        sc = torch.empty((flat, mx_scale_cols(h)), dtype=torch.uint8, device=dev)
+    avail = torch.empty((1,), dtype=torch.int64, device=dev)
+    nbytes = ctypes.c_size_t()
+    _check(lib.moe_init_routing_workspace_size(n, k, expert_num, ctypes.byref(nbytes)))
+    ws = _workspace(nbytes.value, dev)
+    _check(lib.moe_init_routing(_ptr(_u8(x)), x_codes, _ptr(scale), n, h, _ptr(expert_idx), k, expert_num, s, e,
+                                QUANT_NONE, row_idx_type, expert_tokens_num_type, _ptr(ex), _ptr(idx), _ptr(tok),
+                                _ptr(sc), _ptr(avail), _ptr(ws), ws.numel(), _stream(dev)))
     return ex, idx, tok, sc, avail
 
 

@@ -438,7 +438,8 @@ moe_status moe_init_routing_workspace_size(int64_t num_rows, int64_t k, int64_t 
   return ok();
 }
 
-moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_t hidden, const int32_t* expert_idx,
+moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows, int64_t hidden,
+                            const int32_t* expert_idx,
                             int64_t k, int64_t expert_num, int64_t active_start, int64_t active_end, int quant_mode,
                             int row_idx_type, int expert_tokens_num_type, void* expanded_x,
                             int32_t* expanded_row_idx, int64_t* expert_tokens, uint8_t* expanded_scale,
@@ -453,10 +454,18 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
                 (long long)active_start, (long long)active_end, (long long)expert_num);
   const int64_t flat = num_rows * k;
   if (flat >= MOE_MAX_FLAT_ROWS) return fail(MOE_ERR_SHAPE, "%s: num_rows*k must be < %d", who, MOE_MAX_FLAT_ROWS);
-  if (!valid_x_dtype(x_dtype)) return fail(MOE_ERR_DTYPE, "%s: x_dtype %d not FP32/FP16/BF16", who, x_dtype);
+  // x of MX codes ([V3] quantMode -1 with an FP8 / FP4 x): rows gathered as they are
+  const bool codes = x_dtype == MOE_DTYPE_FP8_E5M2 || x_dtype == MOE_DTYPE_FP8_E4M3 || x_dtype == MOE_DTYPE_FP4_E2M1;
+  if (!valid_x_dtype(x_dtype) && !codes)
+    return fail(MOE_ERR_DTYPE, "%s: x_dtype %d not FP32/FP16/BF16 or FP8/FP4 codes", who, x_dtype);
   if (!valid_quant_mode(quant_mode))
     return fail(MOE_ERR_UNSUPPORTED, "%s: quant_mode %d not supported (-1, 2, 3, 9)", who, quant_mode);
   const bool mx = quant_mode != MOE_QUANT_NONE;
+  if (codes && mx) return fail(MOE_ERR_UNSUPPORTED, "%s: x of FP8/FP4 codes takes quant_mode -1 (pass-through)", who);
+  if (x_dtype == MOE_DTYPE_FP4_E2M1 && hidden % 2 != 0)
+    return fail(MOE_ERR_SHAPE, "%s: FP4 codes need an even hidden", who);
+  if (scale && !codes) return fail(MOE_ERR_INVALID_ARG, "%s: a scale input goes only with x of FP8/FP4 codes", who);
+  if (scale && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: scales need hidden %% 32 == 0", who);
   if (mx && hidden % 32 != 0) return fail(MOE_ERR_SHAPE, "%s: MX quantization needs hidden %% 32 == 0", who);
   if (row_idx_type != MOE_ROW_IDX_GATHER && row_idx_type != MOE_ROW_IDX_SCATTER)
     return fail(MOE_ERR_INVALID_ARG, "%s: row_idx_type %d not 0 or 1", who, row_idx_type);
@@ -471,7 +480,8 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   const bool key_value = expert_tokens_num_type == MOE_TOKENS_KEY_VALUE;
   if ((active_end > active_start || key_value) && !expert_tokens)
     return fail(MOE_ERR_INVALID_ARG, "%s: expert_tokens must be non-NULL", who);
-  if (mx && flat > 0 && !expanded_scale) return fail(MOE_ERR_INVALID_ARG, "%s: expanded_scale must be non-NULL in MX modes", who);
+  if ((mx || scale) && flat > 0 && !expanded_scale)
+    return fail(MOE_ERR_INVALID_ARG, "%s: expanded_scale must be non-NULL in MX modes and with a scale input", who);
   const int active = (int)(active_end - active_start);
   const bool want_gather = row_idx_type == MOE_ROW_IDX_GATHER;
   Carver cv(nullptr);
@@ -497,6 +507,15 @@ moe_status moe_init_routing(const void* x, int x_dtype, int64_t num_rows, int64_
   if (key_value) {
     e = moe::launch_key_value(ws.r.offsets, active, (int)active_start, (int)expert_num, expert_tokens, st);
     if (e != hipSuccess) return hip_fail(e, "moe_init_routing key_value launch");
+  }
+  if (codes) {
+    const int64_t row_bytes = x_dtype == MOE_DTYPE_FP4_E2M1 ? hidden / 2 : hidden;
+    e = moe::launch_permute_rows(static_cast<const uint8_t*>(x), num_rows, row_bytes, (int)k, rp.scat, flat,
+                                 static_cast<uint8_t*>(expanded_x), st);
+    if (e == hipSuccess && scale)
+      e = moe::launch_permute_rows(scale, num_rows, scale_cols(hidden), (int)k, rp.scat, flat, expanded_scale, st);
+    if (e != hipSuccess) return hip_fail(e, "moe_init_routing gather launch");
+    return ok();
   }
   moe::PermuteParams pp;
   pp.x = x; pp.in_dtype = x_dtype; pp.n = num_rows; pp.hidden = hidden; pp.topk = (int)k; pp.scat = rp.scat;

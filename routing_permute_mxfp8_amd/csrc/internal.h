@@ -97,6 +97,10 @@ struct PermuteParams {
   uint8_t* tok_scales = nullptr;
 };
 hipError_t launch_permute(const PermuteParams& p, hipStream_t stream);
+// Byte rows: out[dest] = x[t] for each destination of token t (scat as above, identity
+// when null), row_bytes bytes a row.
+hipError_t launch_permute_rows(const uint8_t* x, int64_t n, int64_t row_bytes, int topk, const int32_t* scat,
+                               int64_t m_limit, uint8_t* out, hipStream_t stream);
 
 // ---- grouped GEMMs (gmm.hip) -------------------------------------------------------
 // GMM1's activation (MOE_ACT_* kinds; validated and defaulted by the API layer).

@@ -193,6 +193,13 @@ hipError_t launch_mx_typed(const PermuteParams& p, hipStream_t stream) {
 
 }  // namespace
 
+hipError_t launch_permute_rows(const uint8_t* x, int64_t n, int64_t row_bytes, int topk, const int32_t* scat,
+                               int64_t m_limit, uint8_t* out, hipStream_t stream) {
+  if (n <= 0 || row_bytes <= 0) return hipSuccess;
+  permute_copy_kernel<<<(unsigned)((n + 3) / 4), 256, 0, stream>>>(x, n, row_bytes, topk, scat, m_limit, out);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const PermuteParams& p, hipStream_t stream) {
   if (p.n <= 0) return hipSuccess;
   if (p.quant < 0) {

@@ -75,7 +75,7 @@ def init_routing(lib, **kw):
              row_idx_type=1, tokens_type=1, ex=FAKE, idx=FAKE, tok=FAKE, sc=FAKE, avail=FAKE, ws=FAKE,
              ws_bytes=0)
     a.update(kw)
-    return lib.moe_init_routing(a["x"], a["x_dtype"], a["num_rows"], a["hidden"], a["expert_idx"], a["k"],
+    return lib.moe_init_routing(a["x"], a["x_dtype"], a.get("scale"), a["num_rows"], a["hidden"], a["expert_idx"], a["k"],
                                 a["expert_num"], a["s"], a["e"], a["quant"], a["row_idx_type"], a["tokens_type"],
                                 a["ex"], a["idx"], a["tok"], a["sc"], a["avail"], a["ws"], a["ws_bytes"], None)
 
@@ -85,7 +85,11 @@ def init_routing(lib, **kw):
     (dict(e=9), 2), (dict(s=-1), 2), (dict(quant=1), 4), (dict(quant=9), 5), (dict(quant=16), 4),
     (dict(hidden=100), 2), (dict(row_idx_type=2), 1), (dict(tokens_type=2), 5), (dict(tokens_type=5), 1),
     (dict(tokens_type=2, expert_num=6000, e=100), 2), (dict(tokens_type=2, s=3, e=3, tok=None), 1),
-    (dict(x_dtype=7), 3), (dict(avail=None), 1), (dict(sc=None), 1), (dict(num_rows=1 << 23, k=2), 2),
+    (dict(x_dtype=8), 3), (dict(avail=None), 1), (dict(sc=None), 1), (dict(num_rows=1 << 23, k=2), 2),
+    # x of MX codes ([V3] quantMode -1 with an FP8/FP4 x): quant -1 only, scale only with codes
+    (dict(x_dtype=6), 4), (dict(x_dtype=6, quant=-1), 5), (dict(x_dtype=7, quant=-1, hidden=255), 2),
+    (dict(scale=FAKE, quant=-1), 1), (dict(x_dtype=5, quant=-1, scale=FAKE, hidden=48), 2),
+    (dict(x_dtype=7, quant=-1, scale=FAKE, sc=None), 1), (dict(x_dtype=7, quant=-1, scale=FAKE), 5),
     (dict(), 5),  # valid arguments, but no workspace: MOE_ERR_WORKSPACE names the byte count
 ])
 def test_init_routing_validation(lib, kw, status):

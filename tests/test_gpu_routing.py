@@ -171,3 +171,37 @@ def test_permute_one_dimensional_indices():
     say("token_permute 1-D indices")
     check_permute(tokens, idx, None, 2, 5)
     check_permute(tokens, idx, -7, 9, 5)
+
+
+@pytest.mark.parametrize("fmt,x_codes", [("e4m3", rp.DTYPE_FP8_E4M3), ("e5m2", rp.DTYPE_FP8_E5M2),
+                                         ("e2m1", rp.DTYPE_FP4_E2M1)])
+@pytest.mark.parametrize("with_scale", [True, False])
+@pytest.mark.parametrize("row_idx_type", [1, 0])
+def test_init_routing_passthrough(fmt, x_codes, with_scale, row_idx_type):
+    """MoeInitRoutingV3 quantMode -1 with an x of FP8/FP4 codes and scaleOptional: the code
+    rows and scale rows gathered as they are, bit for bit against the oracle's gather (the
+    codes and scales are the oracle's quantization of bf16 x), with an active range."""
+    cfg = moe_inputs.config("tiny", tokens=301, hidden=256, topk=3, experts=12, seed=78)
+    active = (2, 9)
+    say(f"init_routing pass-through {fmt} scale={with_scale} row_idx_type={row_idx_type}")
+    ids = moe_inputs.expert_ids(cfg)
+    x = moe_inputs.activations(cfg).double().numpy()
+    codes, scales = mxfp.quantize(x, fmt)
+    if fmt == "e2m1":
+        codes = mxfp.pack_fp4(codes)
+    ex, idx, tok, sc, avail = rp.init_routing(to_dev(codes), to_dev(ids.astype(np.int32)), cfg.experts, active,
+                                              rp.QUANT_NONE, row_idx_type, 1, x_codes=x_codes,
+                                              scale=to_dev(scales) if with_scale else None)
+    torch.cuda.synchronize()
+    ref = routing.init_routing(ids, cfg.experts, active, row_idx_type, 1)
+    a = ref["avail"]
+    assert int(avail.item()) == a
+    assert np.array_equal(idx.cpu().numpy(), ref["expanded_row_idx"])
+    assert np.array_equal(tok.cpu().numpy(), ref["expert_tokens"])
+    want_c, want_s = routing.gather_passthrough(codes, scales if with_scale else None, ref["sorted_row_idx"],
+                                                cfg.topk, ref["active_start"], a)
+    assert np.array_equal(ex.cpu().numpy()[:a], want_c)
+    if with_scale:
+        assert np.array_equal(sc.cpu().numpy()[:a], want_s)
+    else:
+        assert sc is None

@@ -114,3 +114,24 @@ def test_key_value_counts():
     assert kv.shape == (50, 2)
     assert [tuple(v) for v in kv[:len(want)].tolist()] == want
     assert np.all(kv[len(want):] == 0)
+
+
+@pytest.mark.parametrize("mode", [2, 3, 9])
+def test_passthrough_gather_equals_quantize_then_gather(mode):
+    """MoeInitRoutingV3 quantMode -1 with an x of MX codes and scaleOptional: gathering
+    already-quantized rows and their scales gives what the MX modes give from bf16 x,
+    because Q_MX is row-local ([V3] 计算公式 5 quantizes x before the gather)."""
+    rng = np.random.default_rng(7 + mode)
+    n, k, e, h = 37, 3, 9, 128
+    ids = np.stack([rng.permutation(e)[:k] for _ in range(n)])
+    x = mxfp.bf16_round(rng.normal(0, 1, (n, h)))
+    r = routing.init_routing(ids, e, active=(2, 7))
+    fmt = routing.quant_mode_format(mode)
+    codes, scales = mxfp.quantize(x, fmt)
+    if fmt == "e2m1":
+        codes = mxfp.pack_fp4(codes)
+    got_c, got_s = routing.gather_passthrough(codes, scales, r["sorted_row_idx"], k, r["active_start"], r["avail"])
+    want_c, want_s = routing.gather_rows(x, r["sorted_row_idx"], k, mode, r["active_start"], r["avail"])
+    assert got_c.dtype == np.uint8 and np.array_equal(got_c, want_c) and np.array_equal(got_s, want_s)
+    only_c, no_s = routing.gather_passthrough(codes, None, r["sorted_row_idx"], k, r["active_start"], r["avail"])
+    assert no_s is None and np.array_equal(only_c, want_c)

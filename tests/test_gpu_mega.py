@@ -145,6 +145,51 @@ def test_stage1_quantize_then_gather():
     assert mx <= 2e-2 and mean <= 5e-3
 
 
+def test_empty_layer():
+    """No tokens: y is empty, expert_token_nums all zero, nothing else is launched."""
+    cfg = moe_inputs.config("tiny")
+    say("mega_moe with no tokens")
+    weights = oracle_weights(cfg)
+    sh = oracle_weights(cfg, 1, shared=True)
+    wf = rp.WEIGHTS_PACKED
+    x = torch.zeros((0, cfg.hidden), dtype=torch.bfloat16, device=DEV)
+    ids = torch.zeros((0, cfg.topk), dtype=torch.int32, device=DEV)
+    w = torch.zeros((0, cfg.topk), dtype=torch.float32, device=DEV)
+    y, etn = rp.mega_moe(x, ids, w, *device_weights(weights, wf), shared=tuple(device_weights(sh, wf)),
+                         quant_out_dtype=FP8[cfg.fmt], weight_format=wf)
+    torch.cuda.synchronize()
+    assert y.shape == (0, cfg.hidden)
+    assert np.array_equal(etn.cpu().numpy(), np.zeros(cfg.experts, np.int32))
+
+
+@pytest.mark.parametrize("experts,topk,shared", [(8, 1, 1), (1, 1, 0), (1, 1, 2)])
+def test_topk_one_and_single_expert(experts, topk, shared):
+    """topK = 1 (each token's row is its expert's output, weighted) and a single routed
+    expert, with and without shared experts, against the oracle."""
+    cfg = moe_inputs.config("tiny", tokens=77, experts=experts, topk=topk, shared=shared, seed=56)
+    say(f"mega_moe E={experts} K={topk} S={shared}")
+    ids = moe_inputs.expert_ids(cfg)
+    x_t = moe_inputs.activations(cfg)
+    w = moe_inputs.gate_weights(cfg)
+    weights = oracle_weights(cfg)
+    wf = rp.WEIGHTS_PACKED
+    shared_np, shared_dev = (), None
+    if shared:
+        sh = oracle_weights(cfg, shared, shared=True)
+        shared_np = [tuple(a[s] for a in sh) for s in range(shared)]
+        shared_dev = tuple(device_weights(sh, wf))
+    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf),
+                              shared=shared_dev, quant_out_dtype=FP8[cfg.fmt], debug=True, weight_format=wf)
+    torch.cuda.synchronize()
+    ref = moe.mega_moe(x_t.double().numpy(), ids, w, weights, cfg.fmt, cfg.experts, shared=shared_np)
+    assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
+    assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
+    assert normwise_err(dbg["h1"].cpu().numpy(), ref["h1"]) <= 2e-3
+    mx, mean = y_errors(y.cpu().double().numpy(), ref["y"])
+    say(f"  Y max {mx:.3g} mean {mean:.3g}")
+    assert mx <= 2e-2 and mean <= 5e-3
+
+
 ACTS = [("swiglu", (0.8,)), ("swiglustep", (0.6,)), ("swiglustep", ()), ("swigluoai", ()),
         ("swigluoai", (0.9, 1.2, 0.5)), ("situglu", (2.0,)), ("situglu", (1.5, 0.7)), ("situglu", ()),
         ("gelu", ()), ("gelu", (float(np.finfo(np.float32).max),))]

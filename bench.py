@@ -1,19 +1,22 @@
 """Benchmark of the MI355X MoE-layer hot path (one GPU).
 
-Default workload (the MegaMoE decode-shaped layer): 128 tokens, hidden 7168,
-intermediate 2048, 256 experts all local, topK 8, MXFP8 E4M3 weights with E8M0
-scales, bf16 activations N(0,1), fp32 softmax gate weights. One step is one
-mega_moe call: routing -> gather + MX quantization -> GMM1 + SwiGLU + MX
-requantization -> GMM2 + weighted combine -> bf16 Y. Inputs and weights are
-resident in HBM before the timed region (weights are generated on the GPU with
-a seeded generator and quantized by the library's own MX quantizer, untimed).
+Default workload (the MegaMoE prefill-shaped layer, the largest single-GPU
+layer of the pages' regimes): 8192 tokens, hidden 7168, intermediate 2048, 256
+experts all local, topK 8, plus one shared expert over all tokens, MXFP8 E4M3
+weights with E8M0 scales, bf16 activations N(0,1), fp32 softmax gate weights.
+One step is one mega_moe call: routing -> gather + MX quantization -> GMM1 +
+SwiGLU + MX requantization -> GMM2 -> shared expert -> weighted combine -> bf16
+Y. Inputs and weights are resident in HBM before the timed region (weights are
+generated on the GPU with a seeded generator and quantized by the library's own
+MX quantizer, untimed).
 
 Prints one JSON line: MoE layer tokens/s, the roofline of the dominant kernel
 (its duration measured with HIP events that the library records on its stream
-at every stage boundary during the timed steps), and the CPU oracle timed on a
-bounded token sample of the same workload on this host.
+at every stage boundary during the timed steps) with both its MXFP8 MFMA and its
+HBM fraction, and the CPU oracle timed on a bounded token sample of the same
+workload on this host.
 
-    python bench.py [--steps K] [--warmup W] [--config decode|prefill|skewed|tiny|routing]
+    python bench.py [--steps K] [--warmup W] [--config prefill|decode|skewed|tiny|routing]
 """
 
 from __future__ import annotations
@@ -195,21 +198,30 @@ def measure_peaks(torch, rp, nbytes=1 << 30, reps=5):
 
 
 def roofline_entry(name, ms, work):
+    """The kernel against the roofline that bounds it (MFMA above the ridge intensity,
+    HBM below), with both fractions: mfma_frac = algorithmic MXFP8 flops / time / the
+    MXFP8 peak, hbm_frac = algorithmic bytes / time / the HBM peak."""
     intensity = work["flops"] / max(work["bytes"], 1.0)
+    tflops = work["flops"] / (ms * 1e-3) / 1e12
+    gbs = work["bytes"] / (ms * 1e-3) / 1e9
+    both = dict(mfma_tflops=round(tflops, 1), mfma_frac=round(tflops / MXFP8_PEAK_TFLOPS, 4),
+                hbm_gbs=round(gbs, 1), hbm_frac=round(gbs / HBM_PEAK_GBS, 4),
+                intensity_flop_per_byte=round(intensity, 1), flops_per_launch=work["flops"],
+                bytes_per_launch=work["bytes"])
     if intensity >= RIDGE:
-        achieved = work["flops"] / (ms * 1e-3) / 1e12
-        return dict(kernel=name, bound="mfma", achieved=round(achieved, 2), peak=MXFP8_PEAK_TFLOPS,
-                    unit="TFLOP/s", frac=round(achieved / MXFP8_PEAK_TFLOPS, 4), traffic=None,
-                    algorithmic_per_launch=work["flops"], avg_launch_ms=round(ms, 5))
-    achieved = work["bytes"] / (ms * 1e-3) / 1e9
-    return dict(kernel=name, bound="hbm", achieved=round(achieved, 1), peak=HBM_PEAK_GBS, unit="GB/s",
-                frac=round(achieved / HBM_PEAK_GBS, 4), traffic=None, algorithmic_per_launch=work["bytes"],
-                avg_launch_ms=round(ms, 5))
+        return dict(kernel=name, bound="mfma", achieved=round(tflops, 2), peak=MXFP8_PEAK_TFLOPS,
+                    unit="TFLOP/s", frac=round(tflops / MXFP8_PEAK_TFLOPS, 4), traffic=None,
+                    algorithmic_per_launch=work["flops"], avg_launch_ms=round(ms, 5), **both)
+    return dict(kernel=name, bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s",
+                frac=round(gbs / HBM_PEAK_GBS, 4), traffic=None, algorithmic_per_launch=work["bytes"],
+                avg_launch_ms=round(ms, 5), **both)
 
 
 def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs, fp4=False):
     """The oracle (CPU, float64) on a bounded token sample: tokens/s of the per-token layer
     (MXFP4 weights with fp4)."""
+    from concurrent.futures import ThreadPoolExecutor
+
     from oracle import moe, mxfp
     wfmt = "e2m1" if fp4 else cfg.fmt
 
@@ -219,16 +231,21 @@ def cpu_baseline_mega(cfg, ids, x_cpu, w, sample_tokens, torch, moe_inputs, fp4=
     rng = np.random.default_rng(123)
     tokens = rng.choice(cfg.tokens, size=sample_tokens, replace=False)
     experts = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
-    cache = {}
-    for e in experts:  # inputs of the oracle: the sampled experts' weights, quantized by the oracle (untimed)
-        m1 = moe_inputs.weight_master(cfg, "w1", e, device="cuda").cpu().double().numpy()
-        m2 = moe_inputs.weight_master(cfg, "w2", e, device="cuda").cpu().double().numpy()
-        cache[e] = (*q(m1), *q(m2))
-    shared = []
+    # inputs of the oracle: the sampled experts' weights, quantized by the oracle (untimed,
+    # in threads: it is input preparation, not the timed oracle)
+    masters = {("w", e): (moe_inputs.weight_master(cfg, "w1", e, device="cuda").cpu(),
+                          moe_inputs.weight_master(cfg, "w2", e, device="cuda").cpu()) for e in experts}
     for s in range(cfg.shared):
-        m1 = moe_inputs.weight_master(cfg, "sw1", s, device="cuda").cpu().double().numpy()
-        m2 = moe_inputs.weight_master(cfg, "sw2", s, device="cuda").cpu().double().numpy()
-        shared.append((*q(m1), *q(m2)))
+        masters[("s", s)] = (moe_inputs.weight_master(cfg, "sw1", s, device="cuda").cpu(),
+                             moe_inputs.weight_master(cfg, "sw2", s, device="cuda").cpu())
+
+    def prep(key):
+        m1, m2 = masters[key]
+        return key, (*q(m1.double().numpy()), *q(m2.double().numpy()))
+    with ThreadPoolExecutor(max_workers=min(16, os.cpu_count() or 1)) as ex:
+        done = dict(ex.map(prep, list(masters)))
+    cache = {e: done[("w", e)] for e in experts}
+    shared = [done[("s", s)] for s in range(cfg.shared)]
     x = x_cpu.double().numpy()
     t0 = time.perf_counter()
     moe.per_token(x, ids, w, lambda e: cache[e], cfg.fmt, tokens, shared=shared, wfmt=wfmt)
@@ -392,9 +409,48 @@ def bench_routing(args, torch, rp, moe_inputs):
                              kernels="route_count, route_scan_fused, route_scatter, permute_mx_kernel (one call)",
                              measured_peak=peaks["copy_gbs"],
                              frac_of_measured=round(achieved / peaks["copy_gbs"], 4)),
-               step_ms=percentiles(times), measured_peaks=peaks, mall_flush="512 MB streaming read between calls",
-               cpu_baseline=None)
+               step_ms=percentiles(times), measured_peaks=peaks, mall_flush="512 MB streaming read between calls")
+    out["roofline"]["target_70pct_ms"] = round(alg / (0.7 * HBM_PEAK_GBS * 1e9) * 1e3, 5)
+    out["roofline"]["measured_copy_ceiling_ms"] = round(alg / (peaks["copy_gbs"] * 1e9) * 1e3, 5)
+    if not args.no_cpu_baseline:
+        log("[bench] cpu baseline (oracle)")
+        out["cpu_baseline"] = cpu_baseline_routing(cfg, ids, x_cpu, avail, args.cpu_sample or 2048)
+    else:
+        out["cpu_baseline"] = None
     return out
+
+
+def cpu_baseline_routing(cfg, ids, x_cpu, avail, sample_rows):
+    """The oracle (CPU, float64) on the routing workload: the whole routing (stable sort,
+    inverse, histogram, active range) on every id, and the quantized gather on a bounded
+    sample of the active rows, scaled to all of them. Timed single-threaded (numpy's
+    element-wise work is single-threaded; BLAS is not used), rows/s of the whole call."""
+    from oracle import routing
+    try:
+        from threadpoolctl import threadpool_limits
+    except Exception:  # threadpoolctl missing: nothing to limit
+        threadpool_limits = None
+    s, e = cfg.active_range
+    x = x_cpu.double().numpy()
+    ctx = threadpool_limits(limits=1) if threadpool_limits else None
+    if ctx is not None:
+        ctx.__enter__()
+    try:
+        t0 = time.perf_counter()
+        r = routing.init_routing(ids, cfg.experts, (s, e), 1, 1)
+        t_route = time.perf_counter() - t0
+        n = min(sample_rows, r["avail"])
+        t0 = time.perf_counter()
+        routing.gather_rows(x, r["sorted_row_idx"], cfg.topk, 3, r["active_start"], n)
+        t_gather = time.perf_counter() - t0
+    finally:
+        if ctx is not None:
+            ctx.__exit__(None, None, None)
+    total = t_route + t_gather * (avail / max(n, 1))
+    return dict(value=round(avail / total, 1), unit="rows/s", cores=1, kind="oracle",
+                sample=f"routing of all {cfg.flat} ids ({t_route:.2f} s) + quantized gather of {n} of the "
+                       f"{avail} active rows ({t_gather:.2f} s), scaled to all rows; float64, single thread",
+                seconds=round(t_route + t_gather, 2), host_cpus=os.cpu_count(), cpu_model=cpu_model())
 
 
 def main():
@@ -402,7 +458,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--config", default="decode", choices=["tiny", "decode", "prefill", "skewed", "routing"])
+    ap.add_argument("--config", default="prefill", choices=["tiny", "decode", "prefill", "skewed", "routing"])
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample", type=int, default=None, help="tokens in the CPU oracle sample")
     ap.add_argument("--weight-dtype", default="fp8", choices=["fp8", "mxfp4"],

@@ -30,9 +30,10 @@
  *   - Preconditions the host cannot check without reading device memory (expert
  *     ids in [0, expert_num), distinct ids per token for mega_moe, finite
  *     activations) are the caller's; violating them gives undefined results.
- *   - Results are deterministic (bit-identical on repeated calls), except y of
- *     mega_moe / moe_gmm2_combine, whose fp32 accumulation order across experts
- *     is not fixed.
+ *   - Results are deterministic (bit-identical on repeated calls), except the
+ *     y_accum of moe_gmm2_combine, which adds each row's weighted O into it with
+ *     fp32 atomics in no fixed order. mega_moe's y is deterministic: its combine
+ *     gathers each token's expert rows and sums them in a fixed order.
  */
 #ifndef MOE_MX_H
 #define MOE_MX_H

@@ -160,11 +160,13 @@ def combine(o_rows, expanded_row_idx, topk_weights, shared_o=(), combine_comm_mo
 
 
 def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), act=("swiglu", ()), wfmt=None,
-             shared_wfmt=None, combine_comm_mode=0) -> dict:
+             shared_wfmt=None, combine_comm_mode=0, workers=1) -> dict:
     """The whole layer on all tokens, in the permuted (expert-contiguous) order.
 
     x: [N, H] values (bf16 as float64); topk_ids int [N, K]; topk_weights [N, K];
     weights: see _getter; shared: list of (w1q, w1s, w2q, w2s) per shared expert.
+    workers > 1 evaluates the experts' FFNs (independent of one another) in that many
+    threads; the results are the same.
     Returns routing, xq/sx (permuted), h1 [F, 2I], a, aq, sa, o [F, H],
     shared outputs, y (float64 bf16 values) and expert_token_nums (int32 [E])."""
     x = np.asarray(x, dtype=np.float64)
@@ -174,11 +176,18 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
     k = r["topk"]
     xq, sx = routing.gather_rows(x, r["sorted_row_idx"], k, quant_mode)
     flat = xq.shape[0]
-    parts = {}
-    for e in range(num_experts):
+    busy = [e for e in range(num_experts) if r["offsets"][e + 1] > r["offsets"][e]]
+
+    def run(e):
         lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
-        if hi > lo:
-            parts[e] = expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt, act, wfmt)
+        return e, expert_ffn(xq[lo:hi], sx[lo:hi], *get(e), fmt, act, wfmt)
+
+    if workers > 1 and len(busy) > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            parts = dict(ex.map(run, busy))
+    else:
+        parts = dict(run(e) for e in busy)
     hidden = x.shape[1]
     two_i = get(0)[0].shape[0]
     aw = get(0)[2].shape[1] * (2 if wfmt == "e2m1" else 1)   # width of A: I (gated) or 2I (gelu)

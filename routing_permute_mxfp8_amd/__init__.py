@@ -199,6 +199,9 @@ def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: 
     are (quant_mode -1), with their E8M0 scales [N, mx_scale_cols(H)] when scale is given."""
     lib = load()
     _need_gpu(x, expert_idx)
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2 or expert_idx.shape[0] != x.shape[0]:
+        raise ValueError(f"expert_idx must be int32 [N, K] with N = x.shape[0] (got {expert_idx.dtype} "
+                         f"{tuple(expert_idx.shape)})")
     n, h = x.shape
     if x_codes is not None:
         return _init_routing_codes(lib, x, expert_idx, expert_num, active_range, row_idx_type,
@@ -285,6 +288,22 @@ def token_permute(tokens, indices, num_out_tokens=None, padded_mode: bool = Fals
     return out, srt, sc
 
 
+def _check_layer_dtypes(x, topk_ids, topk_weights, x_scales=None):
+    """The C side reads int32 ids, fp32/bf16 gate weights and bf16 x (uint8 codes with
+    x_scales): anything else would be misread, so it is rejected here."""
+    if topk_ids.dtype != torch.int32:
+        raise ValueError(f"topk_ids must be int32 (got {topk_ids.dtype}); convert e.g. torch.topk's int64 ids")
+    if topk_weights.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError(f"topk_weights must be float32 or bfloat16 (got {topk_weights.dtype})")
+    if x_scales is None:
+        if x.dtype != torch.bfloat16:
+            raise ValueError(f"x must be bfloat16 (got {x.dtype})")
+    elif x.dtype not in (torch.uint8, torch.float8_e4m3fn, torch.float8_e5m2):
+        raise ValueError(f"pre-quantized x must hold FP8 codes (uint8 or float8), got {x.dtype}")
+    if topk_ids.dim() != 2 or topk_ids.shape != topk_weights.shape or topk_ids.shape[0] != x.shape[0]:
+        raise ValueError("topk_ids and topk_weights must both be [N, K] with N = x.shape[0]")
+
+
 def _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, y, etn,
                  debug, weight_format=WEIGHTS_ND, activation=ACT_SWIGLU, activation_params=(), weight_dtype=0,
                  shared_weight_dtype=0, x_scales=None, combine_comm_mode=0):
@@ -334,14 +353,17 @@ def mega_moe(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared=Non
     (a None entry is skipped; each record costs a few microseconds of GPU time).
     activation / activation_params: ACT_* and its parameter list as in the C header (gelu
     makes A, and w2's input width, 2 * inter).
-    weight_dtype / shared_weight_dtype: 0 (FP8 as the activations) or FP4_E2M1 (MXFP4 codes
+    weight_dtype: 0 or the activations' FP8 type (FP8 weights), or FP4_E2M1 (MXFP4 codes
     two a byte, e.g. from mx_quantize(..., QUANT_MXFP4); pack_weights(..., fp4=True)).
+    shared_weight_dtype: 0 = the same as weight_dtype, else one of the values above
+    (e.g. FP8_E4M3 for FP8 shared experts beside MXFP4 routed experts).
     x_scales: pre-quantized pass-through: x holds FP8 codes of quant_out_dtype (uint8
     [N, H], e.g. from mx_quantize) and x_scales their E8M0 scales [N, H/32].
     combine_comm_mode: 0 (each expert output row rounded to bf16 before the weighted sum,
     MegaMoE's default) or 1 (a token's expert outputs summed in fp32, rounded once)."""
     lib = load()
     _need_gpu(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales)
+    _check_layer_dtypes(x, topk_ids, topk_weights, x_scales)
     if x_scales is not None and x_scales.shape[1] != x.shape[1] // 32:
         x_scales = x_scales[:, :x.shape[1] // 32].contiguous()   # drop the AlignUp(.., 2) padding column
     n, h = x.shape
@@ -388,6 +410,7 @@ def mega_moe_workspace_bytes(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_sc
                              activation: int = ACT_SWIGLU, activation_params=(), weight_dtype: int = 0,
                              shared_weight_dtype: int = 0, combine_comm_mode: int = 0) -> int:
     lib = load()
+    _check_layer_dtypes(x, topk_ids, topk_weights)
     a = _mega_struct(x, topk_ids, topk_weights, w1, w1_scales, w2, w2_scales, shared, quant_out_dtype, x, x, None,
                      weight_format, activation, activation_params, weight_dtype, shared_weight_dtype,
                      combine_comm_mode=combine_comm_mode)

@@ -25,29 +25,42 @@ def lib_path() -> str:
     return os.path.join(HERE, LIB_NAME)
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source into one shared library; always recompiles."""
-    out = lib_path()
-    tmp = out + ".tmp"
-    cmd = [
-        hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC", "-shared",
-        # keep fp32 denormals: MX quantization of subnormal bf16 inputs depends on them
-        "-fno-gpu-flush-denormals-to-zero",
-        "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-        "-Wno-unused-result",
-        "-I", os.path.join(ROOT, "include"),
-        *[os.path.join(HERE, s) for s in SOURCES],
-        "-o", tmp,
-    ]
+FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-std=c++20", "-fPIC",
+    # keep fp32 denormals: MX quantization of subnormal bf16 inputs depends on them
+    "-fno-gpu-flush-denormals-to-zero",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wno-unused-result",
+]
+NOISE = "is not a recognized feature for this target"
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    errs = "\n".join(l for l in res.stderr.splitlines() if noise not in l)
+    errs = "\n".join(l for l in res.stderr.splitlines() if NOISE not in l)
     if res.returncode != 0:
-        raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
+        raise RuntimeError(f"hipcc failed ({res.returncode}): {' '.join(cmd)}\n{errs}")
     if verbose and errs.strip():
         print(errs, file=sys.stderr)
+
+
+def build(verbose: bool = False, jobs: int | None = None) -> str:
+    """Compile every source (in parallel, one object each) and link them into one shared
+    library; always recompiles."""
+    from concurrent.futures import ThreadPoolExecutor
+    out = lib_path()
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    objs = [os.path.join(objdir, os.path.basename(s) + ".o") for s in SOURCES]
+    cmds = [[hipcc(), *FLAGS, *inc, "-c", os.path.join(HERE, s), "-o", o] for s, o in zip(SOURCES, objs)]
+    jobs = jobs or min(len(cmds), max(1, min(16, os.cpu_count() or 1)))
+    with ThreadPoolExecutor(max_workers=jobs) as ex:
+        list(ex.map(lambda c: _run(c, verbose), cmds))
+    tmp = out + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
     os.replace(tmp, out)
     return out
 

@@ -23,8 +23,9 @@
 //   gate and up values of the same channels, so SwiGLU is lane-local and the 32-channel
 //   MX group of the requantization is the lane's 8 values plus 3 lanes (xor 16 / 32).
 //   GMM2 puts the tokens in the A slot (output rows = tokens): a lane group then holds
-//   16 consecutive channels of one token, so the weighted combine issues fp32 atomics on
-//   64 contiguous bytes per token row.
+//   16 consecutive channels of one token, stored as one 32-byte (bf16) or 64-byte (fp32)
+//   piece of that token's O row with plain stores; the weighted combine reads the rows
+//   back per token (combine.hip), in a fixed order.
 // * Blocks are persistent and XCD-aware: block b runs on XCD b % 8 and takes items from
 //   that XCD's contiguous share of the item list, so the channel blocks of one expert run
 //   together on one XCD and share its L2 for the token rows.

@@ -188,3 +188,21 @@ def test_probe_validation(lib):
     assert lib.moe_probe_stream(0, FAKE, FAKE, 0, None) == 2
     assert lib.moe_probe_stream(1, None, FAKE, 1024, None) == 1          # NULL buffer
     assert lib.moe_probe_mfma(0, None, None, None, None) == 2            # iters
+
+
+def test_binding_rejects_dtypes_the_library_would_misread():
+    """The C side reads int32 ids, fp32/bf16 gate weights and bf16 x: the binding rejects
+    anything else (e.g. torch.topk's int64 ids) before any call (host-only check)."""
+    import torch
+    import routing_permute_mxfp8_amd as rp
+    x = torch.zeros((4, 256), dtype=torch.bfloat16)
+    ids = torch.zeros((4, 2), dtype=torch.int32)
+    w = torch.zeros((4, 2), dtype=torch.float32)
+    rp._check_layer_dtypes(x, ids, w)
+    rp._check_layer_dtypes(x, ids, w.to(torch.bfloat16))
+    rp._check_layer_dtypes(torch.zeros((4, 256), dtype=torch.uint8), ids, w, x_scales=torch.zeros((4, 8)))
+    bad = [(x, ids.to(torch.int64), w, None), (x.float(), ids, w, None), (x, ids, w.double(), None),
+           (x, ids, w[:, :1], None), (x[:3], ids, w, None), (x, ids, w, torch.zeros((4, 8)))]
+    for args in bad:
+        with pytest.raises(ValueError):
+            rp._check_layer_dtypes(*args)

@@ -4,9 +4,12 @@ Small layers are compared whole: routing and stage-1 operands bit for bit, h1
 within 2e-3 normwise, the requantized activations code by code, Y within
 max|dY| <= 2e-2 max|Y| and sum|dY| <= 5e-3 sum|Y|. The full-size decode,
 prefill and skewed layers run in the benchmark's configuration (weights made on
-the GPU and quantized by the library) and are checked on sampled tokens: the
-oracle requantizes the sampled experts' masters itself (and the library's weight
-bytes must equal its), then computes those tokens one (token, k) at a time."""
+the GPU and quantized by the library) and are checked on the rows of their
+special experts and on sampled tokens: the oracle requantizes the experts'
+masters itself (and the library's weight bytes must equal its), then computes
+those rows and tokens from its own operands."""
+import os
+
 import numpy as np
 import pytest
 import torch
@@ -39,6 +42,18 @@ def device_weights(arrays, wf):
     return d
 
 
+def assert_same_layer(y_fast, etn_fast, y_dbg, etn_dbg):
+    """The call without parity outputs runs other kernel instances than the debug call
+    (GMM2 stores bf16 O rows instead of the fp32 rows the debug output needs, and the
+    combine reads them as bf16 instead of rounding fp32 rows as it reads them): the two
+    must give the same Y bit for bit, so the instances a plain call runs are checked
+    against the oracle through the debug call's comparison."""
+    assert torch.equal(etn_fast, etn_dbg)
+    if not torch.equal(y_fast, y_dbg):
+        d = (y_fast.float() - y_dbg.float()).abs()
+        raise AssertionError(f"plain and debug calls differ: {int((d > 0).sum())} elements, max {float(d.max()):.3g}")
+
+
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"{c['name']}-{c.get('tokens', '')}-{c.get('shared', 0)}")
 @pytest.mark.parametrize("wdtype,wf", [(torch.float32, rp.WEIGHTS_ND), (torch.bfloat16, rp.WEIGHTS_PACKED),
                                        (torch.float32, rp.WEIGHTS_PACKED)], ids=["fp32-nd", "bf16-packed", "fp32-packed"])
@@ -60,10 +75,12 @@ def test_small_layers(case, wdtype, wf):
         sh = oracle_weights(cfg, cfg.shared, shared=True)
         shared_np = [tuple(a[s] for a in sh) for s in range(cfg.shared)]
         shared = tuple(device_weights(sh, wf))
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), w_t.to(DEV),
-                              *device_weights(weights, wf), shared=shared, quant_out_dtype=FP8[cfg.fmt], debug=True,
-                              weight_format=wf)
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), w_t.to(DEV), *device_weights(weights, wf))
+    kw = dict(shared=shared, quant_out_dtype=FP8[cfg.fmt], weight_format=wf)
+    y, etn, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y_fast, etn_fast = rp.mega_moe(*args, **kw)
     torch.cuda.synchronize()
+    assert_same_layer(y_fast, etn_fast, y, etn)
     ref = moe.mega_moe(x, ids, w_used, weights, cfg.fmt, cfg.experts, shared=shared_np)
     assert np.array_equal(etn.cpu().numpy(), ref["expert_token_nums"])
     assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), ref["routing"]["sorted_row_idx"])
@@ -218,10 +235,13 @@ def test_activations(kind, params, tt):
     weights = oracle_weights(cfg, gelu=gelu)
     sh = oracle_weights(cfg, cfg.shared, shared=True, gelu=gelu)
     wf = rp.WEIGHTS_PACKED
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf),
-                              shared=tuple(device_weights(sh, wf)), quant_out_dtype=FP8[cfg.fmt], debug=True,
-                              weight_format=wf, activation=ACT_KIND[kind], activation_params=params)
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights(weights, wf))
+    kw = dict(shared=tuple(device_weights(sh, wf)), quant_out_dtype=FP8[cfg.fmt], weight_format=wf,
+              activation=ACT_KIND[kind], activation_params=params)
+    y, etn, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y_fast, etn_fast = rp.mega_moe(*args, **kw)
     torch.cuda.synchronize()
+    assert_same_layer(y_fast, etn_fast, y, etn)
     act = (kind, params)
     ref = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=[tuple(a[0] for a in sh)], act=act)
     assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
@@ -290,10 +310,13 @@ def test_a8w4(case, wf):
         shared_dev, swd = tuple(device_weights(sh, wf)), rp.FP8_E4M3
     if sh_kind:
         shared_np = [tuple(a[0] for a in sh)]
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights_fp4(weights, wf),
-                              shared=shared_dev, quant_out_dtype=rp.FP8_E4M3, debug=True, weight_format=wf,
-                              weight_dtype=rp.FP4_E2M1, shared_weight_dtype=swd)
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *device_weights_fp4(weights, wf))
+    kw = dict(shared=shared_dev, quant_out_dtype=rp.FP8_E4M3, weight_format=wf, weight_dtype=rp.FP4_E2M1,
+              shared_weight_dtype=swd)
+    y, etn, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y_fast, etn_fast = rp.mega_moe(*args, **kw)
     torch.cuda.synchronize()
+    assert_same_layer(y_fast, etn_fast, y, etn)
     ref = moe.mega_moe(x, ids, w, weights, "e4m3", cfg.experts, shared=shared_np, wfmt="e2m1",
                        shared_wfmt="e4m3" if sh_kind == "fp8" else "e2m1")
     assert np.array_equal(dbg["xq"].cpu().numpy(), ref["xq"])
@@ -367,22 +390,111 @@ def test_shared_expert_alone(tokens, hidden, inter):
     assert mx <= 2e-2 and mean <= 5e-3
 
 
-def test_repeated_calls_reuse_workspace():
-    cfg = moe_inputs.config("tiny", seed=45)
-    say("mega_moe repeated calls")
+@pytest.mark.parametrize("name", ["tiny", "wide"])
+def test_repeated_calls_reuse_workspace(name):
+    """Two calls on one preallocated workspace (the second finds the first's leftovers in
+    it) give the same Y bit for bit: the layer has no atomics and a fixed summation order."""
+    if name == "tiny":
+        cfg = moe_inputs.config("tiny", seed=45)
+    else:   # 18-tile chunks and a shared expert
+        cfg = moe_inputs.config("tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, shared=1, seed=45)
+    say(f"mega_moe repeated calls on one workspace ({name})")
     ids = to_dev(moe_inputs.expert_ids(cfg).astype(np.int32))
     x = moe_inputs.activations(cfg).to(DEV)
     w = to_dev(moe_inputs.gate_weights(cfg))
-    weights = [to_dev(a) for a in oracle_weights(cfg)]
-    y1, e1 = rp.mega_moe(x, ids, w, *weights)
-    y2, e2 = rp.mega_moe(x, ids, w, *weights)
+    weights = device_weights(oracle_weights(cfg), rp.WEIGHTS_PACKED)
+    shared = tuple(device_weights(oracle_weights(cfg, cfg.shared, shared=True), rp.WEIGHTS_PACKED)) \
+        if cfg.shared else None
+    kw = dict(shared=shared, weight_format=rp.WEIGHTS_PACKED)
+    ws = torch.empty(rp.mega_moe_workspace_bytes(x, ids, w, *weights, **kw), dtype=torch.uint8, device=DEV)
+    ws.fill_(0xA5)
+    y1, e1 = rp.mega_moe(x, ids, w, *weights, workspace=ws, **kw)
+    y1 = y1.clone()
+    y2, e2 = rp.mega_moe(x, ids, w, *weights, workspace=ws, **kw)
     torch.cuda.synchronize()
     assert torch.equal(e1, e2)
-    d = (y1.float() - y2.float()).abs().max().item()
-    assert d <= 2e-2 * y1.float().abs().max().item()
+    assert torch.equal(y1, y2)
 
 
-def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True, wf=rp.WEIGHTS_ND):
+ORACLE_THREADS = min(16, os.cpu_count() or 1)
+
+
+def sample_tokens(ids, counts, n_random, special, seed):
+    """n_random tokens at random plus, for each special expert, the first token routed to it
+    that is not chosen yet (so every special expert's rows reach the sampled Y)."""
+    rng = np.random.default_rng(seed)
+    chosen = [int(t) for t in rng.choice(ids.shape[0], size=n_random, replace=False)]
+    for e in special:
+        for t in np.nonzero((ids == e).any(axis=1))[0]:
+            if int(t) not in chosen:
+                chosen.append(int(t))
+                break
+    return np.array(sorted(chosen))
+
+
+def check_expert_rows(cfg, e, lo, hi, q, x, r, dbg):
+    """Every row of expert e: X^ / S_X bit for bit, h1 within 2e-3 normwise and the
+    elementwise bound, the requantized A^ a valid MX quantization of the oracle's A.
+    Returns the oracle's A^ / S_A and O of the rows (oracle operands only)."""
+    xq_rows = dbg["xq"][lo:hi].cpu().numpy()
+    sx_rows = dbg["sx"][lo:hi].cpu().numpy()
+    src = r["sorted_row_idx"][lo:hi] // cfg.topk
+    xq_o, sx_o = mxfp.quantize(x[src], cfg.fmt)
+    assert np.array_equal(xq_rows, xq_o) and np.array_equal(sx_rows, sx_o)
+    ffn = moe.expert_ffn(xq_o, sx_o, *q, cfg.fmt)
+    h1_abs = abs_gmm(xq_o, sx_o, q[0], q[1], cfg.fmt)
+    h1_got = dbg["h1"][lo:hi].cpu().numpy()
+    err_e = normwise_err(h1_got, ffn["h1"])
+    check_gemm_elementwise(h1_got, ffn["h1"], h1_abs, cfg.hidden)
+    delta = swiglu_delta(ffn["h1"], h1_abs, cfg.hidden, cfg.inter)
+    codes, scales = check_requant(dbg["aq"][lo:hi].cpu().numpy(), dbg["sa"][lo:hi].cpu().numpy(), ffn["a"], delta,
+                                  cfg.fmt)
+    say(f"  expert {e} ({hi - lo} rows): h1 err {err_e:.3g}, requant codes differing {codes:.3g} "
+        f"scales {scales:.3g}")
+    assert err_e <= 2e-3
+    return ffn
+
+
+def check_gmm2_rows(cfg, experts, ffns, cache, wf):
+    """GMM2 on the oracle's own A^ of every row of `experts` (stage entry point, the same
+    kernels as the layer): O row by row within 2e-3 normwise and the elementwise bound,
+    every output channel included (the partial last channel block of hidden 7168)."""
+    aq = np.concatenate([ffns[e]["aq"] for e in experts])
+    sa = np.concatenate([ffns[e]["sa"][:, :cfg.inter // 32] for e in experts])
+    o_ref = np.concatenate([ffns[e]["o"] for e in experts])
+    offs = np.zeros(len(experts) + 1, np.int32)
+    offs[1:] = np.cumsum([ffns[e]["aq"].shape[0] for e in experts])
+    w2q = to_dev(np.stack([cache[e][2] for e in experts]))
+    w2s = to_dev(np.stack([cache[e][3] for e in experts]))
+    if wf == rp.WEIGHTS_PACKED:
+        w2q, w2s = rp.pack_weights(w2q, w2s)
+    rows = aq.shape[0]
+    y_acc = torch.zeros((rows, cfg.hidden), dtype=torch.float32, device=DEV)
+    o = rp.gmm2_combine(to_dev(aq), to_dev(sa), to_dev(offs), w2q, w2s, to_dev(np.arange(rows, dtype=np.int32)),
+                        to_dev(np.ones(rows, np.float32)), y_acc, FP8[cfg.fmt], True, weight_format=wf)
+    torch.cuda.synchronize()
+    o_got = o.cpu().numpy()
+    o_abs = np.concatenate([abs_gmm(ffns[e]["aq"], ffns[e]["sa"], cache[e][2], cache[e][3], cfg.fmt)
+                            for e in experts])
+    err = normwise_err(o_got, o_ref)
+    worst = max(normwise_err(o_got[offs[j]:offs[j + 1]], o_ref[offs[j]:offs[j + 1]]) for j in range(len(experts)))
+    ex = check_gemm_elementwise(o_got, o_ref, o_abs, cfg.inter)
+    say(f"  GMM2 on the oracle's A^ of experts {list(experts)} ({rows} rows): O err {err:.3g} "
+        f"(worst expert {worst:.3g}), elementwise bound use {ex:.3g}")
+    assert err <= 2e-3 and worst <= 2e-3
+
+
+def full_size_check(name, n_random, wf=rp.WEIGHTS_ND, seed=7):
+    """The layer at full size in the benchmark's configuration (weights made on the GPU
+    and quantized by the library):
+    * the plain call (the kernel instances the benchmark times) equals the debug call
+      bit for bit;
+    * routing, counts and the sampled rows' X^ / S_X exact;
+    * the special experts (the busiest one, every expert whose rows take more than one
+      GEMM chunk, the least busy one): all their rows through GMM1 (h1, A^) and GMM2 (O
+      from the oracle's A^);
+    * Y of the sampled tokens (random ones plus one routed to each special expert) from
+      the oracle's layer on those tokens."""
     cfg = moe_inputs.config(name)
     say(f"mega_moe full size {name}: N={cfg.tokens} H={cfg.hidden} I={cfg.inter} E={cfg.experts} K={cfg.topk} "
         f"S={cfg.shared} fmt={cfg.fmt}")
@@ -398,63 +510,57 @@ def full_size_check(name, n_tokens_sampled=1, check_expert_rows=True, wf=rp.WEIG
         dev_w = [*rp.pack_weights(weights[0], weights[1]), *rp.pack_weights(weights[2], weights[3])]
         if shared is not None:
             dev_sh = (*rp.pack_weights(shared[0], shared[1]), *rp.pack_weights(shared[2], shared[3]))
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w, shared=dev_sh,
-                              quant_out_dtype=FP8[cfg.fmt], debug=True, weight_format=wf)
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w)
+    kw = dict(shared=dev_sh, quant_out_dtype=FP8[cfg.fmt], weight_format=wf)
+    y, etn, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y_fast, etn_fast = rp.mega_moe(*args, **kw)
     torch.cuda.synchronize()
-    say("  layer done")
+    say("  layer done (plain and debug calls)")
+    assert_same_layer(y_fast, etn_fast, y, etn)
+    del y_fast
     r = routing.init_routing(ids, cfg.experts)
-    assert np.array_equal(etn.cpu().numpy(), r["counts"].astype(np.int32))
+    counts = r["counts"]
+    assert np.array_equal(etn.cpu().numpy(), counts.astype(np.int32))
     assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), r["sorted_row_idx"])
-    rng = np.random.default_rng(7)
-    tokens = rng.choice(cfg.tokens, size=n_tokens_sampled, replace=False)
-    busiest = int(np.argmax(r["counts"]))
-    needed = sorted(set(int(e) for e in ids[tokens].reshape(-1)) | {busiest})
-    cache = oracle_experts_parallel(cfg, needed)
+    busiest = int(np.argmax(counts))
+    nonempty = np.nonzero(counts)[0]
+    least = int(nonempty[np.argmin(counts[nonempty])])
+    multi = [int(e) for e in np.argsort(-counts, kind="stable")[:8] if counts[e] > 256]
+    special = sorted(set([busiest, least] + multi))
+    tokens = sample_tokens(ids, counts, n_random, special, seed)
+    needed = sorted(set(int(e) for e in ids[tokens].reshape(-1)) | set(special))
+    cache = oracle_experts_parallel(cfg, needed, workers=ORACLE_THREADS)
     for e in needed:   # the library's weight bytes equal the oracle's quantization of the same masters
         for j in range(4):
             assert np.array_equal(weights[j][e].cpu().numpy(), cache[e][j]), (e, j)
-
-    def expert(e):
-        return cache[e]
-
     shared_np = [oracle_expert_from_gpu_masters(cfg, s, shared=True) for s in range(cfg.shared)]
-    say(f"  oracle weights ready ({len(needed)} experts)")
+    say(f"  oracle weights ready ({len(needed)} experts); special experts {special} "
+        f"with {[int(counts[e]) for e in special]} rows")
     x = x_t.double().numpy()
-    ref = moe.per_token(x, ids, w, expert, cfg.fmt, tokens, shared=shared_np)
+    ffns = {}
+    for e in special:
+        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
+        ffns[e] = check_expert_rows(cfg, e, lo, hi, cache[e], x, r, dbg)
+    check_gmm2_rows(cfg, special, ffns, cache, wf)
+    # Y of the sampled tokens: the oracle's layer on those tokens alone (each token's Y
+    # depends only on its own row and experts)
+    ref = moe.mega_moe(x[tokens], ids[tokens], w[tokens], lambda e: cache[e], cfg.fmt, cfg.experts,
+                       shared=shared_np, workers=ORACLE_THREADS)
     y_got = y[torch.from_numpy(tokens).to(DEV)].cpu().double().numpy()
     mx, mean = y_errors(y_got, ref["y"])
-    inv = routing.inverse(r["sorted_row_idx"]).reshape(cfg.tokens, cfg.topk)
-    pos = inv[tokens].reshape(-1)
-    h1_got = dbg["h1"][torch.from_numpy(pos).to(DEV)].cpu().numpy()
-    err = normwise_err(h1_got, ref["h1"].reshape(len(pos), -1))
-    xq_ref, sx_ref = mxfp.quantize(x[tokens], cfg.fmt)
-    assert np.array_equal(dbg["xq"][torch.from_numpy(pos).to(DEV)].cpu().numpy(), np.repeat(xq_ref, cfg.topk, axis=0))
-    assert np.array_equal(dbg["sx"][torch.from_numpy(pos).to(DEV)].cpu().numpy(), np.repeat(sx_ref, cfg.topk, axis=0))
-    say(f"  sampled tokens {tokens.tolist()}: Y max {mx:.3g} mean {mean:.3g}, h1 err {err:.3g}")
+    # h1 / X^ rows of the sampled tokens: position in the full layer vs in the sub-layer
+    inv = routing.inverse(r["sorted_row_idx"])
+    inv_sub = routing.inverse(ref["routing"]["sorted_row_idx"])
+    flat_full = (tokens[:, None] * cfg.topk + np.arange(cfg.topk)[None, :]).reshape(-1)
+    pos = inv[flat_full]
+    pos_sub = inv_sub[np.arange(len(tokens) * cfg.topk)]
+    idx = torch.from_numpy(pos).to(DEV)
+    assert np.array_equal(dbg["xq"][idx].cpu().numpy(), ref["xq"][pos_sub])
+    assert np.array_equal(dbg["sx"][idx].cpu().numpy(), ref["sx"][pos_sub])
+    err = normwise_err(dbg["h1"][idx].cpu().numpy(), ref["h1"][pos_sub])
+    say(f"  {len(tokens)} sampled tokens: Y max {mx:.3g} mean {mean:.3g}, h1 err {err:.3g}")
     assert err <= 2e-3
     assert mx <= 2e-2 and mean <= 5e-3
-    if check_expert_rows:
-        # every row of the busiest expert: h1 of the whole group (largest tile count)
-        e = busiest
-        lo, hi = int(r["offsets"][e]), int(r["offsets"][e + 1])
-        q = expert(e)
-        xq_rows = dbg["xq"][lo:hi].cpu().numpy()
-        sx_rows = dbg["sx"][lo:hi].cpu().numpy()
-        src = r["sorted_row_idx"][lo:hi] // cfg.topk
-        xq_o, sx_o = mxfp.quantize(x[src], cfg.fmt)
-        assert np.array_equal(xq_rows, xq_o) and np.array_equal(sx_rows, sx_o)
-        h1_ref = moe.gmm(xq_o, sx_o, q[0], q[1], cfg.fmt)
-        h1_abs = abs_gmm(xq_o, sx_o, q[0], q[1], cfg.fmt)
-        h1_got = dbg["h1"][lo:hi].cpu().numpy()
-        err_e = normwise_err(h1_got, h1_ref)
-        check_gemm_elementwise(h1_got, h1_ref, h1_abs, cfg.hidden)
-        a_ref = mxfp.fp32_round(moe.swiglu(h1_ref[:, :cfg.inter], h1_ref[:, cfg.inter:]))
-        delta = swiglu_delta(h1_ref, h1_abs, cfg.hidden, cfg.inter)
-        codes, scales = check_requant(dbg["aq"][lo:hi].cpu().numpy(), dbg["sa"][lo:hi].cpu().numpy(), a_ref, delta,
-                                      cfg.fmt)
-        say(f"  expert {e} ({hi - lo} rows): h1 err {err_e:.3g}, requant codes differing {codes:.3g} "
-            f"scales {scales:.3g}")
-        assert err_e <= 2e-3
 
 
 @pytest.mark.timeout(900)
@@ -470,16 +576,18 @@ def test_full_size_decode_a8w4():
     weights = library_weights(cfg, fp4=True)
     dev_w = [*rp.pack_weights(weights[0], weights[1], fp4=True), *rp.pack_weights(weights[2], weights[3], fp4=True)]
     say("  weights ready")
-    y, etn, dbg = rp.mega_moe(x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w,
-                              quant_out_dtype=rp.FP8_E4M3, debug=True, weight_format=rp.WEIGHTS_PACKED,
-                              weight_dtype=rp.FP4_E2M1)
+    args = (x_t.to(DEV), to_dev(ids.astype(np.int32)), to_dev(w), *dev_w)
+    kw = dict(quant_out_dtype=rp.FP8_E4M3, weight_format=rp.WEIGHTS_PACKED, weight_dtype=rp.FP4_E2M1)
+    y, etn, dbg = rp.mega_moe(*args, debug=True, **kw)
+    y_fast, etn_fast = rp.mega_moe(*args, **kw)
     torch.cuda.synchronize()
+    assert_same_layer(y_fast, etn_fast, y, etn)
     r = routing.init_routing(ids, cfg.experts)
     assert np.array_equal(dbg["sorted_row_idx"].cpu().numpy(), r["sorted_row_idx"])
     rng = np.random.default_rng(8)
     tokens = rng.choice(cfg.tokens, size=4, replace=False)
     needed = sorted(set(int(e) for e in ids[tokens].reshape(-1)))
-    cache = oracle_experts_parallel(cfg, needed, fp4=True)
+    cache = oracle_experts_parallel(cfg, needed, fp4=True, workers=ORACLE_THREADS)
     for e in needed:
         for j in range(4):
             assert np.array_equal(weights[j][e].cpu().numpy(), cache[e][j]), (e, j)
@@ -498,14 +606,14 @@ def test_full_size_decode_a8w4():
 
 @pytest.mark.timeout(900)
 def test_full_size_decode():
-    full_size_check("decode", n_tokens_sampled=4, wf=rp.WEIGHTS_PACKED)
+    full_size_check("decode", n_random=8, wf=rp.WEIGHTS_PACKED)
 
 
 @pytest.mark.timeout(900)
 def test_full_size_skewed():
-    full_size_check("skewed", n_tokens_sampled=6)
+    full_size_check("skewed", n_random=32)
 
 
 @pytest.mark.timeout(900)
 def test_full_size_prefill():
-    full_size_check("prefill", n_tokens_sampled=3, wf=rp.WEIGHTS_PACKED)
+    full_size_check("prefill", n_random=6, wf=rp.WEIGHTS_PACKED)

@@ -191,6 +191,23 @@ def test_brute_force_equals_permuted_layer_bitwise(mode):
     assert np.array_equal(full["y"], mxfp.bf16_round(full["y"]))
 
 
+def test_sub_batch_and_threaded_experts_match_the_whole_layer():
+    """The layer on a subset of the tokens gives those tokens' Y of the whole layer bit
+    for bit (each token depends only on its own row and experts), and evaluating the
+    experts in threads changes nothing: the full-size GPU tests use both."""
+    cfg = moe_inputs.config("tiny", tokens=96, experts=8, topk=3, shared=1, seed=77)
+    x, ids, w = layer_inputs(cfg)
+    weights = quantized_weights(cfg)
+    shared = [tuple(a[0] for a in quantized_weights(cfg, 1, shared=True))]
+    full = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared)
+    threaded = moe.mega_moe(x, ids, w, weights, cfg.fmt, cfg.experts, shared=shared, workers=4)
+    for key in ("y", "h1", "a", "aq", "sa", "o"):
+        assert np.array_equal(full[key], threaded[key]), key
+    tokens = np.array([3, 17, 40, 41, 95])
+    sub = moe.mega_moe(x[tokens], ids[tokens], w[tokens], weights, cfg.fmt, cfg.experts, shared=shared, workers=3)
+    assert np.array_equal(sub["y"], full["y"][tokens])
+
+
 @pytest.mark.parametrize("mode", [0, 1])
 def test_topk_one_unit_weight_is_plain_unpermute(mode):
     """K = 1, w = 1, no shared expert: Y is the unpermuted O rounded to bf16 in both

@@ -189,8 +189,9 @@ def mega_moe(x, topk_ids, topk_weights, weights, fmt, num_experts, shared=(), ac
     else:
         parts = dict(run(e) for e in busy)
     hidden = x.shape[1]
-    two_i = get(0)[0].shape[0]
-    aw = get(0)[2].shape[1] * (2 if wfmt == "e2m1" else 1)   # width of A: I (gated) or 2I (gelu)
+    shape_of = get(busy[0] if busy else 0)   # any expert's weights give the widths
+    two_i = shape_of[0].shape[0]
+    aw = shape_of[2].shape[1] * (2 if wfmt == "e2m1" else 1)   # width of A: I (gated) or 2I (gelu)
     out = dict(routing=r, xq=xq, sx=sx,
                h1=np.zeros((flat, two_i)), a=np.zeros((flat, aw)),
                aq=np.zeros((flat, aw), np.uint8),

@@ -206,6 +206,11 @@ def test_sub_batch_and_threaded_experts_match_the_whole_layer():
     tokens = np.array([3, 17, 40, 41, 95])
     sub = moe.mega_moe(x[tokens], ids[tokens], w[tokens], weights, cfg.fmt, cfg.experts, shared=shared, workers=3)
     assert np.array_equal(sub["y"], full["y"][tokens])
+    # a getter that knows only the experts the sub-batch uses
+    used = set(int(e) for e in ids[tokens].reshape(-1))
+    only = {e: tuple(a[e] for a in weights) for e in used}
+    sub2 = moe.mega_moe(x[tokens], ids[tokens], w[tokens], lambda e: only[e], cfg.fmt, cfg.experts, shared=shared)
+    assert np.array_equal(sub2["y"], full["y"][tokens])
 
 
 @pytest.mark.parametrize("mode", [0, 1])

@@ -99,7 +99,9 @@ bool valid_quant_mode(int q) {
 
 bool valid_x_dtype(int d) { return d == MOE_DTYPE_FP32 || d == MOE_DTYPE_FP16 || d == MOE_DTYPE_BF16; }
 
-int token_tile_tt(int64_t rows, int64_t groups) { return moe::gmm_token_tiles(rows, groups); }
+int token_tile_tt(int64_t rows, int64_t groups, int64_t hidden, int64_t inter, int64_t aw) {
+  return moe::gmm_token_tiles(rows, groups, hidden, inter, aw);
+}
 
 // Scale bytes of one weight group (N output channels, K inputs) in a weight format.
 int64_t group_scale_bytes(int64_t n, int64_t k, int format) {
@@ -179,7 +181,7 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.gath = a->sorted_row_idx ? nullptr : cv.take<int32_t>(flat);
   w.row_token = cv.take<int32_t>(flat);
   w.row_weight = cv.take<float>(flat);
-  w.tt = token_tile_tt(flat, e);
+  w.tt = token_tile_tt(flat, e, h, a->inter, i);
   w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.tile_count = cv.take<int>(1);
@@ -193,7 +195,7 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.aq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, i));
   w.sa = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, i));
   if (a->num_shared > 0) {
-    w.sh_tt = token_tile_tt(n, 1);
+    w.sh_tt = token_tile_tt(n, 1, h, a->inter, i);
     w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
     w.sh_tiles = cv.take<int4>(w.sh_max_tiles);
     w.sh_count = cv.take<int>(1);
@@ -343,7 +345,7 @@ struct GmmWs {
 
 GmmWs carve_gmm(Carver& cv, int64_t rows, int64_t groups, int64_t hidden, int64_t inter) {
   GmmWs w;
-  w.tt = token_tile_tt(rows, groups);
+  w.tt = token_tile_tt(rows, groups, hidden, inter, inter);
   w.max_tiles = (int)(rows / (16 * w.tt) + groups + 1);
   w.tiles = cv.take<int4>(w.max_tiles);
   w.count = cv.take<int>(1);

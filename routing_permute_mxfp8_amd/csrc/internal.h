@@ -119,7 +119,7 @@ struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
   const int4* tiles; const int* tile_count; int max_tiles;
-  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, 16, 18)
+  int hidden, inter, fmt, tt;                  // tt = 16-row token tiles per chunk (1, 2, 4, 8, kStreamTiles)
   uint8_t* aq; uint8_t* sa;                    // tiled [padded rows, I] (2I for gelu)
   float* h1;                                   // nullable [rows, 2I]
   int packed;                                  // weights in the MFMA-native packed layout
@@ -140,8 +140,15 @@ struct Gmm2Params {
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 
-// Token tiles (16 rows each) per chunk for `rows` rows over `groups` groups.
-int gmm_token_tiles(int64_t rows, int64_t groups);
+// Token tiles (16 rows each) per chunk for `rows` rows over `groups` groups of an FFN of
+// width hidden x inter (A of width aw): 1, 2, 4 or 8 (the register-streaming kernels of
+// gmm.hip), or kStreamTiles (the LDS-streaming kernels of gmm_stream.hip) for layers whose
+// experts hold more than 128 rows on average, when both GEMMs have a multiple of 4
+// 128-wide K steps and one expert's weights stay below 2 GiB.
+int gmm_token_tiles(int64_t rows, int64_t groups, int64_t hidden, int64_t inter, int64_t aw);
+constexpr int kStreamTiles = 20;
+hipError_t launch_gmm1_stream(const Gmm1Params& p, hipStream_t stream);
+hipError_t launch_gmm2_stream(const Gmm2Params& p, hipStream_t stream);
 
 // codes [G, N, K] + scales [G, N, K/32] -> MFMA-native packed codes (same size) and
 // packed scales [G, N/16, ceil(K/512), 64, 4].

@@ -34,7 +34,9 @@ CASES = [
     dict(name="tiny", tokens=300, hidden=384, inter=256, experts=13, topk=3, seed=21),   # ragged groups
     dict(name="skewed", tokens=700, hidden=512, inter=384, experts=24, topk=4, seed=22),  # zipf, E5M2, big groups
     dict(name="tiny", tokens=16, hidden=256, inter=128, experts=64, topk=6, seed=23),    # many empty groups
-    dict(name="tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, seed=24),    # ~256 rows a group: 288-row chunks
+    dict(name="tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, seed=24),    # ~256 rows a group, odd K steps
+    dict(name="tiny", tokens=600, hidden=512, inter=512, experts=5, topk=3, seed=25),    # LDS-streaming: 2 chunks a group
+    dict(name="skewed", tokens=900, hidden=1024, inter=512, experts=12, topk=2, seed=26),  # LDS-streaming, skewed groups
 ]
 
 

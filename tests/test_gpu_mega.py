@@ -30,8 +30,15 @@ SMALL = [
     dict(name="tiny", tokens=333, hidden=512, inter=256, experts=16, topk=4, shared=2, seed=42),
     dict(name="skewed", tokens=500, hidden=384, inter=384, experts=20, topk=5, seed=43),
     dict(name="tiny", tokens=5, hidden=256, inter=128, experts=32, topk=8, seed=44),
-    # ~256 rows per expert: both GEMMs in 288-row chunks (GMM2 with 48 channels a wave, a partial last block)
+    # ~256 rows per expert, inter 128 (an odd number of 128-wide K steps in GMM2): 128-row chunks
     dict(name="tiny", tokens=512, hidden=256, inter=128, experts=8, topk=4, shared=1, seed=45),
+    # LDS-streaming GEMMs (more than 128 rows per expert, K steps a multiple of 4): ~350 rows per expert
+    # (two chunks each), partial last channel blocks in both GEMMs (GMM1 2 of 6 gate tiles,
+    # GMM2 8 of 12 output tiles), a shared expert over all tokens
+    dict(name="tiny", tokens=700, hidden=512, inter=512, experts=6, topk=3, shared=1, seed=57),
+    # LDS-streaming, Zipf-skewed: experts from a few rows (token tiles some waves do not
+    # own) to several chunks
+    dict(name="skewed", tokens=1500, hidden=1024, inter=512, experts=16, topk=2, seed=58),
 ]
 
 

@@ -181,6 +181,27 @@ moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, in
                             void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* moe_init_routing_noalloc: moe_init_routing without a workspace, for callers */
+/* that cannot allocate device memory (code under HIP graph capture, tight     */
+/* serving loops, harnesses that forbid hipMalloc). Same arguments, outputs,    */
+/* kernels and results as moe_init_routing; its scratch is a static array of    */
+/* 8 MiB (8388608 bytes) that each GPU holds from the library's load until the  */
+/* process ends. The call allocates nothing (no hipMalloc / hipFree). A call     */
+/* whose scratch would exceed 8 MiB returns MOE_ERR_SHAPE before any launch (the */
+/* message gives the bytes it needs); any call whose moe_init_routing_workspace_ */
+/* size is at most 8388608 fits (e.g. num_rows*k up to 1397696 with 256 experts). */
+/* Every call on one GPU shares that GPU's array and leaves its contents behind  */
+/* (nothing in it needs to start at zero): calls that overlap on one GPU (other  */
+/* streams, other threads) race and must be ordered by the caller.             */
+/* ------------------------------------------------------------------------ */
+moe_status moe_init_routing_noalloc(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows,
+                                    int64_t hidden, const int32_t* expert_idx, int64_t k, int64_t expert_num,
+                                    int64_t active_start, int64_t active_end, int quant_mode, int row_idx_type,
+                                    int expert_tokens_num_type, void* expanded_x, int32_t* expanded_row_idx,
+                                    int64_t* expert_tokens, uint8_t* expanded_scale, int64_t* available_idx_num,
+                                    void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* moe_token_permute  ([TP] 功能说明 / 返回值说明, padded_mode = False).        */
 /*   tokens        device, [n, hidden] of dtype (BF16, FP16; FP32 too for -1)  */
 /*   indices       device, int32 or int64 (indices_dtype) [n] (topk = 1) or     */

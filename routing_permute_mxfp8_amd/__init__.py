@@ -22,7 +22,7 @@ from .build import lib_path
 
 __all__ = [
     "MoeError", "load", "QUANT_NONE", "QUANT_E5M2", "QUANT_E4M3", "QUANT_MXFP4", "FP8_E5M2", "FP8_E4M3",
-    "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "token_permute",
+    "mx_scale_cols", "token_permute_out_rows", "mx_quantize", "init_routing", "init_routing_noalloc", "token_permute",
     "mega_moe", "mega_moe_workspace_bytes", "gmm1_swiglu_quant", "gmm2_combine", "combine_finalize",
     "pack_weights", "WEIGHTS_ND", "WEIGHTS_PACKED", "DTYPE_FP8_E5M2", "DTYPE_FP8_E4M3", "DTYPE_FP4_E2M1",
 ]
@@ -87,6 +87,8 @@ _SIGS = {
     "moe_init_routing_workspace_size": ([_I64, _I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_init_routing": ([_VP, _INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
                           _VP, _VP, _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
+    "moe_init_routing_noalloc": ([_VP, _INT, _VP, _I64, _I64, _VP, _I64, _I64, _I64, _I64, _INT, _INT, _INT,
+                                  _VP, _VP, _VP, _VP, _VP, _VP], _INT),
     "moe_token_permute_workspace_size": ([_I64, _I64, ctypes.POINTER(_SZ)], _INT),
     "moe_token_permute": ([_VP, _INT, _I64, _I64, _VP, _INT, _I64, _I64, _I64, _INT, _INT,
                            _VP, _VP, _VP, _VP, _SZ, _VP], _INT),
@@ -189,6 +191,41 @@ def pack_weights(codes, scales, fp4: bool = False):
     return pc, ps
 
 
+def init_routing_noalloc(x, expert_idx, expert_num: int, active_range=None, quant_mode: int = QUANT_NONE,
+                         row_idx_type: int = 1, expert_tokens_num_type: int = 1):
+    """init_routing through moe_init_routing_noalloc: the library takes no workspace (its
+    scratch is a static per-GPU array of 8 MiB; larger calls raise MoeError). The outputs
+    are allocated here, as for init_routing; the same results."""
+    lib = load()
+    _need_gpu(x, expert_idx)
+    if expert_idx.dtype != torch.int32 or expert_idx.dim() != 2 or expert_idx.shape[0] != x.shape[0]:
+        raise ValueError("expert_idx must be int32 [N, K] with N = x.shape[0]")
+    n, h = x.shape
+    k = expert_idx.shape[1]
+    s, e = (0, expert_num) if active_range is None else active_range
+    ex, idx, tok, sc, avail = _routing_outputs(x, n, h, k, expert_num, s, e, quant_mode, expert_tokens_num_type)
+    _check(lib.moe_init_routing_noalloc(_ptr(x), _DT[x.dtype], None, n, h, _ptr(expert_idx), k, expert_num, s, e,
+                                        quant_mode, row_idx_type, expert_tokens_num_type, _ptr(ex), _ptr(idx),
+                                        _ptr(tok), _ptr(sc), _ptr(avail), _stream(x.device)))
+    return ex, idx, tok, sc, avail
+
+
+def _routing_outputs(x, n, h, k, expert_num, s, e, quant_mode, expert_tokens_num_type):
+    flat = n * k
+    mx = quant_mode != QUANT_NONE
+    dev = x.device
+    ex = torch.empty((flat, h // 2 if quant_mode == QUANT_MXFP4 else h), dtype=torch.uint8 if mx else x.dtype,
+                     device=dev)
+    idx = torch.empty((flat,), dtype=torch.int32, device=dev)
+    if expert_tokens_num_type == 2:   # key_value: (expert, count) rows
+        tok = torch.empty((expert_num, 2), dtype=torch.int64, device=dev)
+    else:
+        tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
+    sc = torch.empty((flat, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx else None
+    avail = torch.empty((1,), dtype=torch.int64, device=dev)
+    return ex, idx, tok, sc, avail
+
+
 def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: int = QUANT_NONE,
                  row_idx_type: int = 1, expert_tokens_num_type: int = 1, x_codes: int | None = None, scale=None):
     """MoeInitRoutingV3 (dropless). Returns (expanded_x, expanded_row_idx, expert_tokens,
@@ -208,18 +245,8 @@ def init_routing(x, expert_idx, expert_num: int, active_range=None, quant_mode: 
                                    expert_tokens_num_type, x_codes, scale)
     k = expert_idx.shape[1]
     s, e = (0, expert_num) if active_range is None else active_range
-    flat = n * k
-    mx = quant_mode != QUANT_NONE
     dev = x.device
-    ex = torch.empty((flat, h // 2 if quant_mode == QUANT_MXFP4 else h), dtype=torch.uint8 if mx else x.dtype,
-                     device=dev)
-    idx = torch.empty((flat,), dtype=torch.int32, device=dev)
-    if expert_tokens_num_type == 2:   # key_value: (expert, count) rows
-        tok = torch.empty((expert_num, 2), dtype=torch.int64, device=dev)
-    else:
-        tok = torch.empty((max(e - s, 0),), dtype=torch.int64, device=dev)
-    sc = torch.empty((flat, mx_scale_cols(h)), dtype=torch.uint8, device=dev) if mx else None
-    avail = torch.empty((1,), dtype=torch.int64, device=dev)
+    ex, idx, tok, sc, avail = _routing_outputs(x, n, h, k, expert_num, s, e, quant_mode, expert_tokens_num_type)
     nbytes = ctypes.c_size_t()
     _check(lib.moe_init_routing_workspace_size(n, k, expert_num, ctypes.byref(nbytes)))
     ws = _workspace(nbytes.value, dev)

@@ -11,7 +11,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 LIB_NAME = "libmoe_mx.so"
 SOURCES = ["csrc/api.cpp", "csrc/routing.hip", "csrc/permute_quant.hip", "csrc/tiles.hip", "csrc/gmm.hip",
-           "csrc/gmm_stream.hip", "csrc/combine.hip", "csrc/peaks.hip"]
+           "csrc/gmm_stream.hip", "csrc/combine.hip", "csrc/peaks.hip", "csrc/noalloc.hip"]
 ARCH = os.environ.get("MOE_MX_ARCH", "gfx950")
 
 

@@ -440,13 +440,18 @@ moe_status moe_init_routing_workspace_size(int64_t num_rows, int64_t k, int64_t 
   return ok();
 }
 
-moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows, int64_t hidden,
-                            const int32_t* expert_idx,
-                            int64_t k, int64_t expert_num, int64_t active_start, int64_t active_end, int quant_mode,
-                            int row_idx_type, int expert_tokens_num_type, void* expanded_x,
-                            int32_t* expanded_row_idx, int64_t* expert_tokens, uint8_t* expanded_scale,
-                            int64_t* available_idx_num, void* workspace, size_t workspace_bytes, void* stream) {
-  const char* who = "moe_init_routing";
+}  // extern "C"
+
+namespace {
+
+// moe_init_routing and moe_init_routing_noalloc: with noalloc the scratch is the
+// library's static per-device array (its size checked here) instead of `workspace`.
+moe_status init_routing_impl(const char* who, bool noalloc, const void* x, int x_dtype, const uint8_t* scale,
+                             int64_t num_rows, int64_t hidden, const int32_t* expert_idx, int64_t k,
+                             int64_t expert_num, int64_t active_start, int64_t active_end, int quant_mode,
+                             int row_idx_type, int expert_tokens_num_type, void* expanded_x,
+                             int32_t* expanded_row_idx, int64_t* expert_tokens, uint8_t* expanded_scale,
+                             int64_t* available_idx_num, void* workspace, size_t workspace_bytes, void* stream) {
   if (num_rows < 0 || hidden < 1) return fail(MOE_ERR_SHAPE, "%s: num_rows >= 0 and hidden >= 1 required", who);
   if (k < 1 || k > 64) return fail(MOE_ERR_SHAPE, "%s: k %lld outside [1, 64]", who, (long long)k);
   if (expert_num < 1 || expert_num > MOE_MAX_EXPERTS)
@@ -488,7 +493,16 @@ moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, in
   const bool want_gather = row_idx_type == MOE_ROW_IDX_GATHER;
   Carver cv(nullptr);
   carve_init_routing(cv, flat, active, want_gather);
-  if (moe_status st = check_ws(who, cv.off, workspace, workspace_bytes)) return st;
+  if (noalloc) {
+    if (cv.off > moe::kNoAllocScratchBytes)
+      return fail(MOE_ERR_SHAPE, "%s: needs %zu bytes of scratch, more than the %zu bytes of its static scratch",
+                  who, cv.off, moe::kNoAllocScratchBytes);
+    hipError_t e = moe::noalloc_scratch(&workspace);
+    if (e != hipSuccess) return hip_fail(e, "moe_init_routing_noalloc scratch lookup");
+    workspace_bytes = moe::kNoAllocScratchBytes;
+  } else if (moe_status st = check_ws(who, cv.off, workspace, workspace_bytes)) {
+    return st;
+  }
   Carver w(workspace);
   InitRoutingWs ws = carve_init_routing(w, flat, active, want_gather);
   hipStream_t st = (hipStream_t)stream;
@@ -526,6 +540,34 @@ moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, in
   e = moe::launch_permute(pp, st);
   if (e != hipSuccess) return hip_fail(e, "moe_init_routing permute launch");
   return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_init_routing(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows, int64_t hidden,
+                            const int32_t* expert_idx, int64_t k, int64_t expert_num, int64_t active_start,
+                            int64_t active_end, int quant_mode, int row_idx_type, int expert_tokens_num_type,
+                            void* expanded_x, int32_t* expanded_row_idx, int64_t* expert_tokens,
+                            uint8_t* expanded_scale, int64_t* available_idx_num, void* workspace,
+                            size_t workspace_bytes, void* stream) {
+  return init_routing_impl("moe_init_routing", false, x, x_dtype, scale, num_rows, hidden, expert_idx, k, expert_num,
+                           active_start, active_end, quant_mode, row_idx_type, expert_tokens_num_type, expanded_x,
+                           expanded_row_idx, expert_tokens, expanded_scale, available_idx_num, workspace,
+                           workspace_bytes, stream);
+}
+
+moe_status moe_init_routing_noalloc(const void* x, int x_dtype, const uint8_t* scale, int64_t num_rows,
+                                    int64_t hidden, const int32_t* expert_idx, int64_t k, int64_t expert_num,
+                                    int64_t active_start, int64_t active_end, int quant_mode, int row_idx_type,
+                                    int expert_tokens_num_type, void* expanded_x, int32_t* expanded_row_idx,
+                                    int64_t* expert_tokens, uint8_t* expanded_scale, int64_t* available_idx_num,
+                                    void* stream) {
+  return init_routing_impl("moe_init_routing_noalloc", true, x, x_dtype, scale, num_rows, hidden, expert_idx, k,
+                           expert_num, active_start, active_end, quant_mode, row_idx_type, expert_tokens_num_type,
+                           expanded_x, expanded_row_idx, expert_tokens, expanded_scale, available_idx_num, nullptr, 0,
+                           stream);
 }
 
 moe_status moe_token_permute_workspace_size(int64_t flat_rows, int64_t num_experts, size_t* bytes) {

@@ -188,6 +188,13 @@ hipError_t launch_scatter_add(const float* o, int64_t rows, int hidden, const in
 hipError_t launch_finalize(const float* acc, int64_t count, uint16_t* y, hipStream_t stream);
 
 
+// ---- static scratch of the allocation-free entry point (noalloc.hip) ---------------------
+// Bytes of the per-device scratch array moe_init_routing_noalloc uses instead of a
+// caller workspace.
+constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
+// Device address of this device's scratch array (looked up once per device and kept).
+hipError_t noalloc_scratch(void** out);
+
 // ---- measured peaks (peaks.hip) ------------------------------------------------------
 hipError_t launch_probe_stream(int copy, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 int probe_mfma_blocks();   // blocks of 256 threads the MFMA probe launches (one per CU)

@@ -206,3 +206,16 @@ def test_binding_rejects_dtypes_the_library_would_misread():
     for args in bad:
         with pytest.raises(ValueError):
             rp._check_layer_dtypes(*args)
+
+
+def test_noalloc_routing_rejects_oversized_calls_on_the_host(lib):
+    """moe_init_routing_noalloc: a call whose scratch exceeds its static 8 MiB array is
+    refused before the device is touched (MOE_ERR_SHAPE, bytes named); argument errors
+    come first, as for moe_init_routing."""
+    out = (FAKE, FAKE, FAKE, FAKE, FAKE)
+    st = lib.moe_init_routing_noalloc(FAKE, 2, None, 1 << 19, 32, FAKE, 8, 4096, 0, 4096, -1, 0, 1, *out, None)
+    assert st == 2 and "static scratch" in lib.moe_last_error().decode()
+    st = lib.moe_init_routing_noalloc(FAKE, 2, None, 16, 32, FAKE, 8, 64, 5, 3, -1, 0, 1, *out, None)
+    assert st == 2 and "active range" in lib.moe_last_error().decode()
+    b = ctypes.c_size_t()
+    assert lib.moe_init_routing_workspace_size(32768, 8, 256, ctypes.byref(b)) == 0 and b.value <= 8 << 20

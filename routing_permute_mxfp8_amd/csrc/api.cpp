@@ -137,6 +137,13 @@ struct MegaWs {
   int4* sh_tiles;
   int* sh_count;
   int sh_max_tiles, sh_tt;
+  // one shared expert folded into the routed experts' GEMM launches (LDS-streaming
+  // kernels for both, same weight type): its chunks follow the routed ones in `tiles`
+  // (all_count counts both) and its rows follow theirs in xq / sx / aq / sa (from padded
+  // row routed_padded) and in the O rows (from row flat); the *_sh buffers point there
+  bool fold;
+  int* all_count;
+  int64_t routed_padded;
   // x quantized once in token order (row-major codes [tokens, hidden] and scales
   // [tokens, hidden/32]) when the gather re-reads many x rows; else null
   uint8_t* xrow;
@@ -183,34 +190,58 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
   w.row_weight = cv.take<float>(flat);
   w.tt = token_tile_tt(flat, e, h, a->inter, i);
   w.max_tiles = (int)(flat / (16 * w.tt) + e + 1);
-  w.tiles = cv.take<int4>(w.max_tiles);
+  const int64_t S = a->num_shared;
+  if (S > 0) {
+    w.sh_tt = token_tile_tt(n, 1, h, a->inter, i);
+    w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
+    const int sw = a->shared_weight_dtype ? a->shared_weight_dtype : a->weight_dtype;
+    // (not with the caller's o: it has room for the routed rows only)
+    w.fold = S == 1 && !a->o && w.tt == moe::kStreamTiles && w.sh_tt == moe::kStreamTiles &&
+             (sw == MOE_FP4_E2M1) == (a->weight_dtype == MOE_FP4_E2M1);
+  }
+  w.tiles = cv.take<int4>(w.max_tiles + (w.fold ? w.sh_max_tiles : 0));
   w.tile_count = cv.take<int>(1);
+  w.all_count = w.fold ? cv.take<int>(1) : nullptr;
   if (quantize_first(a)) {
     w.xrow = cv.take<uint8_t>((size_t)(n * h));
     w.xrow_s = cv.take<uint8_t>((size_t)(n * (h / 32)));
   }
   const int64_t padded = moe::t16_padded_rows(flat, e);
-  w.xq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, h));
-  w.sx = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, h));
-  w.aq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded, i));
-  w.sa = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded, i));
-  if (a->num_shared > 0) {
-    w.sh_tt = token_tile_tt(n, 1, h, a->inter, i);
-    w.sh_max_tiles = (int)((n + 16 * w.sh_tt - 1) / (16 * w.sh_tt));
+  const int64_t padded_sh = S > 0 ? moe::t16_padded_rows(n, 1) : 0;
+  const int64_t all_padded = padded + (w.fold ? padded_sh : 0);
+  w.routed_padded = padded;
+  w.xq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(all_padded, h));
+  w.sx = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(all_padded, h));
+  w.aq = cv.take<uint8_t>((size_t)moe::t16_code_bytes(all_padded, i));
+  w.sa = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(all_padded, i));
+  if (S > 0) {
     w.sh_tiles = cv.take<int4>(w.sh_max_tiles);
     w.sh_count = cv.take<int>(1);
-    const int64_t padded_sh = moe::t16_padded_rows(n, 1);
-    w.xq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, h));
-    w.sx_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, h));
-    w.aq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, i));
-    w.sa_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, i));
+    if (w.fold) {
+      w.xq_sh = w.xq + moe::t16_code_bytes(padded, h);
+      w.sx_sh = w.sx + moe::t16_scale_bytes(padded, h);
+      w.aq_sh = w.aq + moe::t16_code_bytes(padded, i);
+      w.sa_sh = w.sa + moe::t16_scale_bytes(padded, i);
+    } else {
+      w.xq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, h));
+      w.sx_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, h));
+      w.aq_sh = cv.take<uint8_t>((size_t)moe::t16_code_bytes(padded_sh, i));
+      w.sa_sh = cv.take<uint8_t>((size_t)moe::t16_scale_bytes(padded_sh, i));
+    }
   }
   const bool rows16 = a->combine_comm_mode == 0;
-  w.o = (a->o || rows16) ? nullptr : cv.take<float>((size_t)flat * h);
-  w.o16 = (a->o || !rows16) ? nullptr : cv.take<uint16_t>((size_t)flat * h);
-  const size_t nsh = (size_t)a->num_shared * n * h;
-  w.o_sh = a->num_shared > 0 && !rows16 ? cv.take<float>(nsh) : nullptr;
-  w.o16_sh = a->num_shared > 0 && rows16 ? cv.take<uint16_t>(nsh) : nullptr;
+  const size_t nsh = (size_t)S * n * h;
+  // folded: the shared expert's O rows follow the routed rows
+  const size_t orows = (size_t)flat * h + (w.fold ? nsh : 0);
+  w.o = (a->o || rows16) ? nullptr : cv.take<float>(orows);
+  w.o16 = (a->o || !rows16) ? nullptr : cv.take<uint16_t>(orows);
+  if (w.fold) {
+    w.o_sh = w.o ? w.o + (size_t)flat * h : nullptr;
+    w.o16_sh = w.o16 ? w.o16 + (size_t)flat * h : nullptr;
+  } else {
+    w.o_sh = S > 0 && !rows16 ? cv.take<float>(nsh) : nullptr;
+    w.o16_sh = S > 0 && rows16 ? cv.take<uint16_t>(nsh) : nullptr;
+  }
   return w;
 }
 
@@ -670,6 +701,11 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   if (n == 0) return ok();
   e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt, w.max_tiles, w.tiles, w.tile_count, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
+  if (w.fold) {
+    e = moe::launch_append_shared_tiles(w.tile_count, w.max_tiles, (int)n, 16 * w.sh_tt, (int)ne,
+                                        (int)w.routed_padded, (int)flat, w.tiles, w.all_count, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile list launch");
+  }
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
   // of the shared experts)
@@ -724,6 +760,11 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   const int swfp4 = (a->shared_weight_dtype ? a->shared_weight_dtype : a->weight_dtype) == MOE_FP4_E2M1;
   moe::Gmm1Params g1{w.xq, w.sx, a->w1, a->w1_scales, w.tiles, w.tile_count, w.max_tiles,
                      (int)h, (int)inter, fmt, w.tt, w.aq, w.sa, a->h1, packed, act, wfp4};
+  if (w.fold) {   // the shared expert's chunks run in the same launch
+    g1.tile_count = w.all_count;
+    g1.max_tiles = w.max_tiles + w.sh_max_tiles;
+    g1.shared.group = (int)ne; g1.shared.w = a->shared_w1; g1.shared.ws = a->shared_w1_scales;
+  }
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
   if (a->aq || a->sa) {
@@ -736,11 +777,17 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   moe::Gmm2Params g2{w.aq, w.sa, a->w2, a->w2_scales, w.tiles, w.tile_count, w.max_tiles,
                      (int)h, (int)aw, fmt, w.tt, o, packed, wfp4};
   g2.o16 = o ? nullptr : w.o16;
+  if (w.fold) {
+    g2.tile_count = w.all_count;
+    g2.max_tiles = g1.max_tiles;
+    g2.shared.group = (int)ne; g2.shared.w = a->shared_w2; g2.shared.ws = a->shared_w2_scales;
+  }
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");
-  // shared experts: the same FFN over all tokens in token order
-  for (int64_t s = 0; s < a->num_shared; ++s) {
+  // shared experts (when not folded into the launches above): the same FFN over all
+  // tokens in token order
+  for (int64_t s = 0; s < (w.fold ? 0 : a->num_shared); ++s) {
     // bytes of one shared expert's codes: halved for MXFP4 (two codes a byte)
     moe::Gmm1Params s1{w.xq_sh, w.sx_sh, a->shared_w1 + (s * 2 * inter * h >> swfp4),
                        a->shared_w1_scales + s * group_scale_bytes(2 * inter, h, a->weight_format), w.sh_tiles,

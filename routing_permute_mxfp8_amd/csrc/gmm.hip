@@ -493,6 +493,19 @@ __global__ void single_group_tiles_kernel(int rows, int tm, int4* __restrict__ t
   if (blockIdx.x == 0 && threadIdx.x == 0) *count = nt;
 }
 
+// One shared expert's chunks (token rows [0, rows), chunks of tm rows, group `group`,
+// padded rows prow0 + r, sorted rows srow0 + r) after the routed chunks (*count_in, at
+// most max_routed); *count_out = all chunks.
+__global__ void append_shared_tiles_kernel(const int* __restrict__ count_in, int max_routed, int rows, int tm,
+                                           int group, int prow0, int srow0, int4* __restrict__ tiles,
+                                           int* __restrict__ count_out) {
+  const int nt = (rows + tm - 1) / tm;
+  const int base = min(*count_in, max_routed);
+  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < nt; c += gridDim.x * blockDim.x)
+    tiles[base + c] = make_int4(group, prow0 + c * tm, min(tm, rows - c * tm), srow0 + c * tm);
+  if (blockIdx.x == 0 && threadIdx.x == 0) *count_out = base + nt;
+}
+
 template <int FMT, int NT, bool PACKED, int EPI, int WF>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI, WF>;
@@ -612,6 +625,13 @@ hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, 
   pack_codes_fp4_kernel<<<(unsigned)b1, 256, 0, st>>>(codes, packed, pieces, (int)k);
   pack_scales_kernel<<<(unsigned)b2, 256, 0, st>>>(scales, reinterpret_cast<uint32_t*>(packed_scales), words, (int)n,
                                                    (int)k);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_shared_tiles(const int* count_in, int max_routed, int rows, int tm, int group, int prow0,
+                                      int srow0, int4* tiles, int* count_out, hipStream_t st) {
+  append_shared_tiles_kernel<<<4, 256, 0, st>>>(count_in, max_routed, rows, tm, group, prow0, srow0, tiles,
+                                                 count_out);
   return hipGetLastError();
 }
 

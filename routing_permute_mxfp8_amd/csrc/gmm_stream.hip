@@ -41,6 +41,7 @@
 // draining the pipeline each step.
 
 #include <algorithm>
+#include <climits>
 
 #include "device_common.h"
 #include "gmm_device.h"
@@ -104,7 +105,15 @@ struct StreamArgs {
   ActParams act;
   float* o;                     // GMM2: fp32 O rows [rows, N] (sorted rows), or
   uint16_t* o16;                // GMM2: bf16 O rows
+  // A shared expert folded into the launch: group sh_first (INT_MAX: none) takes its
+  // weights from w + sh_first N K + sh_wdelta (codes) and the matching scales address +
+  // sh_sdelta, i.e. from the shared expert's own weights; its rows live in the same token,
+  // A^ and O buffers as the routed experts' (after theirs).
+  int sh_first;
+  int64_t sh_wdelta, sh_sdelta;
 };
+
+
 
 // The item's weight tile q (0..kCB-1) of channel block cb, clamped into the expert (the
 // tiles of a partial last block repeat the last one; their results are not stored).
@@ -210,7 +219,11 @@ __device__ __forceinline__ WeightStep weight_step(const StreamArgs& p, const Ite
   const int K = p.K, kq = ((K >> 7) + 3) >> 2;
   const int64_t cbytes = (int64_t)p.N * (SW::kFp4 ? K >> 1 : K);
   const int64_t sbytes = PACKED ? (int64_t)n16 * kq * kTileScaleBytes : (int64_t)p.N * (K >> 5);
-  return WeightStep{rsrc(p.w + c.e * cbytes, cbytes), rsrc(p.ws + c.e * sbytes, sbytes), c.cb, k};
+  // the shared expert's weights by an added offset, not a select of two pointers (the
+  // compiler turns that into a branch, which cuts the K loop into blocks)
+  const int64_t m = -(int64_t)(c.e == p.sh_first);
+  return WeightStep{rsrc(p.w + c.e * cbytes + (p.sh_wdelta & m), cbytes),
+                    rsrc(p.ws + c.e * sbytes + (p.sh_sdelta & m), sbytes), c.cb, k};
 }
 
 // This wave's i-th weight tile of a step (tile wave + 4 i of the channel block): its code
@@ -392,6 +405,8 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
   const int i16 = p.inter >> 4;
   const int aw = EPI == kActGelu ? 2 * p.inter : p.inter;
   const int ks2 = aw >> 7;
+  uint8_t* const aq = p.aq;
+  uint8_t* const sa = p.sa;
 #pragma unroll
   for (int j = 0; j < kRT; ++j) {
     if (j >= nw) break;                        // uniform per wave
@@ -412,8 +427,8 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
             ag[jj][i] = gelu_act(acc[2 * pg + jj][j][i]);
             au[jj][i] = gelu_act(acc[kCB / 2 + 2 * pg + jj][j][i]);
           }
-        store_a_group<FMT>(ag, p.aq, p.sa, tl, ks2, ch, g, r);
-        store_a_group<FMT>(au, p.aq, p.sa, tl, ks2, p.inter + ch, g, r);
+        store_a_group<FMT>(ag, aq, sa, tl, ks2, ch, g, r);
+        store_a_group<FMT>(au, aq, sa, tl, ks2, p.inter + ch, g, r);
       } else {
         float a2[2][4];
 #pragma unroll
@@ -421,10 +436,10 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
 #pragma unroll
           for (int i = 0; i < 4; ++i)
             a2[jj][i] = gated_act<EPI>(acc[2 * pg + jj][j][i], acc[kCB / 2 + 2 * pg + jj][j][i], p.act);
-        store_a_group<FMT>(a2, p.aq, p.sa, tl, ks2, ch, g, r);
+        store_a_group<FMT>(a2, aq, sa, tl, ks2, ch, g, r);
       }
       const int rr = 16 * t + r;
-      if (H1 && rr < c.nrows) {
+      if (H1 && c.e != p.sh_first && rr < c.nrows) {   // h1: the routed experts' rows only
         float* row = p.h1 + (int64_t)(c.srow0 + rr) * 2 * p.inter;
 #pragma unroll
         for (int jj = 0; jj < 2; ++jj) {
@@ -446,6 +461,8 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
   const int lane = epilogue_lane();
   const int g = lane >> 4, r = lane & 15;
   const int n16 = p.N >> 4;
+  float* const o = p.o;
+  uint16_t* const o16 = p.o16;
 #pragma unroll
   for (int j = 0; j < kRT; ++j) {
     if (j >= nw) break;
@@ -463,11 +480,11 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
         uint2 u;
         u.x = (uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16);
         u.y = (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16);
-        *reinterpret_cast<uint2*>(p.o16 + at) = u;
+        *reinterpret_cast<uint2*>(o16 + at) = u;
       } else {
         v4f x = v;
         asm volatile("" : "+v"(x));   // through vector registers, as the bf16 path
-        *reinterpret_cast<float4*>(p.o + at) = make_float4(x[0], x[1], x[2], x[3]);
+        *reinterpret_cast<float4*>(o + at) = make_float4(x[0], x[1], x[2], x[3]);
       }
     }
   }
@@ -638,12 +655,35 @@ hipError_t stream_gmm2(const StreamArgs& a, hipStream_t st) {
                : stream_go<FMT, PACKED, WF, 2, 0, false, false>(a, st);
 }
 
+// The folded shared expert's weights as offsets from where group sh.group's weights
+// would sit in the routed experts' arrays.
+template <bool PACKED>
+void set_shared_t(StreamArgs& a, const SharedGroups& sh, bool fp4) {
+  a.sh_first = INT_MAX;
+  a.sh_wdelta = a.sh_sdelta = 0;
+  if (!sh.w) return;
+  const int64_t K = a.K, kq = ((K >> 7) + 3) >> 2;
+  const int64_t cbytes = (int64_t)a.N * (fp4 ? K >> 1 : K);
+  const int64_t sbytes = PACKED ? (int64_t)(a.N >> 4) * kq * kTileScaleBytes : (int64_t)a.N * (K >> 5);
+  a.sh_first = sh.group;
+  a.sh_wdelta = (int64_t)((uintptr_t)sh.w - (uintptr_t)(a.w + sh.group * cbytes));
+  a.sh_sdelta = (int64_t)((uintptr_t)sh.ws - (uintptr_t)(a.ws + sh.group * sbytes));
+}
+
+void set_shared(StreamArgs& a, const SharedGroups& sh, int wfp4, int packed) {
+  if (packed)
+    set_shared_t<true>(a, sh, wfp4 != 0);
+  else
+    set_shared_t<false>(a, sh, wfp4 != 0);
+}
+
 }  // namespace
 
 hipError_t launch_gmm1_stream(const Gmm1Params& p, hipStream_t st) {
   StreamArgs a{};
   a.tok = p.xq; a.toks = p.sx; a.w = p.w; a.ws = p.ws; a.tiles = p.tiles; a.tile_count = p.tile_count;
   a.K = p.hidden; a.N = 2 * p.inter; a.inter = p.inter; a.aq = p.aq; a.sa = p.sa; a.h1 = p.h1; a.act = p.act;
+  set_shared(a, p.shared, p.wfp4, p.packed);
   if (p.wfp4) {
     if (p.fmt != 0) return hipErrorInvalidValue;
     return p.packed ? stream_gmm1<0, true, kFmtFp4>(a, p.act.kind, st) : stream_gmm1<0, false, kFmtFp4>(a, p.act.kind, st);
@@ -656,6 +696,7 @@ hipError_t launch_gmm2_stream(const Gmm2Params& p, hipStream_t st) {
   StreamArgs a{};
   a.tok = p.aq; a.toks = p.sa; a.w = p.w; a.ws = p.ws; a.tiles = p.tiles; a.tile_count = p.tile_count;
   a.K = p.inter; a.N = p.hidden; a.inter = p.inter; a.o = p.o; a.o16 = p.o16;
+  set_shared(a, p.shared, p.wfp4, p.packed);
   if (p.wfp4) {
     if (p.fmt != 0) return hipErrorInvalidValue;
     return p.packed ? stream_gmm2<0, true, kFmtFp4>(a, st) : stream_gmm2<0, false, kFmtFp4>(a, st);

@@ -115,6 +115,16 @@ constexpr int kActGelu = 4;
 
 // Token operands and GMM1's requantized output are in the tiled layout, indexed by the
 // chunks' padded rows; h1, o, row_token and row_weight are indexed by sorted rows.
+// A shared expert folded into the routed experts' launch of an LDS-streaming GEMM: the
+// chunks of group `group` take their weights from w / ws (one expert, the routed
+// experts' format); their rows are in the launch's token and output buffers like the
+// routed ones. w = nullptr: none.
+struct SharedGroups {
+  int group = 0;
+  const uint8_t* w = nullptr;
+  const uint8_t* ws = nullptr;
+};
+
 struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
@@ -125,6 +135,7 @@ struct Gmm1Params {
   int packed;                                  // weights in the MFMA-native packed layout
   ActParams act;                               // A = act(G, U) [rows, I], or gelu(Z) [rows, 2I]
   int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, 2I, H/2]; fmt must be E4M3)
+  SharedGroups shared;                         // LDS-streaming kernels only
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 
@@ -137,6 +148,7 @@ struct Gmm2Params {
   int packed;
   int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, H, I/2]; fmt must be E4M3)
   uint16_t* o16 = nullptr;                     // if set, O rows go here as bf16 (RNE) instead of o
+  SharedGroups shared;                         // LDS-streaming kernels only
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 
@@ -162,6 +174,11 @@ hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, 
 
 // Chunks of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), i*tm}.
 hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);
+// After *count_in routed chunks (at most max_routed): the chunks of one shared expert
+// (group `group`) over `rows` token rows in chunks of tm rows, at padded rows prow0 + r
+// and sorted rows srow0 + r; *count_out = all chunks.
+hipError_t launch_append_shared_tiles(const int* count_in, int max_routed, int rows, int tm, int group, int prow0,
+                                      int srow0, int4* tiles, int* count_out, hipStream_t stream);
 
 // ---- weighted combine (combine.hip) -------------------------------------------------
 // Y[t] = bf16(sum_k w[t, k] * O[pos[t*K + k]] + sum_s O_shared[s][t]) for every token t:

@@ -144,6 +144,9 @@ struct MegaWs {
   bool fold;
   int* all_count;
   int64_t routed_padded;
+  // LDS-streaming GEMMs: the chunk list split by chunk size (one launch per class)
+  int4* cls_tiles;
+  int* cls_count;
   // x quantized once in token order (row-major codes [tokens, hidden] and scales
   // [tokens, hidden/32]) when the gather re-reads many x rows; else null
   uint8_t* xrow;
@@ -199,9 +202,14 @@ MegaWs carve_mega(Carver& cv, const moe_mega_args* a) {
     w.fold = S == 1 && !a->o && w.tt == moe::kStreamTiles && w.sh_tt == moe::kStreamTiles &&
              (sw == MOE_FP4_E2M1) == (a->weight_dtype == MOE_FP4_E2M1);
   }
-  w.tiles = cv.take<int4>(w.max_tiles + (w.fold ? w.sh_max_tiles : 0));
+  const int all_max = w.max_tiles + (w.fold ? w.sh_max_tiles : 0);
+  w.tiles = cv.take<int4>(all_max);
   w.tile_count = cv.take<int>(1);
   w.all_count = w.fold ? cv.take<int>(1) : nullptr;
+  if (w.tt == moe::kStreamTiles) {
+    w.cls_tiles = cv.take<int4>((size_t)moe::kStreamClasses * all_max);
+    w.cls_count = cv.take<int>(moe::kStreamClasses);
+  }
   if (quantize_first(a)) {
     w.xrow = cv.take<uint8_t>((size_t)(n * h));
     w.xrow_s = cv.take<uint8_t>((size_t)(n * (h / 32)));
@@ -706,6 +714,14 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
                                         (int)w.routed_padded, (int)flat, w.tiles, w.all_count, st);
     if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile list launch");
   }
+  moe::StreamClasses classes;
+  if (w.cls_tiles) {
+    const int all_max = w.max_tiles + (w.fold ? w.sh_max_tiles : 0);
+    e = moe::launch_split_stream_chunks(w.tiles, w.fold ? w.all_count : w.tile_count, all_max, w.cls_tiles,
+                                        w.cls_count, st);
+    if (e != hipSuccess) return hip_fail(e, "mega_moe chunk split launch");
+    classes.tiles = w.cls_tiles; classes.count = w.cls_count; classes.stride = all_max;
+  }
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
   // of the shared experts)
@@ -765,6 +781,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     g1.max_tiles = w.max_tiles + w.sh_max_tiles;
     g1.shared.group = (int)ne; g1.shared.w = a->shared_w1; g1.shared.ws = a->shared_w1_scales;
   }
+  g1.classes = classes;
   e = moe::launch_gmm1(g1, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm1 launch");
   if (a->aq || a->sa) {
@@ -782,6 +799,7 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
     g2.max_tiles = g1.max_tiles;
     g2.shared.group = (int)ne; g2.shared.w = a->shared_w2; g2.shared.ws = a->shared_w2_scales;
   }
+  g2.classes = classes;
   e = moe::launch_gmm2(g2, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe gmm2 launch");
   if ((e = mark(4)) != hipSuccess) return hip_fail(e, "mega_moe event record");

@@ -506,6 +506,34 @@ __global__ void append_shared_tiles_kernel(const int* __restrict__ count_in, int
   if (blockIdx.x == 0 && threadIdx.x == 0) *count_out = base + nt;
 }
 
+// One wave: a stable split of the chunk list by the token tiles a wave needs,
+// ceil(tiles / 4), into the classes of kStreamClassRT.
+__global__ __launch_bounds__(64) void split_stream_chunks_kernel(const int4* __restrict__ chunks,
+                                                                  const int* __restrict__ count, int max_tiles,
+                                                                  int4* __restrict__ out, int* __restrict__ out_count) {
+  const int lane = threadIdx.x;
+  const int n = min(*count, max_tiles);
+  int base[kStreamClasses] = {};
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const bool valid = i < n;
+    const int4 c = valid ? chunks[i] : make_int4(0, 0, 0, 0);
+    const int rt = (((c.z + 15) >> 4) + 3) >> 2;
+    int cls = kStreamClasses - 1;
+#pragma unroll
+    for (int k = kStreamClasses - 2; k >= 0; --k)
+      if (rt <= kStreamClassRT[k]) cls = k;
+#pragma unroll
+    for (int k = 0; k < kStreamClasses; ++k) {
+      const uint64_t m = __ballot(valid && cls == k);
+      if (valid && cls == k) out[k * max_tiles + base[k] + __popcll(m & ((1ull << lane) - 1))] = c;
+      base[k] += __popcll(m);
+    }
+  }
+  if (lane == 0)
+    for (int k = 0; k < kStreamClasses; ++k) out_count[k] = base[k];
+}
+
 template <int FMT, int NT, bool PACKED, int EPI, int WF>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI, WF>;
@@ -632,6 +660,12 @@ hipError_t launch_append_shared_tiles(const int* count_in, int max_routed, int r
                                       int srow0, int4* tiles, int* count_out, hipStream_t st) {
   append_shared_tiles_kernel<<<4, 256, 0, st>>>(count_in, max_routed, rows, tm, group, prow0, srow0, tiles,
                                                  count_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_split_stream_chunks(const int4* chunks, const int* count, int max_tiles, int4* out, int* out_count,
+                                      hipStream_t st) {
+  split_stream_chunks_kernel<<<1, 64, 0, st>>>(chunks, count, max_tiles, out, out_count);
   return hipGetLastError();
 }
 

@@ -51,11 +51,10 @@ namespace moe {
 namespace {
 
 constexpr int kCB = 12;         // 16-channel weight tiles per channel block (192 channels)
-constexpr int kRT = 5;          // token tiles per wave: a chunk holds up to 20 tiles (320 rows)
+constexpr int kRT = 5;          // most token tiles per wave: a chunk holds up to 20 tiles (320 rows)
 constexpr int kSlots = 5;       // LDS weight slots
 constexpr int kLead = 4;        // weight loads run kLead steps ahead (kSlots - 1)
 constexpr int kTokLead = 3;     // token loads run three steps ahead (four register sets)
-constexpr int kTokLoads = 2 * kRT;   // per wave and step: lo and hi half of each token tile
 
 // LDS: kSlots weight code slots (one K step of the channel block each), then two scale
 // groups (the E8M0 scales of four K steps: the block's weight tiles, then the chunk's
@@ -75,8 +74,7 @@ struct StreamW {
   static constexpr int kGroups = kSlots * kSlotBytes;   // offset of the two scale groups
   static constexpr int kLds = kGroups + 2 * kGroupBytes;
   static constexpr int kDma = (kCB / 4) * kHalves;   // weight code loads per wave and step
-  static constexpr int kScaleDma = kCB / 4 + kRT;    // scale loads per wave, every fourth step
-  // Step h issues T(h + 3) (kTokLoads ops) before its MFMAs, W(h + 4) (kDma ops) between
+  // Step h issues T(h + 3) (2 RT ops) before its MFMAs, W(h + 4) (kDma ops) between
   // two of its MFMA groups, and, when h = 0 mod 4, the scale group S of steps h + 4 ..
   // h + 7 after a later group. The prologue is steps -4..-1 of the same pattern (S0, W0,
   // T0 W1, T1 W2, T2 W3). At the top of step g the weight codes W(g) and the scales of
@@ -84,8 +82,10 @@ struct StreamW {
   // them are at least three whole steps' worth without scale loads, so vmcnt(kWait)
   // covers both from step 0 on (vector memory loads complete in order). The compiler's
   // own wait for the token registers of step g comes after that.
-  static constexpr int kWait = 3 * (kDma + kTokLoads);
-  static_assert(kWait <= 63, "vmcnt holds at most 63");
+  // (kTokLoads = 2 RT per wave and step: lo and hi half of each of its RT token tiles)
+  template <int RT>
+  static constexpr int kWait = 3 * (kDma + 2 * RT);
+  static_assert(kWait<kRT> <= 63, "vmcnt holds at most 63");
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
 
@@ -286,16 +286,17 @@ __device__ __forceinline__ void issue_token_tile(const TokenStep& L, int j, int 
 }
 
 // All of this wave's token tiles of step k of item c.
+template <int RT>
 __device__ __forceinline__ void issue_tokens(const StreamArgs& p, const Item& c, int k, int ks, int kq, int wave,
-                                             const LaneOffsets& lo, v8i (&t)[kRT]) {
+                                             const LaneOffsets& lo, v8i (&t)[RT]) {
   const TokenStep L = token_step(p, c, k, ks, kq);
 #pragma unroll
-  for (int j = 0; j < kRT; ++j) issue_token_tile(L, j, ks, wave, lo, t[j]);
+  for (int j = 0; j < RT; ++j) issue_token_tile(L, j, ks, wave, lo, t[j]);
 }
 
 // This wave's share of the scale group of steps k .. k + 3 of item c (k = 0 mod 4) into
 // `group`: the scales of its weight tiles wave + 4 i and of its token tiles 4 j + wave.
-template <int GMM, bool PACKED, int WF>
+template <int GMM, bool PACKED, int WF, int RT>
 __device__ __forceinline__ void issue_scales(const StreamArgs& p, const Item& c, int k, uint8_t* group, int ks, int kq,
                                              int n16, int i16, const LaneOffsets& lo, int wave) {
   using SW = StreamW<WF, PACKED>;
@@ -313,7 +314,7 @@ __device__ __forceinline__ void issue_scales(const StreamArgs& p, const Item& c,
       __builtin_amdgcn_raw_ptr_buffer_load_lds(W.sr, (lds_void_ptr)(group + q * SW::kWsTile), 16, lo.wscale, so, 0, 0);
   }
 #pragma unroll
-  for (int j = 0; j < kRT; ++j)
+  for (int j = 0; j < RT; ++j)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(T.sr, (lds_void_ptr)(group + SW::kTsOff + (4 * j + wave) * kTileScaleBytes),
                                              4, lo.scale, (wave_tile(T, j, wave) * kq + g4) * kTileScaleBytes, 0, 0);
 }
@@ -325,11 +326,11 @@ __device__ __forceinline__ void issue_scales(const StreamArgs& p, const Item& c,
 // core busy. The E8M0 scales come from the step's scale group (byte k % 4 of a packed or
 // token dword; byte lane / 16 of the ND dword of step k % 4).
 template <int FMT, bool PACKED, int WF, int NW, class Between>
-__device__ __forceinline__ void step_mfma(v4f (&acc)[kCB][kRT], const uint8_t* slot, const uint8_t* group, int k,
-                                          int lane, int wave, const v8i (&t)[kRT], Between&& between) {
+__device__ __forceinline__ void step_mfma(v4f (&acc)[kCB][NW], const uint8_t* slot, const uint8_t* group, int k,
+                                          int lane, int wave, const v8i (&t)[NW], Between&& between) {
   using SW = StreamW<WF, PACKED>;
   const int sh = 8 * (k & 3);
-  int tsc[kRT];
+  int tsc[NW];
 #pragma unroll
   for (int j = 0; j < NW; ++j)
     tsc[j] = (int)((uint32_t)reinterpret_cast<const int*>(group + SW::kTsOff + (4 * j + wave) * kTileScaleBytes)[lane] >>
@@ -397,8 +398,8 @@ __device__ __forceinline__ int epilogue_lane() {
   return l;
 }
 
-template <int FMT, int EPI, bool H1>
-__device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4f (&acc)[kCB][kRT], int nw,
+template <int FMT, int EPI, bool H1, int RT>
+__device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4f (&acc)[kCB][RT], int nw,
                                           int wave) {
   const int lane = epilogue_lane();
   const int g = lane >> 4, r = lane & 15;
@@ -408,7 +409,7 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
   uint8_t* const aq = p.aq;
   uint8_t* const sa = p.sa;
 #pragma unroll
-  for (int j = 0; j < kRT; ++j) {
+  for (int j = 0; j < RT; ++j) {
     if (j >= nw) break;                        // uniform per wave
     const int t = 4 * j + wave;
     const int64_t tl = (int64_t)(c.row0 >> 4) + t;
@@ -455,8 +456,8 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
 }
 
 // GMM2 epilogue: acc[q][j][i] = O[row 16 t + r][channel 16 (12 cb + q) + 4 g + i].
-template <bool OBF16>
-__device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4f (&acc)[kCB][kRT], int nw,
+template <bool OBF16, int RT>
+__device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4f (&acc)[kCB][RT], int nw,
                                           int wave) {
   const int lane = epilogue_lane();
   const int g = lane >> 4, r = lane & 15;
@@ -464,7 +465,7 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
   float* const o = p.o;
   uint16_t* const o16 = p.o16;
 #pragma unroll
-  for (int j = 0; j < kRT; ++j) {
+  for (int j = 0; j < RT; ++j) {
     if (j >= nw) break;
     const int rr = 16 * (4 * j + wave) + r;
     if (rr >= c.nrows) continue;               // per lane; no cross-lane work below
@@ -490,11 +491,12 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
   }
 }
 
-__device__ __forceinline__ void zero_acc(v4f (&acc)[kCB][kRT]) {
+template <int RT>
+__device__ __forceinline__ void zero_acc(v4f (&acc)[kCB][RT]) {
 #pragma unroll
   for (int q = 0; q < kCB; ++q)
 #pragma unroll
-    for (int j = 0; j < kRT; ++j) acc[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < RT; ++j) acc[q][j] = v4f{0.f, 0.f, 0.f, 0.f};
 }
 
 // The kernel body gets the LDS area twice, as two restrict pointers: one that the
@@ -503,18 +505,18 @@ __device__ __forceinline__ void zero_acc(v4f (&acc)[kCB][kRT]) {
 // such a load writes); the reads of a weight slot are ordered after its loads by the
 // explicit wait and barrier at the top of each K step, with a compiler-level memory fence
 // after the barrier.
-template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1>
+template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
 __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __restrict__ lds,
                                             const uint8_t* __restrict__ ldsr);
 
-template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1>
+template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void gmm_stream_kernel(StreamArgs p) {
   extern __shared__ __align__(16) uint8_t lds_area[];
-  stream_body<FMT, PACKED, WF, GMM, EPI, OBF16, H1>(p, lds_area, lds_area);
+  stream_body<FMT, PACKED, WF, GMM, EPI, OBF16, H1, RT>(p, lds_area, lds_area);
 }
 
-template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1>
+template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
 __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __restrict__ lds,
                                             const uint8_t* __restrict__ ldsr) {
   using SW = StreamW<WF, PACKED>;
@@ -528,9 +530,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
   const int count = first < last ? (last - first + stride - 1) / stride : 0;
   if (count == 0) return;
 
-  v4f acc[kCB][kRT];
+  v4f acc[kCB][RT];
   zero_acc(acc);
-  v8i t0[kRT], t1[kRT], t2[kRT], t3[kRT];
+  v8i t0[RT], t1[RT], t2[RT], t3[RT];
 
   // items n (cur), n + 1 (nxt) and n + 2 (nn, read an item early so that its scalar loads
   // have landed when it becomes nxt); past the last item each repeats the last one
@@ -542,13 +544,13 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
   // of steps 0..3), W0, T0 W1, T1 W2, T2 W3 (all in item 0: ks >= 4)
   uint8_t* const groups = lds + SW::kGroups;
   const uint8_t* const groups_r = ldsr + SW::kGroups;
-  issue_scales<GMM, PACKED, WF>(p, cur, 0, groups, ks, kq, n16, i16, lofs, wave);
+  issue_scales<GMM, PACKED, WF, RT>(p, cur, 0, groups, ks, kq, n16, i16, lofs, wave);
   issue_weights<GMM, PACKED, WF>(p, cur, 0, lds, n16, i16, lofs, wave);
-  issue_tokens(p, cur, 0, ks, kq, wave, lofs, t0);
+  issue_tokens<RT>(p, cur, 0, ks, kq, wave, lofs, t0);
   issue_weights<GMM, PACKED, WF>(p, cur, 1, lds + SW::kSlotBytes, n16, i16, lofs, wave);
-  issue_tokens(p, cur, 1, ks, kq, wave, lofs, t1);
+  issue_tokens<RT>(p, cur, 1, ks, kq, wave, lofs, t1);
   issue_weights<GMM, PACKED, WF>(p, cur, 2, lds + 2 * SW::kSlotBytes, n16, i16, lofs, wave);
-  issue_tokens(p, cur, 2, ks, kq, wave, lofs, t2);
+  issue_tokens<RT>(p, cur, 2, ks, kq, wave, lofs, t2);
   issue_weights<GMM, PACKED, WF>(p, cur, 3, lds + 3 * SW::kSlotBytes, n16, i16, lofs, wave);
   int wslot = 4;   // slot of the next weight loads
   int cslot = 0;   // slot of the next compute step
@@ -562,8 +564,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
     // K step kc of item n with the token registers of set (tc); the token loads of
     // kc + kTokLead go into set (tn), the set the previous step used; a step kc = 0 mod 4
     // also loads the scale group of steps kc + 4 .. kc + 7 into the other group.
-    auto step = [&](int kc, bool group_start, v8i(&tc)[kRT], v8i(&tn)[kRT]) {
-      wait_vmcnt<SW::kWait>();
+    auto step = [&](int kc, bool group_start, v8i(&tc)[RT], v8i(&tn)[RT]) {
+      wait_vmcnt<SW::template kWait<RT>>();
       __builtin_amdgcn_sched_barrier(0);
       __builtin_amdgcn_s_barrier();
       asm volatile("" ::: "memory");
@@ -579,7 +581,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
       // the scale group after the next one (placements measured best: the loads of a
       // step spread over it, and a clean register allocation of the K loop)
 #pragma unroll
-      for (int j = 0; j < kRT; ++j) issue_token_tile(tl, j, ks, wave, lofs, tn[j]);
+      for (int j = 0; j < RT; ++j) issue_token_tile(tl, j, ks, wave, lofs, tn[j]);
       __builtin_amdgcn_sched_barrier(0);
       auto between = [&](int q) {
         if (q == kWeightsAfter) {
@@ -587,11 +589,11 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
           for (int i = 0; i < kCB / 4; ++i)
             issue_weight_tile<GMM, PACKED, WF>(wl, i, wdst, p.K, n16, i16, lofs, wave);
         } else if (q == kWeightsAfter + 1 && group_start) {
-          issue_scales<GMM, PACKED, WF>(p, aw.d, aw.k, groups + (grp ^ 1) * SW::kGroupBytes, ks, kq, n16, i16, lofs,
+          issue_scales<GMM, PACKED, WF, RT>(p, aw.d, aw.k, groups + (grp ^ 1) * SW::kGroupBytes, ks, kq, n16, i16, lofs,
                                         wave);
         }
       };
-      step_mfma<FMT, PACKED, WF, kRT>(acc, ldsr + cslot * SW::kSlotBytes, groups_r + grp * SW::kGroupBytes, kc, lane,
+      step_mfma<FMT, PACKED, WF, RT>(acc, ldsr + cslot * SW::kSlotBytes, groups_r + grp * SW::kGroupBytes, kc, lane,
                                       wave, tc, between);
       cslot = cslot == kSlots - 1 ? 0 : cslot + 1;
     };
@@ -605,9 +607,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
     }
     const int nw = wave_tiles(cur.nrows, wave);
     if constexpr (GMM == 1)
-      epilogue1<FMT, EPI, H1>(p, cur, acc, nw, wave);
+      epilogue1<FMT, EPI, H1, RT>(p, cur, acc, nw, wave);
     else
-      epilogue2<OBF16>(p, cur, acc, nw, wave);
+      epilogue2<OBF16, RT>(p, cur, acc, nw, wave);
     zero_acc(acc);
     cur = nxt;
     nxt = nn;
@@ -621,9 +623,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
 #ifndef MOE_STREAM_KERNEL_ONLY   // (defined by single-instance builds that inspect the kernel's code)
 namespace {
 
-template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1>
+template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT = kRT>
 hipError_t stream_go(const StreamArgs& a, hipStream_t st) {
-  auto kern = gmm_stream_kernel<FMT, PACKED, WF, GMM, EPI, OBF16, H1>;
+  auto kern = gmm_stream_kernel<FMT, PACKED, WF, GMM, EPI, OBF16, H1, RT>;
   LaunchShape ls;
   hipError_t e = persistent_shape(kern, StreamW<WF, PACKED>::kLds, &ls);
   if (e != hipSuccess) return e;
@@ -677,6 +679,19 @@ void set_shared(StreamArgs& a, const SharedGroups& sh, int wfp4, int packed) {
     set_shared_t<false>(a, sh, wfp4 != 0);
 }
 
+// One launch per chunk class, each with the instance of that class's token tiles a wave.
+template <int FMT, int WF, int GMM, int EPI, bool OBF16>
+hipError_t stream_classes(StreamArgs a, const StreamClasses& cl, hipStream_t st) {
+  static_assert(kStreamClasses == 3 && kStreamClassRT[2] == kRT, "classes of 2, 4 and 5 token tiles a wave");
+  hipError_t e;
+  a.tiles = cl.tiles; a.tile_count = cl.count;
+  if ((e = stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[0]>(a, st)) != hipSuccess) return e;
+  a.tiles = cl.tiles + cl.stride; a.tile_count = cl.count + 1;
+  if ((e = stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[1]>(a, st)) != hipSuccess) return e;
+  a.tiles = cl.tiles + 2 * cl.stride; a.tile_count = cl.count + 2;
+  return stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[2]>(a, st);
+}
+
 }  // namespace
 
 hipError_t launch_gmm1_stream(const Gmm1Params& p, hipStream_t st) {
@@ -684,6 +699,10 @@ hipError_t launch_gmm1_stream(const Gmm1Params& p, hipStream_t st) {
   a.tok = p.xq; a.toks = p.sx; a.w = p.w; a.ws = p.ws; a.tiles = p.tiles; a.tile_count = p.tile_count;
   a.K = p.hidden; a.N = 2 * p.inter; a.inter = p.inter; a.aq = p.aq; a.sa = p.sa; a.h1 = p.h1; a.act = p.act;
   set_shared(a, p.shared, p.wfp4, p.packed);
+  // chunk classes: the packed FP8 SwiGLU instance without the h1 output
+  if (p.classes.tiles && p.packed && !p.wfp4 && !p.h1 && p.act.kind == 0)
+    return p.fmt == 0 ? stream_classes<0, 0, 1, 0, false>(a, p.classes, st)
+                      : stream_classes<1, 1, 1, 0, false>(a, p.classes, st);
   if (p.wfp4) {
     if (p.fmt != 0) return hipErrorInvalidValue;
     return p.packed ? stream_gmm1<0, true, kFmtFp4>(a, p.act.kind, st) : stream_gmm1<0, false, kFmtFp4>(a, p.act.kind, st);
@@ -697,6 +716,10 @@ hipError_t launch_gmm2_stream(const Gmm2Params& p, hipStream_t st) {
   a.tok = p.aq; a.toks = p.sa; a.w = p.w; a.ws = p.ws; a.tiles = p.tiles; a.tile_count = p.tile_count;
   a.K = p.inter; a.N = p.hidden; a.inter = p.inter; a.o = p.o; a.o16 = p.o16;
   set_shared(a, p.shared, p.wfp4, p.packed);
+  // chunk classes: the packed FP8 instance with bf16 O rows
+  if (p.classes.tiles && p.packed && !p.wfp4 && p.o16)
+    return p.fmt == 0 ? stream_classes<0, 0, 2, 0, true>(a, p.classes, st)
+                      : stream_classes<1, 1, 2, 0, true>(a, p.classes, st);
   if (p.wfp4) {
     if (p.fmt != 0) return hipErrorInvalidValue;
     return p.packed ? stream_gmm2<0, true, kFmtFp4>(a, st) : stream_gmm2<0, false, kFmtFp4>(a, st);

@@ -125,6 +125,23 @@ struct SharedGroups {
   const uint8_t* ws = nullptr;
 };
 
+// The chunk list of an LDS-streaming GEMM split by chunk size: class c (list tiles +
+// c stride, count[c]) holds the chunks of more than 4 kStreamClassRT[c - 1] and at most
+// 4 kStreamClassRT[c] token tiles, run by the instance with kStreamClassRT[c] token tiles
+// a wave (no MFMAs for tiles past the chunk's end). tiles = nullptr: one list, one
+// launch.
+constexpr int kStreamClasses = 3;
+constexpr int kStreamClassRT[kStreamClasses] = {2, 4, 5};
+struct StreamClasses {
+  const int4* tiles = nullptr;
+  const int* count = nullptr;
+  int stride = 0;
+};
+// Splits chunks[0, min(*count, max_tiles)) into the classes above (stable order):
+// out + c max_tiles, out_count[c].
+hipError_t launch_split_stream_chunks(const int4* chunks, const int* count, int max_tiles, int4* out, int* out_count,
+                                      hipStream_t stream);
+
 struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
   const uint8_t* w; const uint8_t* ws;         // [G, 2I, H], [G, 2I, H/32]
@@ -136,6 +153,7 @@ struct Gmm1Params {
   ActParams act;                               // A = act(G, U) [rows, I], or gelu(Z) [rows, 2I]
   int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, 2I, H/2]; fmt must be E4M3)
   SharedGroups shared;                         // LDS-streaming kernels only
+  StreamClasses classes;                       // LDS-streaming kernels only
 };
 hipError_t launch_gmm1(const Gmm1Params& p, hipStream_t stream);
 
@@ -149,6 +167,7 @@ struct Gmm2Params {
   int wfp4 = 0;                                // weights MXFP4 E2M1 (codes [G, H, I/2]; fmt must be E4M3)
   uint16_t* o16 = nullptr;                     // if set, O rows go here as bf16 (RNE) instead of o
   SharedGroups shared;                         // LDS-streaming kernels only
+  StreamClasses classes;                       // LDS-streaming kernels only
 };
 hipError_t launch_gmm2(const Gmm2Params& p, hipStream_t stream);
 

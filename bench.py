@@ -81,14 +81,26 @@ def layer_work(cfg, ids, fp4=False):
     gmm2_flops = 2.0 * f * i * h
     if cfg.shared:
         n = cfg.tokens
-        gmm1_bytes_s = cfg.shared * (2 * i * h * sc + n * h * sc + n * i * sc)
-        gmm2_bytes_s = cfg.shared * (h * i * sc + n * i * sc + n * h * 2)
-        shared = dict(bytes=gmm1_bytes_s + gmm2_bytes_s, flops=cfg.shared * 6.0 * n * h * i)
+        gmm1_bytes_s = cfg.shared * (2 * i * h * wsc + n * h * sc + n * i * sc)
+        gmm2_bytes_s = cfg.shared * (h * i * wsc + n * i * sc + n * h * 2)
+        shared1 = dict(bytes=gmm1_bytes_s, flops=cfg.shared * 4.0 * n * h * i)
+        shared2 = dict(bytes=gmm2_bytes_s, flops=cfg.shared * 2.0 * n * h * i)
     else:
-        shared = dict(bytes=0.0, flops=0.0)
+        shared1 = shared2 = dict(bytes=0.0, flops=0.0)
+    shared = dict(bytes=shared1["bytes"] + shared2["bytes"], flops=shared1["flops"] + shared2["flops"])
     return dict(touched=touched, gmm1=dict(bytes=gmm1_bytes, flops=gmm1_flops),
                 gmm2=dict(bytes=gmm2_bytes, flops=gmm2_flops), combine=dict(bytes=combine_bytes, flops=0.0),
-                shared=shared)
+                shared=shared, shared1=shared1, shared2=shared2)
+
+
+def shared_folded(cfg):
+    """Whether the library runs the shared expert inside the routed experts' GEMM launches:
+    one shared expert, and the LDS-streaming GEMMs for the routed experts (more than 128
+    rows an expert on average, K steps of both GEMMs a multiple of 4) and for the shared
+    expert (more than 128 tokens). The GMM stage times then include the shared expert."""
+    h, i = cfg.hidden, cfg.inter
+    steps4 = (h // 128) % 4 == 0 and (i // 128) % 4 == 0
+    return cfg.shared == 1 and steps4 and cfg.flat / cfg.experts > 128 and cfg.tokens > 128
 
 
 def kernel_source_hash():
@@ -319,8 +331,16 @@ def bench_mega(args, torch, rp, moe_inputs):
     stage_ms["routing_and_permute"] = between(0, 2)
     step_ms = [evs[k][0].elapsed_time(evs[k][6]) for k in range(args.steps)]
     work = layer_work(cfg, ids, fp4)
-    roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], work["gmm1"]),
-            "gmm2": roofline_entry("gmm2_kernel", stage_ms["gmm2"], work["gmm2"])}
+    folded = shared_folded(cfg)
+    w1, w2 = work["gmm1"], work["gmm2"]
+    if folded:   # the shared expert runs inside the GMM stages
+        w1 = dict(bytes=w1["bytes"] + work["shared1"]["bytes"], flops=w1["flops"] + work["shared1"]["flops"])
+        w2 = dict(bytes=w2["bytes"] + work["shared2"]["bytes"], flops=w2["flops"] + work["shared2"]["flops"])
+    roof = {"gmm1_swiglu_quant": roofline_entry("gmm1_swiglu_kernel", stage_ms["gmm1_swiglu_quant"], w1),
+            "gmm2": roofline_entry("gmm2_kernel", stage_ms["gmm2"], w2)}
+    if folded:
+        for r in roof.values():
+            r["includes_shared_expert"] = True
     dominant = max(roof, key=lambda k: stage_ms[k])
     roofline = dict(roof[dominant])
     roofline["traffic"] = measured_traffic(roofline["kernel"], cfg.name + ("-mxfp4" if fp4 else ""))

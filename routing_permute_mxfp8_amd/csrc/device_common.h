@@ -96,6 +96,14 @@ __device__ __forceinline__ int quad_max_bits(int v) {
 __device__ __forceinline__ float bf16_to_f(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 // float -> bf16 bits, round to nearest even (finite inputs).
+// Two floats to bf16, round to nearest even, as one gfx950 V_CVT_PK_BF16_F32 (a in the
+// low half); the same bits as f_to_bf16 for every finite value.
+__device__ __forceinline__ uint32_t bf16x2(float a, float b) {
+  typedef float f2_t __attribute__((ext_vector_type(2)));
+  typedef __bf16 bf2_t __attribute__((ext_vector_type(2)));
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f2_t{a, b}, bf2_t));
+}
+
 __device__ __forceinline__ uint16_t f_to_bf16(float f) {
   uint32_t u = __float_as_uint(f);
   u += 0x7fffu + ((u >> 16) & 1u);

@@ -134,22 +134,31 @@ __device__ __forceinline__ void block_barrier() {
 // ---- activations (MegaMoE README, "Activation function formulas") ------------------
 // sigma(z) = 1 / (1 + e^-z); SiLU(z) = z sigma(z); with the clamp c (+inf when none),
 // Gc = min(G, c), Uc = clip(U, -c, c).
-__device__ __forceinline__ float sigmoid(float z) { return 1.0f / (1.0f + expf(-z)); }
+//
+// e^x and 1/x by the hardware's V_EXP_F32 (2^(x log2 e)) and V_RCP_F32: a few ulp where
+// the library's expf and an IEEE division take ten or more instructions each. A is
+// requantized to FP8 right after (a step of 2^-4 of its group's scale), and its
+// products carry the GEMM's own error (up to 2^-12 of their magnitudes), so the
+// difference does not show. e^x overflows to +inf and underflows to 0 as expf does;
+// 1/inf = 0.
+__device__ __forceinline__ float exp_hw(float x) { return __builtin_amdgcn_exp2f(x * 1.4426950408889634f); }
+__device__ __forceinline__ float rcp_hw(float x) { return __builtin_amdgcn_rcpf(x); }
+__device__ __forceinline__ float sigmoid(float z) { return rcp_hw(1.0f + exp_hw(-z)); }
 
 // swiglu: SiLU(Gc) Uc.
 __device__ __forceinline__ float swiglu_act(float g, float u, float c) {
   const float gc = fminf(g, c), uc = fminf(fmaxf(u, -c), c);
-  return gc / (1.0f + expf(-gc)) * uc;
+  return gc * sigmoid(gc) * uc;
 }
 
 // tanh without branches: 1 - 2 / (e^(2|x|) + 1) with the sign of x (e^(2|x|) = inf gives
-// 1 exactly), and for |x| < 0.05, where that difference cancels, the series
+// 1 exactly; e^x and 1/x as above), and for |x| < 0.05, where that difference cancels, the series
 // x (1 - x^2/3 + 2 x^4/15) (next term below 1e-10 relative there). The library tanhf
 // branches, and a branch in the epilogue of the 240-accumulator GEMM costs it its
 // register allocation.
 __device__ __forceinline__ float tanh_nb(float x) {
   const float a = fabsf(x);
-  const float big = 1.0f - 2.0f / (expf(2.0f * a) + 1.0f);
+  const float big = 1.0f - 2.0f * rcp_hw(exp_hw(2.0f * a) + 1.0f);
   const float x2 = x * x;
   const float small = a * (1.0f - x2 * (1.0f / 3.0f) + x2 * x2 * (2.0f / 15.0f));
   return copysignf(a < 0.05f ? small : big, x);
@@ -163,7 +172,7 @@ template <int KIND>
 __device__ __forceinline__ float gated_act(float g, float u, const ActParams& p) {
   if constexpr (KIND == 1) {  // swiglustep: min(SiLU(G), c) Uc
     const float uc = fminf(fmaxf(u, -p.clamp), p.clamp);
-    return fminf(g / (1.0f + expf(-g)), p.clamp) * uc;
+    return fminf(g * sigmoid(g), p.clamp) * uc;
   } else if constexpr (KIND == 2) {  // swigluoai: Gc sigma(alpha Gc) (Uc + beta)
     const float gc = fminf(g, p.clamp), uc = fminf(fmaxf(u, -p.clamp), p.clamp);
     return gc * sigmoid(p.alpha * gc) * (uc + p.beta);

@@ -478,9 +478,11 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
       const int64_t at = row + 16 * tile + 4 * g;
       const v4f& v = acc[q][j];
       if constexpr (OBF16) {
+        v4f x = v;
+        asm volatile("" : "+v"(x));   // through vector registers, as the fp32 path
         uint2 u;
-        u.x = (uint32_t)f_to_bf16(v[0]) | ((uint32_t)f_to_bf16(v[1]) << 16);
-        u.y = (uint32_t)f_to_bf16(v[2]) | ((uint32_t)f_to_bf16(v[3]) << 16);
+        u.x = bf16x2(x[0], x[1]);
+        u.y = bf16x2(x[2], x[3]);
         *reinterpret_cast<uint2*>(o16 + at) = u;
       } else {
         v4f x = v;

@@ -10,12 +10,17 @@
 // (E, H, I), every output channel a K-contiguous row with one E8M0 scale per 32; the
 // first I channels of weight1 are the gate branch, the last I the up branch.
 //
+// These kernels take layers whose experts hold at most 128 rows on average (decode-
+// shaped); layers with more rows per expert take the LDS-streaming kernels of
+// gmm_stream.hip (gmm_token_tiles chooses).
+//
 // Design (one kernel per GEMM, persistent):
 // * Work item = (token chunk of one expert, channel block). A chunk holds up to 16*NT
-//   rows of one expert (device-built tile list, no host readback of the counts).
-// * Each wave owns 64 output channels (GMM1: 32 gate + the matching 32 up channels;
-//   GMM2 over 288-row chunks: 48) and streams their weights from HBM straight into VGPRs
-//   exactly once per chunk, with a one- or two-step register prefetch. The chunk's token rows are staged per K step into LDS
+//   rows of one expert, NT = 1, 2, 4 or 8 (device-built tile list, no host readback of
+//   the counts).
+// * Each wave owns 64 output channels (GMM1: 32 gate + the matching 32 up channels) and
+//   streams their weights from HBM straight into VGPRs exactly once per chunk, with a
+//   two-step register prefetch. The chunk's token rows are staged per K step into LDS
 //   (double-buffered, laid out exactly as the MFMA operand so every ds_read_b128 is
 //   conflict-free) and shared by the block's waves.
 // * V_MFMA_SCALE_F32_16X16X128_F8F6F4 with the E8M0 scales applied by the matrix core.
@@ -51,11 +56,10 @@ namespace {
 // tile: operand lo half, hi half, scale dword; from HBM into the VGPR buffer that step
 // uses), then the token tiles of step s + 2 (per tile this wave stages: lo half, hi
 // half, scale dword; from L2 into ring slot (s + 2) % 3). WPF (weight prefetch
-// distance) is 2 where three weight buffers fit in the registers beside the
-// accumulators, else 1. At the top of step s the weights and token tiles of step s
-// must have landed; with WPF = 2 the newest batch (step s + 1's) may be in flight,
-// with WPF = 1 the token tiles issued after step s's weights may: one fixed vmcnt.
-template <int NT> struct WeightPrefetch { static constexpr int value = NT >= 16 ? 1 : 2; };
+// distance) is 2: three weight buffers fit in the registers beside the accumulators of
+// up to 8 token tiles. At the top of step s the weights and token tiles of step s must
+// have landed; the newest batch (step s + 1's) may be in flight: one fixed vmcnt.
+template <int NT> struct WeightPrefetch { static constexpr int value = 2; };
 
 template <int NT, int WF, int QW>
 struct Batch {
@@ -366,10 +370,8 @@ void gmm1_swiglu_kernel(
 // reads them back per token (combine.hip). Combining here with fp32 atomics would send every
 // add to memory: a token's K rows are computed on different XCDs, whose L2s are not
 // coherent, so device-scope atomics are not resolved in L2.
-// QW 16-channel weight tiles per wave: 4 (256 channels a block), or 3 with 288-row
-// chunks (192 channels a block), whose 3 x 18 accumulator tiles fit the accumulation
-// registers (4 x 18 do not).
-template <int NT> struct Gmm2Tiles { static constexpr int value = NT == 18 ? 3 : 4; };
+// QW 16-channel weight tiles per wave: 4 (256 channels a block).
+template <int NT> struct Gmm2Tiles { static constexpr int value = 4; };
 
 template <int FMT, int NT, bool PACKED, int WF, bool OBF16>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(WavesPerEU<NT>::value)))

@@ -183,17 +183,16 @@ def check_requant(aq_gpu, sa_gpu, a_ref, delta, fmt, max_code_diff=0.02, max_sca
 
 def oracle_experts_parallel(cfg, experts, shared=False, workers=8, fp4=False):
     """oracle_expert_from_gpu_masters for several experts: masters regenerated on the GPU
-    one after the other, the oracle quantizations run in a thread pool (MXFP4, codes
-    packed two a byte, with fp4)."""
+    one batch of `workers` experts at a time (so that only one batch of float masters is
+    held), the oracle quantizations of a batch run in a thread pool (MXFP4, codes packed
+    two a byte, with fp4)."""
     from concurrent.futures import ThreadPoolExecutor
     t1, t2 = ("sw1", "sw2") if shared else ("w1", "w2")
-    masters = {}
-    for e in experts:
-        masters[e] = (moe_inputs.weight_master(cfg, t1, e, device=DEV).cpu(),
-                      moe_inputs.weight_master(cfg, t2, e, device=DEV).cpu())
+    experts = list(experts)
+    out = {}
 
-    def work(e):
-        m1, m2 = masters[e]
+    def work(item):
+        e, (m1, m2) = item
         q1, s1 = mxfp.quantize(m1.double().numpy(), "e2m1" if fp4 else cfg.fmt)
         q2, s2 = mxfp.quantize(m2.double().numpy(), "e2m1" if fp4 else cfg.fmt)
         if fp4:
@@ -201,4 +200,11 @@ def oracle_experts_parallel(cfg, experts, shared=False, workers=8, fp4=False):
         return e, (q1, s1, q2, s2)
 
     with ThreadPoolExecutor(max_workers=workers) as ex:
-        return dict(ex.map(work, experts))
+        for b in range(0, len(experts), workers):
+            masters = [(e, (moe_inputs.weight_master(cfg, t1, e, device=DEV).cpu(),
+                            moe_inputs.weight_master(cfg, t2, e, device=DEV).cpu()))
+                       for e in experts[b:b + workers]]
+            out.update(ex.map(work, masters))
+            if len(experts) > 4 * workers and (b // workers) % 4 == 3:
+                say(f"  oracle weights: {len(out)} of {len(experts)} experts")
+    return out

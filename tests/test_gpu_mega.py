@@ -613,14 +613,14 @@ def test_full_size_decode_a8w4():
 
 @pytest.mark.timeout(900)
 def test_full_size_decode():
-    full_size_check("decode", n_random=8, wf=rp.WEIGHTS_PACKED)
+    full_size_check("decode", n_random=128, wf=rp.WEIGHTS_PACKED)   # every token
 
 
 @pytest.mark.timeout(900)
 def test_full_size_skewed():
-    full_size_check("skewed", n_random=32)
+    full_size_check("skewed", n_random=64)
 
 
 @pytest.mark.timeout(900)
 def test_full_size_prefill():
-    full_size_check("prefill", n_random=6, wf=rp.WEIGHTS_PACKED)
+    full_size_check("prefill", n_random=64, wf=rp.WEIGHTS_PACKED)

@@ -58,10 +58,12 @@ int64_t scale_cols(int64_t cols) {
   return g + (g & 1);
 }
 
-// Chunking of the routing passes: chunk of 256 rows (<= 64Ki rows) or 1024, grown
-// until the per-chunk histogram table stays within 2Mi entries.
+// Chunking of the routing passes: chunk of 256 rows (<= 4Ki rows) or 1024, grown
+// until the per-chunk histogram table stays within 2Mi entries. 1024-row chunks keep the
+// chunk count of mid-size layers (24Ki-64Ki rows) at or below 64, where the scatter pass
+// scans the histogram itself (two launches instead of three or four).
 void route_chunks(int64_t flat, int active, int* nch, int* chunk) {
-  int64_t c = flat <= 65536 ? 256 : 1024;
+  int64_t c = flat <= 4096 ? 256 : 1024;
   int64_t n = std::max<int64_t>(1, (flat + c - 1) / c);
   while (n * std::max(active, 1) > (int64_t(1) << 21)) {
     c *= 2;
@@ -707,21 +709,27 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   e = moe::launch_routing(rp, st);
   if (e != hipSuccess) return hip_fail(e, "mega_moe routing launch");
   if (n == 0) return ok();
-  e = moe::launch_build_tiles(w.r.offsets, (int)ne, (int)flat, 16 * w.tt, w.max_tiles, w.tiles, w.tile_count, st);
-  if (e != hipSuccess) return hip_fail(e, "mega_moe tile list launch");
-  if (w.fold) {
-    e = moe::launch_append_shared_tiles(w.tile_count, w.max_tiles, (int)n, 16 * w.sh_tt, (int)ne,
-                                        (int)w.routed_padded, (int)flat, w.tiles, w.all_count, st);
-    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile list launch");
+  // the chunk lists: routed experts, the folded shared expert after them, the shared
+  // expert's own list (its token-order rows), and the chunk classes
+  moe::ChunkListParams cl;
+  cl.offsets = w.r.offsets; cl.groups = (int)ne; cl.rows = (int)flat; cl.tm = 16 * w.tt; cl.max_tiles = w.max_tiles;
+  cl.tiles = w.tiles; cl.count = w.tile_count;
+  if (a->num_shared > 0) {
+    cl.sh_rows = (int)n; cl.sh_tm = 16 * w.sh_tt;
+    cl.sh_tiles = w.sh_tiles; cl.sh_count = w.sh_count;
+    if (w.fold) {
+      cl.sh_group = (int)ne; cl.sh_prow0 = (int)w.routed_padded; cl.sh_srow0 = (int)flat;
+      cl.count_all = w.all_count;
+    }
   }
   moe::StreamClasses classes;
   if (w.cls_tiles) {
     const int all_max = w.max_tiles + (w.fold ? w.sh_max_tiles : 0);
-    e = moe::launch_split_stream_chunks(w.tiles, w.fold ? w.all_count : w.tile_count, all_max, w.cls_tiles,
-                                        w.cls_count, st);
-    if (e != hipSuccess) return hip_fail(e, "mega_moe chunk split launch");
+    cl.cls_tiles = w.cls_tiles; cl.cls_count = w.cls_count; cl.cls_stride = all_max;
     classes.tiles = w.cls_tiles; classes.count = w.cls_count; classes.stride = all_max;
   }
+  e = moe::launch_chunk_lists(cl, st);
+  if (e != hipSuccess) return hip_fail(e, "mega_moe chunk list launch");
   if ((e = mark(1)) != hipSuccess) return hip_fail(e, "mega_moe event record");
   // stage 1b: gather + MX quantization into the tiled layout (and the token-order rows
   // of the shared experts)
@@ -751,8 +759,6 @@ moe_status mega_moe(const moe_mega_args* a, void* workspace, size_t workspace_by
   }
   if (e != hipSuccess) return hip_fail(e, "mega_moe permute launch");
   if (a->num_shared > 0) {
-    e = moe::launch_single_group_tiles((int)n, 16 * w.sh_tt, w.sh_tiles, w.sh_count, st);
-    if (e != hipSuccess) return hip_fail(e, "mega_moe shared tile launch");
     if (codes_in) {
       e = moe::launch_pack_tokens(xcodes, xscales, (int)h, w.sh_tiles, w.sh_count, w.sh_max_tiles, w.sh_tt,
                                   w.xq_sh, w.sx_sh, st);

@@ -488,54 +488,6 @@ __global__ void pack_scales_kernel(const uint8_t* __restrict__ scales, uint32_t*
   }
 }
 
-__global__ void single_group_tiles_kernel(int rows, int tm, int4* __restrict__ tiles, int* __restrict__ count) {
-  const int nt = (rows + tm - 1) / tm;
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < nt; i += gridDim.x * blockDim.x)
-    tiles[i] = make_int4(0, i * tm, min(tm, rows - i * tm), i * tm);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *count = nt;
-}
-
-// One shared expert's chunks (token rows [0, rows), chunks of tm rows, group `group`,
-// padded rows prow0 + r, sorted rows srow0 + r) after the routed chunks (*count_in, at
-// most max_routed); *count_out = all chunks.
-__global__ void append_shared_tiles_kernel(const int* __restrict__ count_in, int max_routed, int rows, int tm,
-                                           int group, int prow0, int srow0, int4* __restrict__ tiles,
-                                           int* __restrict__ count_out) {
-  const int nt = (rows + tm - 1) / tm;
-  const int base = min(*count_in, max_routed);
-  for (int c = blockIdx.x * blockDim.x + threadIdx.x; c < nt; c += gridDim.x * blockDim.x)
-    tiles[base + c] = make_int4(group, prow0 + c * tm, min(tm, rows - c * tm), srow0 + c * tm);
-  if (blockIdx.x == 0 && threadIdx.x == 0) *count_out = base + nt;
-}
-
-// One wave: a stable split of the chunk list by the token tiles a wave needs,
-// ceil(tiles / 4), into the classes of kStreamClassRT.
-__global__ __launch_bounds__(64) void split_stream_chunks_kernel(const int4* __restrict__ chunks,
-                                                                  const int* __restrict__ count, int max_tiles,
-                                                                  int4* __restrict__ out, int* __restrict__ out_count) {
-  const int lane = threadIdx.x;
-  const int n = min(*count, max_tiles);
-  int base[kStreamClasses] = {};
-  for (int i0 = 0; i0 < n; i0 += 64) {
-    const int i = i0 + lane;
-    const bool valid = i < n;
-    const int4 c = valid ? chunks[i] : make_int4(0, 0, 0, 0);
-    const int rt = (((c.z + 15) >> 4) + 3) >> 2;
-    int cls = kStreamClasses - 1;
-#pragma unroll
-    for (int k = kStreamClasses - 2; k >= 0; --k)
-      if (rt <= kStreamClassRT[k]) cls = k;
-#pragma unroll
-    for (int k = 0; k < kStreamClasses; ++k) {
-      const uint64_t m = __ballot(valid && cls == k);
-      if (valid && cls == k) out[k * max_tiles + base[k] + __popcll(m & ((1ull << lane) - 1))] = c;
-      base[k] += __popcll(m);
-    }
-  }
-  if (lane == 0)
-    for (int k = 0; k < kStreamClasses; ++k) out_count[k] = base[k];
-}
-
 template <int FMT, int NT, bool PACKED, int EPI, int WF>
 hipError_t gmm1_go(const Gmm1Params& p, hipStream_t st) {
   auto kern = gmm1_swiglu_kernel<FMT, NT, PACKED, EPI, WF>;
@@ -655,24 +607,6 @@ hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, 
   pack_codes_fp4_kernel<<<(unsigned)b1, 256, 0, st>>>(codes, packed, pieces, (int)k);
   pack_scales_kernel<<<(unsigned)b2, 256, 0, st>>>(scales, reinterpret_cast<uint32_t*>(packed_scales), words, (int)n,
                                                    (int)k);
-  return hipGetLastError();
-}
-
-hipError_t launch_append_shared_tiles(const int* count_in, int max_routed, int rows, int tm, int group, int prow0,
-                                      int srow0, int4* tiles, int* count_out, hipStream_t st) {
-  append_shared_tiles_kernel<<<4, 256, 0, st>>>(count_in, max_routed, rows, tm, group, prow0, srow0, tiles,
-                                                 count_out);
-  return hipGetLastError();
-}
-
-hipError_t launch_split_stream_chunks(const int4* chunks, const int* count, int max_tiles, int4* out, int* out_count,
-                                      hipStream_t st) {
-  split_stream_chunks_kernel<<<1, 64, 0, st>>>(chunks, count, max_tiles, out, out_count);
-  return hipGetLastError();
-}
-
-hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t st) {
-  single_group_tiles_kernel<<<64, 256, 0, st>>>(rows, tm, tiles, count);
   return hipGetLastError();
 }
 

@@ -137,10 +137,30 @@ struct StreamClasses {
   const int* count = nullptr;
   int stride = 0;
 };
-// Splits chunks[0, min(*count, max_tiles)) into the classes above (stable order):
-// out + c max_tiles, out_count[c].
-hipError_t launch_split_stream_chunks(const int4* chunks, const int* count, int max_tiles, int4* out, int* out_count,
-                                      hipStream_t stream);
+
+// Every chunk list of one layer call in one launch (one workgroup, routing.hip):
+// * tiles[0, *count): the routed experts' chunks, as launch_build_tiles (offsets, groups,
+//   rows, tm, max_tiles);
+// * count_all != nullptr: one shared expert folded in, its chunks (group sh_group over
+//   sh_rows token rows in chunks of sh_tm rows, padded rows sh_prow0 + r, sorted rows
+//   sh_srow0 + r) right after the routed ones; *count_all = all chunks;
+// * sh_tiles != nullptr: the shared expert's own list, {0, i sh_tm, rows, i sh_tm};
+// * cls_tiles != nullptr: all chunks split into the classes above (stable order), class c
+//   at cls_tiles + c cls_stride, cls_count[c].
+struct ChunkListParams {
+  const int* offsets = nullptr;
+  int groups = 0, rows = 0, tm = 0, max_tiles = 0;
+  int4* tiles = nullptr;
+  int* count = nullptr;
+  int sh_rows = 0, sh_tm = 16, sh_group = 0, sh_prow0 = 0, sh_srow0 = 0;
+  int* count_all = nullptr;
+  int4* sh_tiles = nullptr;
+  int* sh_count = nullptr;
+  int4* cls_tiles = nullptr;
+  int* cls_count = nullptr;
+  int cls_stride = 0;
+};
+hipError_t launch_chunk_lists(const ChunkListParams& p, hipStream_t stream);
 
 struct Gmm1Params {
   const uint8_t* xq; const uint8_t* sx;        // tiled [padded rows, H]
@@ -191,13 +211,6 @@ hipError_t launch_pack_weights(const uint8_t* codes, const uint8_t* scales, int6
 hipError_t launch_pack_weights_fp4(const uint8_t* codes, const uint8_t* scales, int64_t groups, int64_t n, int64_t k,
                                    uint8_t* packed, uint8_t* packed_scales, hipStream_t stream);
 
-// Chunks of one group covering rows [0, rows): tiles[i] = {0, i*tm, min(tm, rows - i*tm), i*tm}.
-hipError_t launch_single_group_tiles(int rows, int tm, int4* tiles, int* count, hipStream_t stream);
-// After *count_in routed chunks (at most max_routed): the chunks of one shared expert
-// (group `group`) over `rows` token rows in chunks of tm rows, at padded rows prow0 + r
-// and sorted rows srow0 + r; *count_out = all chunks.
-hipError_t launch_append_shared_tiles(const int* count_in, int max_routed, int rows, int tm, int group, int prow0,
-                                      int srow0, int4* tiles, int* count_out, hipStream_t stream);
 
 // ---- weighted combine (combine.hip) -------------------------------------------------
 // Y[t] = bf16(sum_k w[t, k] * O[pos[t*K + k]] + sum_s O_shared[s][t]) for every token t:

@@ -488,10 +488,9 @@ __global__ __launch_bounds__(1024) void route_key_value(const int* __restrict__ 
 // tiles are written, so caller-given offsets can never send a GEMM out of bounds.
 // Each group is padded to whole 16-row tiles in the tiled token layout: its padded
 // start is the sum of the padded sizes of the groups before it.
-__global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict__ offsets, int G, int rows, int tm,
-                                                           int max_tiles, int4* __restrict__ tiles,
-                                                           int* __restrict__ count) {
-  __shared__ int part[1024];
+// One 1024-thread workgroup; returns the number of chunks written (block-uniform).
+__device__ int build_tiles_block(const int* __restrict__ offsets, int G, int rows, int tm, int max_tiles,
+                                 int4* __restrict__ tiles, int* part) {
   const int t = threadIdx.x;
   const int P = (G + 1023) / 1024;
   const int g0 = min(G, t * P), g1 = min(G, g0 + P);
@@ -528,7 +527,70 @@ __global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict
     pad += (cnt + 15) & ~15;
     prev = nxt;
   }
-  if (t == 0) *count = min(total, max_tiles);
+  return min(total, max_tiles);
+}
+
+__global__ __launch_bounds__(1024) void build_tiles_kernel(const int* __restrict__ offsets, int G, int rows, int tm,
+                                                           int max_tiles, int4* __restrict__ tiles,
+                                                           int* __restrict__ count) {
+  __shared__ int part[1024];
+  const int n = build_tiles_block(offsets, G, rows, tm, max_tiles, tiles, part);
+  if (threadIdx.x == 0) *count = n;
+}
+
+// Chunks c < nt of one group over `rows` rows in chunks of tm rows: {group, prow0 + c tm,
+// rows in the chunk, srow0 + c tm}, written to out[c].
+__device__ void group_chunks(int rows, int tm, int group, int prow0, int srow0, int4* __restrict__ out) {
+  const int nt = (rows + tm - 1) / tm;
+  for (int c = threadIdx.x; c < nt; c += blockDim.x)
+    out[c] = make_int4(group, prow0 + c * tm, min(tm, rows - c * tm), srow0 + c * tm);
+}
+
+// One wave: a stable split of chunks[0, n) by the token tiles a wave needs, ceil(tiles /
+// 4), into the classes of kStreamClassRT (class c at out + c stride, out_count[c]).
+__device__ void split_chunks_wave(const int4* __restrict__ chunks, int n, int stride, int4* __restrict__ out,
+                                  int* __restrict__ out_count) {
+  const int lane = threadIdx.x & 63;
+  int base[kStreamClasses] = {};
+  for (int i0 = 0; i0 < n; i0 += 64) {
+    const int i = i0 + lane;
+    const bool valid = i < n;
+    const int4 c = valid ? chunks[i] : make_int4(0, 0, 0, 0);
+    const int rt = (((c.z + 15) >> 4) + 3) >> 2;
+    int cls = kStreamClasses - 1;
+#pragma unroll
+    for (int k = kStreamClasses - 2; k >= 0; --k)
+      if (rt <= kStreamClassRT[k]) cls = k;
+#pragma unroll
+    for (int k = 0; k < kStreamClasses; ++k) {
+      const uint64_t m = __ballot(valid && cls == k);
+      if (valid && cls == k) out[k * stride + base[k] + __popcll(m & ((1ull << lane) - 1))] = c;
+      base[k] += __popcll(m);
+    }
+  }
+  if (lane == 0)
+    for (int k = 0; k < kStreamClasses; ++k) out_count[k] = base[k];
+}
+
+// All chunk lists of one layer call in one workgroup (see ChunkListParams).
+__global__ __launch_bounds__(1024) void chunk_lists_kernel(ChunkListParams p) {
+  __shared__ int part[1024];
+  const int routed = build_tiles_block(p.offsets, p.groups, p.rows, p.tm, p.max_tiles, p.tiles, part);
+  if (threadIdx.x == 0) *p.count = routed;
+  int all = routed;
+  if (p.count_all) {   // the folded shared expert's chunks right after the routed ones
+    group_chunks(p.sh_rows, p.sh_tm, p.sh_group, p.sh_prow0, p.sh_srow0, p.tiles + routed);
+    all = routed + (p.sh_rows + p.sh_tm - 1) / p.sh_tm;
+    if (threadIdx.x == 0) *p.count_all = all;
+  }
+  if (p.sh_tiles) {    // the shared expert's own list: rows [0, sh_rows) of group 0
+    group_chunks(p.sh_rows, p.sh_tm, 0, 0, 0, p.sh_tiles);
+    if (threadIdx.x == 0) *p.sh_count = (p.sh_rows + p.sh_tm - 1) / p.sh_tm;
+  }
+  if (p.cls_tiles) {
+    __syncthreads();   // the chunk list above is written by the whole workgroup, read by wave 0
+    if (threadIdx.x < 64) split_chunks_wave(p.tiles, min(all, p.cls_stride), p.cls_stride, p.cls_tiles, p.cls_count);
+  }
 }
 
 }  // namespace
@@ -568,6 +630,11 @@ hipError_t launch_routing(const RouteParams& p, hipStream_t stream) {
 
 hipError_t launch_key_value(const int* offsets, int active, int s, int rows, int64_t* out, hipStream_t stream) {
   route_key_value<<<1, 1024, 0, stream>>>(offsets, active, s, rows, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_lists(const ChunkListParams& p, hipStream_t stream) {
+  chunk_lists_kernel<<<1, 1024, 0, stream>>>(p);
   return hipGetLastError();
 }
 

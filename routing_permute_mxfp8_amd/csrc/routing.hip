@@ -252,6 +252,25 @@ constexpr int kBlockMaxActive = 512;
 // Histogram entries (A * chunks) up to which the scatter pass may derive its chunk's
 // first positions from the histogram itself instead of a separate scan pass.
 constexpr int kScanInScatter = 16384;
+// Chunk counts per expert up to which one thread walks them in global memory (beyond:
+// one wave per expert, 64 chunk counts a step and a shuffle reduction). Counts staged in
+// LDS are always walked by one thread per expert.
+constexpr int kThreadScan = 64;
+
+// Dynamic LDS of the block path's scatter pass: per-wave counts [waves][A], first
+// positions [A], totals [A], wave sums [waves + 1].
+size_t scatter_lds(int A, int chunk) {
+  return sizeof(int) * ((size_t)(chunk / 64) * A + (size_t)2 * A + chunk / 64 + 1);
+}
+
+// Whether the scanning scatter pass stages the chunk counts in LDS (16-bit each, the
+// histogram's [A][nch] layout) after those buffers: for 17-64 chunks (the walks of up to
+// 16 chunks read global memory about as fast; longer LDS walks are latency-bound, where
+// one wave per expert reads global memory faster), when all of it stays within 64 KB.
+__host__ __device__ inline bool scatter_stages(int A, int nch, int nw) {
+  const int64_t base = (int64_t)4 * ((int64_t)nw * A + 2 * A + nw + 1);
+  return nch > 16 && nch <= 64 && base + (int64_t)2 * A * nch <= 65536;
+}
 
 template <typename KeyT>
 __device__ __forceinline__ void block_rank(const KeyT* __restrict__ keys, int64_t r, bool valid, int s, int A,
@@ -321,7 +340,43 @@ __global__ __launch_bounds__(1024) void route_scatter_block(
   const bool act = a < A;
   int avail;
   if constexpr (SCAN) {
-    if (nch <= 64) {   // few chunks: one thread per expert walks its chunk counts
+    // The chunk counts (each at most the chunk's 1024 rows) into LDS as 16-bit values when
+    // they fit (scatter_stages); the walks below then read LDS instead of waiting on one
+    // global load after another.
+    const bool staged = scatter_stages(A, nch, nw);
+    uint16_t* hl = reinterpret_cast<uint16_t*>(part + nw + 1);
+    if (staged) {   // flat copy, eight loads in flight per thread
+      const int n = A * nch;
+      for (int i0 = 0; i0 < n; i0 += 8 * (int)blockDim.x) {
+        int v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * (int)blockDim.x + tid;
+          v[u] = i < n ? hist[i] : 0;
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          const int i = i0 + u * (int)blockDim.x + tid;
+          if (i < n) hl[i] = (uint16_t)v[u];
+        }
+      }
+      __syncthreads();
+      // one thread per expert walks its row, starting at chunk ex % nch so that the threads
+      // of a wave read different banks (the sums do not depend on the order)
+      for (int ex = tid; ex < A; ex += blockDim.x) {
+        const uint16_t* h = hl + ex * nch;
+        int before = 0, total = 0;
+        int cc = ex % nch;
+        for (int j = 0; j < nch; ++j) {
+          const int v = h[cc];
+          total += v;
+          if (cc < c) before += v;
+          cc = cc + 1 == nch ? 0 : cc + 1;
+        }
+        pre[ex] = before;
+        tot[ex] = total;
+      }
+    } else if (nch <= kThreadScan) {   // one thread per expert walks its chunk counts
       for (int ex = tid; ex < A; ex += blockDim.x) {
         const int* h = hist + (int64_t)ex * nch;
         int before = 0, total = 0;
@@ -333,23 +388,24 @@ __global__ __launch_bounds__(1024) void route_scatter_block(
         pre[ex] = before;
         tot[ex] = total;
       }
-    }
-    for (int ex = nch <= 64 ? A : wave; ex < A; ex += nw) {   // else one wave per expert
-      const int* h = hist + (int64_t)ex * nch;
-      int before = 0, total = 0;
-      for (int cc = lane; cc < nch; cc += 64) {
-        const int v = h[cc];
-        total += v;
-        if (cc < c) before += v;
-      }
+    } else {   // one wave per expert
+      for (int ex = wave; ex < A; ex += nw) {
+        const int* h = hist + (int64_t)ex * nch;
+        int before = 0, total = 0;
+        for (int cc = lane; cc < nch; cc += 64) {
+          const int v = h[cc];
+          total += v;
+          if (cc < c) before += v;
+        }
 #pragma unroll
-      for (int d = 32; d >= 1; d >>= 1) {
-        before += __shfl_xor(before, d);
-        total += __shfl_xor(total, d);
-      }
-      if (lane == 0) {
-        pre[ex] = before;
-        tot[ex] = total;
+        for (int d = 32; d >= 1; d >>= 1) {
+          before += __shfl_xor(before, d);
+          total += __shfl_xor(total, d);
+        }
+        if (lane == 0) {
+          pre[ex] = before;
+          tot[ex] = total;
+        }
       }
     }
     __syncthreads();
@@ -433,9 +489,10 @@ hipError_t routing_block_path(const RouteParams& p, int A, int nbits, hipStream_
   // in-kernel scan only where it is short: at most 64 chunk counts per thread (thread per
   // expert) or at most two experts per wave (wave per expert)
   const bool scan_here = (p.nch <= 64 && (int64_t)A * p.nch <= kScanInScatter) || A <= 2 * (p.chunk / 64);
-  const size_t sl = wl + sizeof(int) * ((size_t)2 * A + p.chunk / 64 + 1);
+  const size_t sl = scatter_lds(A, p.chunk);
   if (scan_here) {
-    route_scatter_block<KeyT, true><<<p.nch, p.chunk, sl, stream>>>(
+    const size_t sls = sl + (scatter_stages(A, p.nch, p.chunk / 64) ? (size_t)2 * A * p.nch : 0);
+    route_scatter_block<KeyT, true><<<p.nch, p.chunk, sls, stream>>>(
         keys, p.flat, p.topk, p.s, A, nbits, p.chunk, p.hist, p.base, p.offsets, p.avail64, p.expert_tokens,
         p.tokens_type, p.token_nums32, p.scat, p.gath, p.gath_fill, p.row_token, p.row_weight, p.topk_w,
         p.topk_w_bf16);

@@ -130,6 +130,9 @@ __device__ __forceinline__ int block_tile(int cb, int q, int n16, int i16) {
 
 // Buffer descriptor word 3 for raw (untyped) buffer loads on CDNA.
 constexpr int kRsrcWord3 = 0x00020000;
+// Cache-policy operand of a buffer load: non-temporal (the weight codes are streamed once
+// per chunk; a plain streaming read measured ~6.3 TB/s, a non-temporal one ~7.1 TB/s).
+constexpr int kNonTemporal = 2;
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, int64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, kRsrcWord3);
@@ -245,7 +248,7 @@ __device__ __forceinline__ void issue_weight_tile(const WeightStep& L, int i, ui
     else
       so = tile * 16 * K + 128 * L.k + 64 * h;
     __builtin_amdgcn_raw_ptr_buffer_load_lds(L.wr, (lds_void_ptr)(slot + q * SW::kCode + h * 1024), 16, lo.wcode, so,
-                                             0, 0);
+                                             0, kNonTemporal);
   }
 }
 

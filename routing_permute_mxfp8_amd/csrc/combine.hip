@@ -32,12 +32,17 @@ __device__ __forceinline__ float round_bf16(float v) { return bf16_to_f(f_to_bf1
 // 2 bf16.
 template <int OF>
 __device__ __forceinline__ float4 load4(const void* base, int64_t row, int hidden, int c) {
+  // (each expert row is read once: non-temporal loads)
   if constexpr (OF == 2) {
-    const uint2 u = reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + row * hidden)[c];
-    return make_float4(bf16_to_f((uint16_t)u.x), bf16_to_f((uint16_t)(u.x >> 16)), bf16_to_f((uint16_t)u.y),
-                       bf16_to_f((uint16_t)(u.y >> 16)));
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    const u32x2 u =
+        __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(reinterpret_cast<const uint16_t*>(base) + row * hidden) + c);
+    return make_float4(bf16_to_f((uint16_t)u[0]), bf16_to_f((uint16_t)(u[0] >> 16)), bf16_to_f((uint16_t)u[1]),
+                       bf16_to_f((uint16_t)(u[1] >> 16)));
   } else {
-    float4 v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + row * hidden)[c];
+    const v4f u =
+        __builtin_nontemporal_load(reinterpret_cast<const v4f*>(reinterpret_cast<const float*>(base) + row * hidden) + c);
+    float4 v = make_float4(u[0], u[1], u[2], u[3]);
     if constexpr (OF == 1) v = make_float4(round_bf16(v.x), round_bf16(v.y), round_bf16(v.z), round_bf16(v.w));
     return v;
   }
@@ -86,10 +91,11 @@ __global__ __launch_bounds__(256) void combine_kernel(const void* __restrict__ o
       const float4 v = load4<SF>(o_shared, (int64_t)s * tokens + t, hidden, c);
       acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
     }
-    uint2 out;
-    out.x = (uint32_t)f_to_bf16(acc.x) | ((uint32_t)f_to_bf16(acc.y) << 16);
-    out.y = (uint32_t)f_to_bf16(acc.z) | ((uint32_t)f_to_bf16(acc.w) << 16);
-    reinterpret_cast<uint2*>(y + t * hidden)[c] = out;
+    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+    u32x2 out;
+    out[0] = (uint32_t)f_to_bf16(acc.x) | ((uint32_t)f_to_bf16(acc.y) << 16);
+    out[1] = (uint32_t)f_to_bf16(acc.z) | ((uint32_t)f_to_bf16(acc.w) << 16);
+    __builtin_nontemporal_store(out, reinterpret_cast<u32x2*>(y + t * hidden) + c);   // Y is not read back here
   }
 }
 

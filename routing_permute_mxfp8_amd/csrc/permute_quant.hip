@@ -27,8 +27,8 @@ constexpr int kUnroll = 4;
 template <typename InT> struct Load8;
 template <> struct Load8<uint16_t> {  // bf16
   static __device__ __forceinline__ void run(const uint16_t* p, float* f) {
-    const uint4 u = *reinterpret_cast<const uint4*>(p);
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    const u32x4 u = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));   // each row is read once
+    const uint32_t w[4] = {u[0], u[1], u[2], u[3]};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       f[2 * i] = __uint_as_float(w[i] << 16);

@@ -402,7 +402,7 @@ def bench_routing(args, torch, rp, moe_inputs):
     torch.cuda.synchronize()
     flush.fill_(0)
     for a, b in evs:
-        rp.probe_stream(flush)
+        rp.probe_stream(flush, fill_caches=True)
         a.record()
         rp.init_routing(x, ids_d, cfg.experts, (s, e), q, 1, 1)
         b.record()

@@ -398,7 +398,11 @@ moe_status moe_combine_finalize(const float* y_accum, int64_t num_tokens, int64_
 /* it with events on `stream`).                                                */
 /* moe_probe_stream: mode 0 reads `bytes` from src (dst receives nothing      */
 /*   unless an impossible value turns up; give a 16-byte buffer), mode 1     */
-/*   copies them to dst. bytes: a positive multiple of 16; both device.       */
+/*   copies them to dst, both with non-temporal accesses (the GPU's best      */
+/*   streaming rates); mode 2 reads like mode 0 with plain, cache-filling      */
+/*   loads (evicts other data from the caches, e.g. before a cold-cache       */
+/*   timing). bytes: a positive multiple of 16; both device. Any other mode:   */
+/*   MOE_ERR_INVALID_ARG.                                                     */
 /* moe_probe_mfma: `iters` rounds of 16 independent V_MFMA_SCALE 16x16x128    */
 /*   FP8 products per wave, two 256-thread blocks per compute unit; out:     */
 /*   device fp32, at least *out_floats (host out, may be queried with        */

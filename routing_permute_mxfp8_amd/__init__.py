@@ -497,16 +497,19 @@ def combine_finalize(y_accum):
     return y
 
 
-def probe_stream(src, dst=None, copy: bool = False):
+def probe_stream(src, dst=None, copy: bool = False, fill_caches: bool = False):
     """One launch of the library's streaming kernel: read src (uint8 device tensor, a
-    multiple of 16 bytes), or copy it to dst. Returns None; time it with events."""
+    multiple of 16 bytes), or copy it to dst, with non-temporal accesses; with
+    fill_caches a read with plain loads (to evict other data from the caches). Returns
+    None; time it with events."""
     lib = load()
     _need_gpu(src)
     if copy and (dst is None or dst.numel() < src.numel()):
         raise ValueError("probe_stream: copy needs a dst at least as large as src")
     if dst is None:
         dst = torch.empty(16, dtype=torch.uint8, device=src.device)
-    _check(lib.moe_probe_stream(1 if copy else 0, _ptr(src), _ptr(dst), src.numel(), _stream(src.device)))
+    mode = 1 if copy else (2 if fill_caches else 0)
+    _check(lib.moe_probe_stream(mode, _ptr(src), _ptr(dst), src.numel(), _stream(src.device)))
 
 
 def probe_mfma(iters: int, out=None, device="cuda"):

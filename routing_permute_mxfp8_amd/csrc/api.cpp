@@ -925,7 +925,7 @@ moe_status moe_combine_finalize(const float* y_accum, int64_t num_tokens, int64_
 }
 
 moe_status moe_probe_stream(int mode, const void* src, void* dst, int64_t bytes, void* stream) {
-  if (mode != 0 && mode != 1) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream: mode %d not 0 or 1", mode);
+  if (mode < 0 || mode > 2) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream: mode %d not 0, 1 or 2", mode);
   if (bytes <= 0 || bytes % 16 != 0) return fail(MOE_ERR_SHAPE, "moe_probe_stream: bytes must be a positive multiple of 16");
   if (!src || !dst) return fail(MOE_ERR_INVALID_ARG, "moe_probe_stream: NULL buffer");
   hipError_t e = moe::launch_probe_stream(mode, src, dst, bytes, (hipStream_t)stream);

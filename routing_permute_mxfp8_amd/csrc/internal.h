@@ -245,7 +245,8 @@ constexpr size_t kNoAllocScratchBytes = size_t(8) << 20;
 hipError_t noalloc_scratch(void** out);
 
 // ---- measured peaks (peaks.hip) ------------------------------------------------------
-hipError_t launch_probe_stream(int copy, const void* src, void* dst, int64_t bytes, hipStream_t stream);
+// mode 0: non-temporal read, 1: non-temporal copy, 2: plain (cache-filling) read
+hipError_t launch_probe_stream(int mode, const void* src, void* dst, int64_t bytes, hipStream_t stream);
 int probe_mfma_blocks();   // blocks of 256 threads the MFMA probe launches (one per CU)
 hipError_t launch_probe_mfma(int iters, float* out, hipStream_t stream);
 double probe_mfma_flops(int iters);

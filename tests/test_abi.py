@@ -183,7 +183,8 @@ def test_mega_moe_validation(lib):
 
 def test_probe_validation(lib):
     """The measurement probes reject bad arguments before any launch."""
-    assert lib.moe_probe_stream(2, FAKE, FAKE, 1024, None) == 1          # mode
+    assert lib.moe_probe_stream(3, FAKE, FAKE, 1024, None) == 1          # mode
+    assert lib.moe_probe_stream(-1, FAKE, FAKE, 1024, None) == 1
     assert lib.moe_probe_stream(0, FAKE, FAKE, 1000, None) == 2          # not a multiple of 16
     assert lib.moe_probe_stream(0, FAKE, FAKE, 0, None) == 2
     assert lib.moe_probe_stream(1, None, FAKE, 1024, None) == 1          # NULL buffer

@@ -60,3 +60,21 @@ def test_other_input_dtypes(dtype):
     assert scales.shape == (37, 4)
     assert np.array_equal(scales.cpu().numpy(), os_)
     assert np.array_equal(codes.cpu().numpy(), oc)
+
+
+@pytest.mark.gpu
+def test_bandwidth_probes():
+    """The roofline probes: the non-temporal copy copies every byte (a buffer whose size is
+    not a multiple of the kernel's 4 KB step per thread group), the reads (non-temporal and
+    cache-filling) and the MFMA loop run and report positive work."""
+    n = (64 << 20) + 16 * 37
+    src = torch.randint(0, 256, (n,), dtype=torch.uint8, device=DEV)
+    dst = torch.zeros(n + 64, dtype=torch.uint8, device=DEV)
+    rp.probe_stream(src, dst, copy=True)
+    rp.probe_stream(src)
+    rp.probe_stream(src, fill_caches=True)
+    out, flops = rp.probe_mfma(10)
+    torch.cuda.synchronize()
+    assert torch.equal(dst[:n], src)
+    assert int(dst[n:].count_nonzero()) == 0
+    assert flops > 0 and out.numel() > 0

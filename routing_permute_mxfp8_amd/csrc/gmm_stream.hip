@@ -30,7 +30,9 @@
 //
 // Per K step and wave: one fixed vmcnt wait (this step's weight slot, landed by every
 // wave's own loads) and one barrier (every wave's loads have landed; every wave is done
-// with the slot about to be refilled); then the token loads of step + 3 and this wave's
+// with the slot about to be refilled) -- with six LDS slots (kLead + 2, where they fit)
+// the wait and the barrier come every second step and cover two steps' slots (the
+// waves then drift apart by up to a step between barriers); then the token loads of step + 3 and this wave's
 // share of the weight loads of step + kLead (always the same number of each, so the
 // wait count is a constant: loads past the last step or for tiles the wave does not own
 // read valid addresses again); then the MFMAs. The epilogue of an item (activation and
@@ -52,8 +54,7 @@ namespace {
 
 constexpr int kCB = 12;         // 16-channel weight tiles per channel block (192 channels)
 constexpr int kRT = 5;          // most token tiles per wave: a chunk holds up to 20 tiles (320 rows)
-constexpr int kSlots = 5;       // LDS weight slots
-constexpr int kLead = 4;        // weight loads run kLead steps ahead (kSlots - 1)
+constexpr int kLead = 4;        // weight loads run kLead steps ahead
 constexpr int kTokLead = 3;     // token loads run three steps ahead (four register sets)
 
 // LDS: kSlots weight code slots (one K step of the channel block each), then two scale
@@ -71,6 +72,9 @@ struct StreamW {
   static constexpr int kWsTile = PACKED ? kTileScaleBytes : 1024;
   static constexpr int kTsOff = kCB * kWsTile;       // token scales in a group
   static constexpr int kGroupBytes = kTsOff + 4 * kRT * kTileScaleBytes;
+  // weight slots: kLead + 2 where they fit in LDS (the barrier every second step), else
+  // kLead + 1 (a barrier every step)
+  static constexpr int kSlots = 6 * kSlotBytes + 2 * kGroupBytes <= 160 * 1024 ? 6 : 5;
   static constexpr int kGroups = kSlots * kSlotBytes;   // offset of the two scale groups
   static constexpr int kLds = kGroups + 2 * kGroupBytes;
   static constexpr int kDma = (kCB / 4) * kHalves;   // weight code loads per wave and step
@@ -85,6 +89,11 @@ struct StreamW {
   // (kTokLoads = 2 RT per wave and step: lo and hi half of each of its RT token tiles)
   template <int RT>
   static constexpr int kWait = 3 * (kDma + 2 * RT);
+  // With six slots the wait at the top of an even step g also covers W(g + 1), issued in
+  // step g - 3: the ops after it are at least two whole steps' worth (the scales of
+  // steps g and g + 1 belong to one group, issued in step g - 4 or earlier).
+  template <int RT>
+  static constexpr int kWaitPair = 2 * (kDma + 2 * RT);
   static_assert(kWait<kRT> <= 63, "vmcnt holds at most 63");
   static_assert(kLds <= 160 * 1024, "LDS per workgroup");
 };
@@ -569,18 +578,22 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
     // K step kc of item n with the token registers of set (tc); the token loads of
     // kc + kTokLead go into set (tn), the set the previous step used; a step kc = 0 mod 4
     // also loads the scale group of steps kc + 4 .. kc + 7 into the other group.
-    auto step = [&](int kc, bool group_start, v8i(&tc)[RT], v8i(&tn)[RT]) {
-      wait_vmcnt<SW::template kWait<RT>>();
-      __builtin_amdgcn_sched_barrier(0);
-      __builtin_amdgcn_s_barrier();
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
+    // (even: kc is even; with six slots only even steps wait and meet the barrier)
+    auto step = [&](int kc, bool group_start, bool even, v8i(&tc)[RT], v8i(&tn)[RT]) {
+      constexpr bool kPaired = SW::kSlots == 6;
+      if (!kPaired || even) {
+        wait_vmcnt<kPaired ? SW::template kWaitPair<RT> : SW::template kWait<RT>>();
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        asm volatile("" ::: "memory");
+        __builtin_amdgcn_sched_barrier(0);
+      }
       const Ahead at = ahead(cur, nxt, last_item, kc, kTokLead, ks);
       const TokenStep tl = token_step(p, at.d, at.k, ks, kq);
       const Ahead aw = ahead(cur, nxt, last_item, kc, kLead, ks);
       const WeightStep wl = weight_step<WF, PACKED>(p, aw.d, aw.k, n16);
       uint8_t* const wdst = lds + wslot * SW::kSlotBytes;
-      wslot = wslot == kSlots - 1 ? 0 : wslot + 1;
+      wslot = wslot == SW::kSlots - 1 ? 0 : wslot + 1;
       __builtin_amdgcn_sched_barrier(0);
       // the token loads before the MFMAs; the weight codes after MFMA group kWeightsAfter,
       // the scale group after the next one (placements measured best: the loads of a
@@ -600,14 +613,14 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
       };
       step_mfma<FMT, PACKED, WF, RT>(acc, ldsr + cslot * SW::kSlotBytes, groups_r + grp * SW::kGroupBytes, kc, lane,
                                       wave, tc, between);
-      cslot = cslot == kSlots - 1 ? 0 : cslot + 1;
+      cslot = cslot == SW::kSlots - 1 ? 0 : cslot + 1;
     };
     // K steps of item n (a multiple of 4): t0..t3 in turn, the first step uses t0
     for (int k = 0; k < ks; k += 4) {
-      step(k, true, t0, t3);
-      step(k + 1, false, t1, t0);
-      step(k + 2, false, t2, t1);
-      step(k + 3, false, t3, t2);
+      step(k, true, true, t0, t3);
+      step(k + 1, false, false, t1, t0);
+      step(k + 2, false, true, t2, t1);
+      step(k + 3, false, false, t3, t2);
       grp ^= 1;
     }
     const int nw = wave_tiles(cur.nrows, wave);

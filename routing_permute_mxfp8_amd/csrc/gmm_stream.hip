@@ -468,6 +468,9 @@ __device__ __forceinline__ void epilogue1(const StreamArgs& p, const Item& c, v4
 }
 
 // GMM2 epilogue: acc[q][j][i] = O[row 16 t + r][channel 16 (12 cb + q) + 4 g + i].
+// bf16 O: the lanes exchange halves of two tiles so that each stores 16 bytes (GMM2 of
+// the prefill-shaped layer 8% faster than with 8-byte stores: the store instructions of
+// an item, not its bytes, were the cost).
 template <bool OBF16, int RT>
 __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4f (&acc)[kCB][RT], int nw,
                                           int wave) {
@@ -480,24 +483,35 @@ __device__ __forceinline__ void epilogue2(const StreamArgs& p, const Item& c, v4
   for (int j = 0; j < RT; ++j) {
     if (j >= nw) break;
     const int rr = 16 * (4 * j + wave) + r;
-    if (rr >= c.nrows) continue;               // per lane; no cross-lane work below
+    const bool row_ok = rr < c.nrows;         // the same for the four lanes of row r
     const int64_t row = (int64_t)(c.srow0 + rr) * p.N;
+    if constexpr (OBF16) {
+      // tiles q, q + 1: after one row swap per dword a lane of row g holds 8 contiguous
+      // channels, 4 (g & 2) .. + 7 of tile q + (g & 1) (n16 is even: pairs never straddle
+      // the end of hidden)
 #pragma unroll
-    for (int q = 0; q < kCB; ++q) {
-      const int tile = c.cb * kCB + q;
-      if (tile >= n16) break;                  // partial last block (uniform)
-      __builtin_amdgcn_sched_barrier(0);
-      const int64_t at = row + 16 * tile + 4 * g;
-      const v4f& v = acc[q][j];
-      if constexpr (OBF16) {
-        v4f x = v;
-        asm volatile("" : "+v"(x));   // through vector registers, as the fp32 path
-        uint2 u;
-        u.x = bf16x2(x[0], x[1]);
-        u.y = bf16x2(x[2], x[3]);
-        *reinterpret_cast<uint2*>(o16 + at) = u;
-      } else {
-        v4f x = v;
+      for (int q = 0; q < kCB; q += 2) {
+        const int tile = c.cb * kCB + q;
+        if (tile >= n16) break;                  // partial last block (uniform)
+        __builtin_amdgcn_sched_barrier(0);
+        v4f x = acc[q][j], y = acc[q + 1][j];
+        asm volatile("" : "+v"(x), "+v"(y));     // through vector registers
+        const auto lo = __builtin_amdgcn_permlane16_swap(bf16x2(x[0], x[1]), bf16x2(y[0], y[1]), false, false);
+        const auto hi = __builtin_amdgcn_permlane16_swap(bf16x2(x[2], x[3]), bf16x2(y[2], y[3]), false, false);
+        if (row_ok) {
+          const int64_t at = row + 16 * (tile + (g & 1)) + 4 * (g & 2);
+          *reinterpret_cast<u32x4*>(o16 + at) = u32x4{lo[0], hi[0], lo[1], hi[1]};
+        }
+      }
+    } else {
+      if (!row_ok) continue;                    // per lane; no cross-lane work below
+#pragma unroll
+      for (int q = 0; q < kCB; ++q) {
+        const int tile = c.cb * kCB + q;
+        if (tile >= n16) break;                  // partial last block (uniform)
+        __builtin_amdgcn_sched_barrier(0);
+        const int64_t at = row + 16 * tile + 4 * g;
+        v4f x = acc[q][j];
         asm volatile("" : "+v"(x));   // through vector registers, as the bf16 path
         *reinterpret_cast<float4*>(o + at) = make_float4(x[0], x[1], x[2], x[3]);
       }

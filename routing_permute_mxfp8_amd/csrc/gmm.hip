@@ -57,16 +57,20 @@ namespace {
 // uses), then the token tiles of step s + 2 (per tile this wave stages: lo half, hi
 // half, scale dword; from L2 into ring slot (s + 2) % 3). WPF (weight prefetch
 // distance) is 2: three weight buffers fit in the registers beside the accumulators of
-// up to 8 token tiles. At the top of step s the weights and token tiles of step s must
-// have landed; the newest batch (step s + 1's) may be in flight: one fixed vmcnt.
-template <int NT> struct WeightPrefetch { static constexpr int value = 2; };
+// up to 8 token tiles; MXFP4 weights in chunks of up to 2 tiles take WPF = 3 (four
+// buffers; the half-size FP4 loads keep half the bytes in flight: GMM1 of the MXFP4
+// decode-shaped layer 2.6% faster; with FP8 weights the fourth buffer spills). At the
+// top of step s the weights and token tiles of step s must have landed; the newest
+// batch (step s + 1's) may be in flight: one fixed vmcnt (with WPF = 3 too: the batch
+// issued in step s - 2 holds the token tiles of step s and is followed by one batch).
+template <int NT, int WF> struct WeightPrefetch { static constexpr int value = WF == kFmtFp4 && NT <= 2 ? 3 : 2; };
 
 template <int NT, int WF, int QW>
 struct Batch {
   static constexpr int kWeights = QW * WeightFmt<WF>::kParts;
   static constexpr int kTokens = 3 * StageLayout<NT>::kPerWave;
   static constexpr int kLoads = kWeights + kTokens;
-  static constexpr int kInFlight = WeightPrefetch<NT>::value == 2 ? kLoads : kTokens;
+  static constexpr int kInFlight = WeightPrefetch<NT, WF>::value >= 2 ? kLoads : kTokens;
 };
 
 // NTW: the weight codes with non-temporal loads (streamed once per chunk; GMM1 measured
@@ -148,7 +152,7 @@ __device__ __forceinline__ void k_step(int s, int ks, int cur, v4f (&acc)[QW][NT
   constexpr int kBuf = StageLayout<NT>::kBufBytes;
   wait_vmcnt<Batch<NT, WF, QW>::kInFlight>();
   block_barrier<NT>();
-  const int wstep = min(s + WeightPrefetch<NT>::value, ks - 1), tstep = min(s + 2, ks - 1);
+  const int wstep = min(s + WeightPrefetch<NT, WF>::value, ks - 1), tstep = min(s + 2, ks - 1);
   uint8_t* slot = lds + (cur == 0 ? 2 : cur - 1) * kBuf;   // (cur + 2) % 3
   const uint8_t* buf = lds + cur * kBuf;
   load_slots<NT, PACKED, WF, QW, WEIGHTS_A, 0>(std::make_integer_sequence<int, kTop>{}, aload, sload, wp, wstep, tok, toks, ks, row0,
@@ -233,6 +237,71 @@ __device__ __forceinline__ void k_loop_pf2(v4f (&acc)[QW][NT], const WPtr<PACKED
   __syncthreads();
 }
 
+// The K loop of one chunk with WPF = 3: four weight register buffers with fixed roles in
+// the unrolled four-step body (a0 -> a3, a1 -> a0, a2 -> a1, a3 -> a2: the buffer a step
+// uses, then the one it loads the weights of step + 3 into); the ks % 4 leftover steps
+// run first from buffers chosen so that the roles line up at the loop's first step. The
+// prologue loads weights 0, 1, 2 and the token tiles of steps 0 and 1.
+template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
+__device__ __forceinline__ void k_loop_pf3(v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW], const uint8_t* tok,
+                                           const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
+                                           int lane) {
+  constexpr int kL = Batch<NT, WF, QW>::kLoads;
+  constexpr int kW = Batch<NT, WF, QW>::kWeights;
+  constexpr int kBuf = StageLayout<NT>::kBufBytes;
+  const int ks = K >> 7, r = ks % 4, s1 = min(1, ks - 1), s2 = min(2, ks - 1);
+  v8i a0[QW], a1[QW], a2[QW], a3[QW];
+  int c0[QW], c1[QW], c2[QW], c3[QW];
+  auto seq = std::make_integer_sequence<int, kL>{};
+  auto wseq = std::make_integer_sequence<int, kW>{};
+  auto pro = [&](v8i (&x0)[QW], int (&y0)[QW], v8i (&x1)[QW], int (&y1)[QW], v8i (&x2)[QW], int (&y2)[QW]) {
+    load_slots<NT, PACKED, WF, QW, WEIGHTS_A, 0>(seq, x0, y0, wp, 0, tok, toks, ks, row0, ntt, 0, lds, wave, lane);
+    load_slots<NT, PACKED, WF, QW, WEIGHTS_A, 0>(seq, x1, y1, wp, s1, tok, toks, ks, row0, ntt, s1, lds + kBuf, wave,
+                                                 lane);
+    load_slots<NT, PACKED, WF, QW, WEIGHTS_A, 0>(wseq, x2, y2, wp, s2, tok, toks, ks, row0, ntt, s2, lds, wave, lane);
+  };
+  if (r == 0)
+    pro(a0, c0, a1, c1, a2, c2);
+  else if (r == 1)
+    pro(a3, c3, a0, c0, a1, c1);
+  else if (r == 2)
+    pro(a2, c2, a3, c3, a0, c0);
+  else
+    pro(a1, c1, a2, c2, a3, c3);
+  int s = 0, cur = 0;
+  if (r == 1) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a3, c3, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    s = 1;
+    cur = 1;
+  } else if (r == 2) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(1, ks, 1, acc, wp, a3, c3, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    s = 2;
+    cur = 2;
+  } else if (r == 3) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(0, ks, 0, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(1, ks, 1, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave, lane);
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(2, ks, 2, acc, wp, a3, c3, a2, c2, tok, toks, row0, ntt, lds, wave, lane);
+    s = 3;
+    cur = 0;
+  }
+  for (; s < ks; s += 4) {
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s, ks, cur, acc, wp, a0, c0, a3, c3, tok, toks, row0, ntt, lds, wave, lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 1, ks, cur, acc, wp, a1, c1, a0, c0, tok, toks, row0, ntt, lds, wave,
+                                               lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 2, ks, cur, acc, wp, a2, c2, a1, c1, tok, toks, row0, ntt, lds, wave,
+                                               lane);
+    cur = cur == 2 ? 0 : cur + 1;
+    k_step<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(s + 3, ks, cur, acc, wp, a3, c3, a2, c2, tok, toks, row0, ntt, lds, wave,
+                                               lane);
+    cur = cur == 2 ? 0 : cur + 1;
+  }
+  wait_vmcnt<0>();
+  __syncthreads();
+}
+
 // The K loop of one chunk with WPF = 1: weights of step 0 and token tiles of steps 0 and
 // 1 first; if ks is odd, step 0 alone (its weight buffers then swap by copies); then
 // the steps two at a time (the two weight buffers alternate, roles fixed in the
@@ -275,7 +344,9 @@ template <int FMT, int NT, bool PACKED, bool WEIGHTS_A, int WF, int QW>
 __device__ __forceinline__ void k_loop(v4f (&acc)[QW][NT], const WPtr<PACKED> (&wp)[QW], const uint8_t* tok,
                                        const uint8_t* toks, int K, int row0, int ntt, uint8_t* lds, int wave,
                                        int lane) {
-  if constexpr (WeightPrefetch<NT>::value == 2)
+  if constexpr (WeightPrefetch<NT, WF>::value == 3)
+    k_loop_pf3<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
+  else if constexpr (WeightPrefetch<NT, WF>::value == 2)
     k_loop_pf2<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);
   else
     k_loop_pf1<FMT, NT, PACKED, WEIGHTS_A, WF, QW>(acc, wp, tok, toks, K, row0, ntt, lds, wave, lane);

@@ -54,20 +54,38 @@ __global__ __launch_bounds__(256) void route_count(const KeyT* __restrict__ keys
   for (int a = threadIdx.x; a < A; a += blockDim.x) hist[(int64_t)a * gridDim.x + c] = lds_hist[a];
 }
 
-// Inclusive scan (sum, or max when MAX) of one int per thread over a 1024-thread block
-// (LDS, Hillis-Steele). Leaves the block total in part[1023].
+// Inclusive scan (sum, or max when MAX) of one int per thread over a 1024-thread block:
+// a shuffle scan within each wave, a scan of the 16 wave totals by wave 0, then each
+// wave adds the totals before it (three barriers). Leaves every thread's inclusive value
+// in part[t] (the block total in part[1023]) for the callers that read another thread's.
 template <bool MAX = false>
 __device__ int block_inclusive_scan_1024(int v, int* part) {
-  const int t = threadIdx.x;
-  part[t] = v;
-  __syncthreads();
-  for (int d = 1; d < 1024; d <<= 1) {
-    const int other = t >= d ? part[t - d] : (MAX ? INT_MIN : 0);
-    __syncthreads();
-    part[t] = MAX ? max(part[t], other) : part[t] + other;
-    __syncthreads();
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  constexpr int kId = MAX ? INT_MIN : 0;
+  auto op = [](int a, int b) { return MAX ? max(a, b) : a + b; };
+  int x = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x = op(x, y);
   }
-  return part[t];
+  if (lane == 63) part[wave] = x;
+  __syncthreads();
+  if (wave == 0) {
+    int w = lane < 16 ? part[lane] : kId;
+#pragma unroll
+    for (int d = 1; d < 16; d <<= 1) {
+      const int y = __shfl_up(w, d);
+      if (lane >= d) w = op(w, y);
+    }
+    if (lane < 16) part[lane] = w;
+  }
+  __syncthreads();
+  if (wave > 0) x = op(part[wave - 1], x);
+  __syncthreads();   // every read of the wave totals is done before part is overwritten
+  part[t] = x;
+  __syncthreads();
+  return x;
 }
 
 // Exclusive scan of one expert's chunk counts (one wave per expert, 64 chunks per step,

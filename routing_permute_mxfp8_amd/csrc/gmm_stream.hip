@@ -336,8 +336,9 @@ __device__ __forceinline__ void issue_scales(const StreamArgs& p, const Item& c,
 // between(q): the loads of later steps go out in small groups between the MFMA groups, so
 // that a wave whose loads wait for room in the memory pipeline still keeps its matrix
 // core busy. The E8M0 scales come from the step's scale group (byte k % 4 of a packed or
-// token dword; byte lane / 16 of the ND dword of step k % 4).
-template <int FMT, bool PACKED, int WF, int NW, class Between>
+// token dword; byte lane / 16 of the ND dword of step k % 4). ZERO_C: the MFMAs take a
+// zero C operand (an item's first step) instead of the accumulators.
+template <int FMT, bool PACKED, int WF, int NW, bool ZERO_C, class Between>
 __device__ __forceinline__ void step_mfma(v4f (&acc)[kCB][NW], const uint8_t* slot, const uint8_t* group, int k,
                                           int lane, int wave, const v8i (&t)[NW], Between&& between) {
   using SW = StreamW<WF, PACKED>;
@@ -367,7 +368,8 @@ __device__ __forceinline__ void step_mfma(v4f (&acc)[kCB][NW], const uint8_t* sl
   for (int q = 0; q < kCB; ++q) {
     if (q + 1 < kCB) read(q + 1, a[(q + 1) & 1], sa[(q + 1) & 1]);
 #pragma unroll
-    for (int j = 0; j < NW; ++j) acc[q][j] = mfma_mx16_ab<WF, FMT>(a[q & 1], t[j], acc[q][j], sa[q & 1], tsc[j]);
+    for (int j = 0; j < NW; ++j)
+      acc[q][j] = mfma_mx16_ab<WF, FMT>(a[q & 1], t[j], ZERO_C ? v4f{0.f, 0.f, 0.f, 0.f} : acc[q][j], sa[q & 1], tsc[j]);
     between(q);
     __builtin_amdgcn_sched_barrier(0);   // keep the weight tile reads one tile ahead, not all hoisted
   }
@@ -593,7 +595,8 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
     // kc + kTokLead go into set (tn), the set the previous step used; a step kc = 0 mod 4
     // also loads the scale group of steps kc + 4 .. kc + 7 into the other group.
     // (even: kc is even; with six slots only even steps wait and meet the barrier)
-    auto step = [&](int kc, bool group_start, bool even, v8i(&tc)[RT], v8i(&tn)[RT]) {
+    auto step = [&]<bool ZERO_C>(std::integral_constant<bool, ZERO_C>, int kc, bool group_start, bool even, v8i(&tc)[RT],
+                                 v8i(&tn)[RT]) {
       constexpr bool kPaired = SW::kSlots == 6;
       if (!kPaired || even) {
         wait_vmcnt<kPaired ? SW::template kWaitPair<RT> : SW::template kWait<RT>>();
@@ -625,16 +628,32 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
                                         wave);
         }
       };
-      step_mfma<FMT, PACKED, WF, RT>(acc, ldsr + cslot * SW::kSlotBytes, groups_r + grp * SW::kGroupBytes, kc, lane,
-                                      wave, tc, between);
+      step_mfma<FMT, PACKED, WF, RT, ZERO_C>(acc, ldsr + cslot * SW::kSlotBytes, groups_r + grp * SW::kGroupBytes, kc,
+                                             lane, wave, tc, between);
       cslot = cslot == SW::kSlots - 1 ? 0 : cslot + 1;
     };
-    // K steps of item n (a multiple of 4): t0..t3 in turn, the first step uses t0
-    for (int k = 0; k < ks; k += 4) {
-      step(k, true, true, t0, t3);
-      step(k + 1, false, false, t1, t0);
-      step(k + 2, false, true, t2, t1);
-      step(k + 3, false, false, t3, t2);
+    // K steps of item n (a multiple of 4): t0..t3 in turn, the first step uses t0. The
+    // GMM2 instances of at most four tiles a wave start an item with a zero C operand in
+    // its first step's MFMAs rather than a zeroing pass after the previous item (measured
+    // ~1.5% off GMM2; in GMM1 the peeled first group measured slower, and the five-tile
+    // instances then spill registers).
+    constexpr bool kZeroC = GMM == 2 && RT < 5;
+    const std::integral_constant<bool, false> accum;
+    int k0 = 0;
+    if constexpr (kZeroC) {
+      const std::integral_constant<bool, true> zero_c;
+      step(zero_c, 0, true, true, t0, t3);
+      step(accum, 1, false, false, t1, t0);
+      step(accum, 2, false, true, t2, t1);
+      step(accum, 3, false, false, t3, t2);
+      grp ^= 1;
+      k0 = 4;
+    }
+    for (int k = k0; k < ks; k += 4) {
+      step(accum, k, true, true, t0, t3);
+      step(accum, k + 1, false, false, t1, t0);
+      step(accum, k + 2, false, true, t2, t1);
+      step(accum, k + 3, false, false, t3, t2);
       grp ^= 1;
     }
     const int nw = wave_tiles(cur.nrows, wave);
@@ -642,7 +661,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
       epilogue1<FMT, EPI, H1, RT>(p, cur, acc, nw, wave);
     else
       epilogue2<OBF16, RT>(p, cur, acc, nw, wave);
-    zero_acc(acc);
+    if constexpr (!kZeroC) zero_acc(acc);
     cur = nxt;
     nxt = nn;
     if (n + 3 < count) nn = load_item(p.tiles, first + (n + 3) * stride, ncb);

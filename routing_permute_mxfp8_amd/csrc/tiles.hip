@@ -169,22 +169,35 @@ __global__ __launch_bounds__(256) void pack_tokens_kernel(const uint8_t* __restr
     if (!tile_item(it, tt, kq, chunks, &ti)) continue;
     const bool valid = r < ti.nvalid;
     const int64_t row = valid && row_token ? (int64_t)row_token[ti.srow + r] : ti.srow + r;
+    // The loads of all four steps first (steps past the end re-read the last one and are
+    // not stored), then the stores: a wave keeps 128 bytes a lane in flight.
+    const uint8_t* src = codes + row * K + 16 * g;
+    u32x4 lo[4], hi[4];
+    uint32_t sb[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int s = min(4 * ti.quad + i, ks - 1);
+      lo[i] = hi[i] = u32x4{0u, 0u, 0u, 0u};
+      sb[i] = 0;
+      if (valid) {
+        lo[i] = *reinterpret_cast<const u32x4*>(src + 128 * s);
+        hi[i] = *reinterpret_cast<const u32x4*>(src + 128 * s + 64);
+        sb[i] = scales[row * kb + 4 * s + g];
+      }
+    }
     uint32_t sword = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * ti.quad + i < ks) sword |= sb[i] << (8 * i);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int s = 4 * ti.quad + i;
       if (s >= ks) break;
-      u32x4 lo = {0u, 0u, 0u, 0u}, hi = {0u, 0u, 0u, 0u};
-      if (valid) {
-        lo = *reinterpret_cast<const u32x4*>(codes + row * K + 128 * s + 16 * g);
-        hi = *reinterpret_cast<const u32x4*>(codes + row * K + 128 * s + 64 + 16 * g);
-        sword |= (uint32_t)scales[row * kb + 4 * s + g] << (8 * i);
-      }
       // non-temporal: the tiles are read back by the GEMM's own loads (measured: GMM1 of
       // the prefill-shaped layer 2% faster than after plain stores)
       uint8_t* tb = out + t16_codes(ti.tile, ks, s);
-      __builtin_nontemporal_store(lo, reinterpret_cast<u32x4*>(tb) + lane);
-      __builtin_nontemporal_store(hi, reinterpret_cast<u32x4*>(tb + 1024) + lane);
+      __builtin_nontemporal_store(lo[i], reinterpret_cast<u32x4*>(tb) + lane);
+      __builtin_nontemporal_store(hi[i], reinterpret_cast<u32x4*>(tb + 1024) + lane);
     }
     reinterpret_cast<uint32_t*>(out_scales + t16_scales(ti.tile, kq, ti.quad))[lane] = sword;
   }

@@ -146,7 +146,7 @@ struct MegaWs {
   bool fold;
   int* all_count;
   int64_t routed_padded;
-  // LDS-streaming GEMMs: the chunk list split by chunk size (one launch per class)
+  // LDS-streaming GEMMs: the chunk list split by chunk size (one phase per class)
   int4* cls_tiles;
   int* cls_count;
   // x quantized once in token order (row-major codes [tokens, hidden] and scales

@@ -535,28 +535,65 @@ __device__ __forceinline__ void zero_acc(v4f (&acc)[kCB][RT]) {
 // such a load writes); the reads of a weight slot are ordered after its loads by the
 // explicit wait and barrier at the top of each K step, with a compiler-level memory fence
 // after the barrier.
+// The channel blocks of an item's chunk.
+template <int GMM>
+__device__ __forceinline__ int channel_blocks(const StreamArgs& p) {
+  return GMM == 1 ? ((p.inter >> 4) + kCB / 2 - 1) / (kCB / 2) : ((p.N >> 4) + kCB - 1) / kCB;
+}
+
+// The items first, first + stride, ... < last of the chunk list `tiles`.
 template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
-__device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __restrict__ lds,
-                                            const uint8_t* __restrict__ ldsr);
+__device__ __forceinline__ void stream_body(const StreamArgs& p, const int4* tiles, int first, int stride, int last,
+                                            uint8_t* __restrict__ lds, const uint8_t* __restrict__ ldsr);
 
 template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
 void gmm_stream_kernel(StreamArgs p) {
   extern __shared__ __align__(16) uint8_t lds_area[];
-  stream_body<FMT, PACKED, WF, GMM, EPI, OBF16, H1, RT>(p, lds_area, lds_area);
+  int first, stride, last;
+  block_items(*p.tile_count * channel_blocks<GMM>(p), &first, &stride, &last);
+  stream_body<FMT, PACKED, WF, GMM, EPI, OBF16, H1, RT>(p, p.tiles, first, stride, last, lds_area, lds_area);
+}
+
+// The three chunk-size classes in one launch, each by the instance of its token tiles a
+// wave, one class after the other (most tiles first). Each XCD takes a contiguous share
+// of every class's items, and the XCD's workgroups deal its items round robin, the deal
+// continuing from class to class: a workgroup left with one item fewer of a class gets
+// the next class's first items, so every workgroup ends within about one item of the
+// others (one launch a class leaves the last round of each class part-empty).
+template <int FMT, int WF, int GMM, int EPI, bool OBF16>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1)))
+void gmm_stream_classes_kernel(StreamArgs p, StreamClasses cl) {
+  static_assert(kStreamClasses == 3 && kStreamClassRT[2] == kRT, "classes of 2, 4 and 5 token tiles a wave");
+  extern __shared__ __align__(16) uint8_t lds_area[];
+  const int ncb = channel_blocks<GMM>(p);
+  const int xcd = blockIdx.x % kXcds, j = blockIdx.x / kXcds, per = gridDim.x / kXcds;
+  int dealt = 0;   // items of the earlier classes dealt on this XCD, modulo per
+  auto phase = [&]<int C>(std::integral_constant<int, C>) {
+    const int total = cl.count[C] * ncb;
+    const int lo = (int)(((int64_t)total * xcd) / kXcds), hi = (int)(((int64_t)total * (xcd + 1)) / kXcds);
+    const int first = lo + (j - dealt + per) % per;
+    if (first < hi) {   // uniform per workgroup
+      stream_body<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[C]>(p, cl.tiles + C * cl.stride, first, per,
+                                                                           hi, lds_area, lds_area);
+      __syncthreads();   // every wave is done with the LDS slots before the next class's prologue fills them
+    }
+    dealt = (dealt + (hi - lo)) % per;
+  };
+  phase(std::integral_constant<int, 2>());
+  phase(std::integral_constant<int, 1>());
+  phase(std::integral_constant<int, 0>());
 }
 
 template <int FMT, bool PACKED, int WF, int GMM, int EPI, bool OBF16, bool H1, int RT>
-__device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __restrict__ lds,
-                                            const uint8_t* __restrict__ ldsr) {
+__device__ __forceinline__ void stream_body(const StreamArgs& p, const int4* tiles, int first, int stride, int last,
+                                            uint8_t* __restrict__ lds, const uint8_t* __restrict__ ldsr) {
   using SW = StreamW<WF, PACKED>;
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ks = p.K >> 7, kq = (ks + 3) >> 2;
   const int n16 = p.N >> 4, i16 = p.inter >> 4;
   const LaneOffsets lofs = lane_offsets<PACKED, WF>(p.K, lane);
-  const int ncb = GMM == 1 ? (i16 + kCB / 2 - 1) / (kCB / 2) : (n16 + kCB - 1) / kCB;
-  int first, stride, last;
-  block_items(*p.tile_count * ncb, &first, &stride, &last);
+  const int ncb = channel_blocks<GMM>(p);
   const int count = first < last ? (last - first + stride - 1) / stride : 0;
   if (count == 0) return;
 
@@ -566,9 +603,9 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
 
   // items n (cur), n + 1 (nxt) and n + 2 (nn, read an item early so that its scalar loads
   // have landed when it becomes nxt); past the last item each repeats the last one
-  Item cur = load_item(p.tiles, first, ncb);
-  Item nxt = count > 1 ? load_item(p.tiles, first + stride, ncb) : cur;
-  Item nn = count > 2 ? load_item(p.tiles, first + 2 * stride, ncb) : nxt;
+  Item cur = load_item(tiles, first, ncb);
+  Item nxt = count > 1 ? load_item(tiles, first + stride, ncb) : cur;
+  Item nn = count > 2 ? load_item(tiles, first + 2 * stride, ncb) : nxt;
 
   // prologue: the loads of steps -4..-1 in the steady state's order, S0 (the scale group
   // of steps 0..3), W0, T0 W1, T1 W2, T2 W3 (all in item 0: ks >= 4)
@@ -664,7 +701,7 @@ __device__ __forceinline__ void stream_body(const StreamArgs& p, uint8_t* __rest
     if constexpr (!kZeroC) zero_acc(acc);
     cur = nxt;
     nxt = nn;
-    if (n + 3 < count) nn = load_item(p.tiles, first + (n + 3) * stride, ncb);
+    if (n + 3 < count) nn = load_item(tiles, first + (n + 3) * stride, ncb);
   }
   wait_vmcnt<0>();   // no direct-to-LDS load still writes when the workgroup's LDS is released
 }
@@ -730,17 +767,15 @@ void set_shared(StreamArgs& a, const SharedGroups& sh, int wfp4, int packed) {
     set_shared_t<false>(a, sh, wfp4 != 0);
 }
 
-// One launch per chunk class, each with the instance of that class's token tiles a wave.
+// The chunk classes in one launch (gmm_stream_classes_kernel).
 template <int FMT, int WF, int GMM, int EPI, bool OBF16>
-hipError_t stream_classes(StreamArgs a, const StreamClasses& cl, hipStream_t st) {
-  static_assert(kStreamClasses == 3 && kStreamClassRT[2] == kRT, "classes of 2, 4 and 5 token tiles a wave");
-  hipError_t e;
-  a.tiles = cl.tiles; a.tile_count = cl.count;
-  if ((e = stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[0]>(a, st)) != hipSuccess) return e;
-  a.tiles = cl.tiles + cl.stride; a.tile_count = cl.count + 1;
-  if ((e = stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[1]>(a, st)) != hipSuccess) return e;
-  a.tiles = cl.tiles + 2 * cl.stride; a.tile_count = cl.count + 2;
-  return stream_go<FMT, true, WF, GMM, EPI, OBF16, false, kStreamClassRT[2]>(a, st);
+hipError_t stream_classes(const StreamArgs& a, const StreamClasses& cl, hipStream_t st) {
+  auto kern = gmm_stream_classes_kernel<FMT, WF, GMM, EPI, OBF16>;
+  LaunchShape ls;
+  hipError_t e = persistent_shape(kern, StreamW<WF, true>::kLds, &ls);
+  if (e != hipSuccess) return e;
+  kern<<<ls.grid, 256, ls.lds, st>>>(a, cl);
+  return hipGetLastError();
 }
 
 }  // namespace

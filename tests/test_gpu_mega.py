@@ -491,11 +491,13 @@ def check_gmm2_rows(cfg, experts, ffns, cache, wf):
     assert err <= 2e-3 and worst <= 2e-3
 
 
-def full_size_check(name, n_random, wf=rp.WEIGHTS_ND, seed=7):
+def full_size_check(name, n_random, wf=rp.WEIGHTS_ND, seed=7, plain_packed=False):
     """The layer at full size in the benchmark's configuration (weights made on the GPU
     and quantized by the library):
     * the plain call (the kernel instances the benchmark times) equals the debug call
-      bit for bit;
+      bit for bit; with plain_packed, so does a plain call on the packed copy of ND
+      weights (the packed layout's kernels, one instance per chunk-size class, against
+      the ND debug call's);
     * routing, counts and the sampled rows' X^ / S_X exact;
     * the special experts (the busiest one, every expert whose rows take more than one
       GEMM chunk, the least busy one): all their rows through GMM1 (h1, A^) and GMM2 (O
@@ -525,6 +527,14 @@ def full_size_check(name, n_random, wf=rp.WEIGHTS_ND, seed=7):
     say("  layer done (plain and debug calls)")
     assert_same_layer(y_fast, etn_fast, y, etn)
     del y_fast
+    if plain_packed:
+        assert wf == rp.WEIGHTS_ND and shared is None
+        packed = [*rp.pack_weights(weights[0], weights[1]), *rp.pack_weights(weights[2], weights[3])]
+        y_p, etn_p = rp.mega_moe(*args[:3], *packed, quant_out_dtype=FP8[cfg.fmt], weight_format=rp.WEIGHTS_PACKED)
+        torch.cuda.synchronize()
+        say("  plain call on packed weights done")
+        assert_same_layer(y_p, etn_p, y, etn)
+        del y_p, packed
     r = routing.init_routing(ids, cfg.experts)
     counts = r["counts"]
     assert np.array_equal(etn.cpu().numpy(), counts.astype(np.int32))
@@ -618,7 +628,7 @@ def test_full_size_decode():
 
 @pytest.mark.timeout(900)
 def test_full_size_skewed():
-    full_size_check("skewed", n_random=64)
+    full_size_check("skewed", n_random=64, plain_packed=True)
 
 
 @pytest.mark.timeout(900)

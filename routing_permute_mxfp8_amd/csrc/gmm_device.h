@@ -183,6 +183,8 @@ __device__ __forceinline__ float gated_act(float g, float u, const ActParams& p)
     const float lb = lin ? p.lin_beta : 1.0f;
     const float l = lin ? lb * tanh_nb(u / lb) : u;
     return p.beta * tanh_nb(g / p.beta) * sigmoid(g) * l;
+  } else if constexpr (KIND == kActSwigluNoClamp) {   // swiglu with c = +inf: SiLU(G) U
+    return g * sigmoid(g) * u;
   } else {
     return swiglu_act(g, u, p.clamp);
   }

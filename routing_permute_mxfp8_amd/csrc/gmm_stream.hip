@@ -786,9 +786,13 @@ hipError_t launch_gmm1_stream(const Gmm1Params& p, hipStream_t st) {
   a.K = p.hidden; a.N = 2 * p.inter; a.inter = p.inter; a.aq = p.aq; a.sa = p.sa; a.h1 = p.h1; a.act = p.act;
   set_shared(a, p.shared, p.wfp4, p.packed);
   // chunk classes: the packed FP8 SwiGLU instance without the h1 output
-  if (p.classes.tiles && p.packed && !p.wfp4 && !p.h1 && p.act.kind == 0)
+  if (p.classes.tiles && p.packed && !p.wfp4 && !p.h1 && p.act.kind == 0) {
+    if (p.act.clamp == __builtin_huge_valf())
+      return p.fmt == 0 ? stream_classes<0, 0, 1, kActSwigluNoClamp, false>(a, p.classes, st)
+                        : stream_classes<1, 1, 1, kActSwigluNoClamp, false>(a, p.classes, st);
     return p.fmt == 0 ? stream_classes<0, 0, 1, 0, false>(a, p.classes, st)
                       : stream_classes<1, 1, 1, 0, false>(a, p.classes, st);
+  }
   if (p.wfp4) {
     if (p.fmt != 0) return hipErrorInvalidValue;
     return p.packed ? stream_gmm1<0, true, kFmtFp4>(a, p.act.kind, st) : stream_gmm1<0, false, kFmtFp4>(a, p.act.kind, st);

@@ -112,6 +112,7 @@ struct ActParams {
   float lin_beta = 0.0f;         // situglu linear beta; 0 = L(U) = U
 };
 constexpr int kActGelu = 4;
+constexpr int kActSwigluNoClamp = 5;   // kind 0 with c = +inf (an instance of the streaming GMM1)
 
 // Token operands and GMM1's requantized output are in the tiled layout, indexed by the
 // chunks' padded rows; h1, o, row_token and row_weight are indexed by sorted rows.

@@ -349,6 +349,8 @@ def bench_mega(args, torch, rp, moe_inputs):
     roofline["measured_peak"] = ref
     roofline["frac_of_measured"] = round(roofline["achieved"] / ref, 4)
     roofline["other"] = {k: v for k, v in roof.items() if k != dominant}
+    for v in roofline["other"].values():
+        v["traffic"] = measured_traffic(v["kernel"], cfg.name + ("-mxfp4" if fp4 else ""))
     total_bytes = work["gmm1"]["bytes"] + work["gmm2"]["bytes"] + work["combine"]["bytes"] + work["shared"]["bytes"]
     total_flops = work["gmm1"]["flops"] + work["gmm2"]["flops"] + work["shared"]["flops"]
     out = dict(metric="MoE layer tokens/s", value=round(cfg.tokens / (ms * 1e-3), 1), unit="tokens/s", n_gpus=1,

@@ -25,8 +25,10 @@
 // chunk's token tiles w, w + 4, w + 8, ... (up to kRT), loads them into registers three
 // K steps ahead, and multiplies them with all kCB weight tiles of the step read from LDS
 // (V_MFMA_SCALE_F32_16X16X128_F8F6F4, weights in the A slot: a lane holds 4 consecutive
-// channels of one token row). Token tiles a wave does not own cost no MFMA time, so a
-// chunk of a few rows costs little more than its weight stream.
+// channels of one token row). A wave runs the MFMAs of RT tiles every step whether or
+// not the chunk has them (tiles past its end repeat its first tile, their results are
+// not stored): the chunk-size classes (RT = 2, 4, 5) keep that close to the chunk's own
+// tiles, so a chunk of a few rows costs little more than its weight stream.
 //
 // Per K step and wave: one fixed vmcnt wait (this step's weight slot, landed by every
 // wave's own loads) and one barrier (every wave's loads have landed; every wave is done

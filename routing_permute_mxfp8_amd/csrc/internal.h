@@ -129,8 +129,8 @@ struct SharedGroups {
 // The chunk list of an LDS-streaming GEMM split by chunk size: class c (list tiles +
 // c stride, count[c]) holds the chunks of more than 4 kStreamClassRT[c - 1] and at most
 // 4 kStreamClassRT[c] token tiles, run by the instance with kStreamClassRT[c] token tiles
-// a wave (no MFMAs for tiles past the chunk's end). tiles = nullptr: one list, one
-// launch.
+// a wave (a 5-tile wave's MFMAs for a 40-row chunk would be mostly idle tiles); the
+// classes run as phases of one launch. tiles = nullptr: one list, the 5-tile instance.
 constexpr int kStreamClasses = 3;
 constexpr int kStreamClassRT[kStreamClasses] = {2, 4, 5};
 struct StreamClasses {

@@ -26,8 +26,8 @@
 // K steps ahead, and multiplies them with all kCB weight tiles of the step read from LDS
 // (V_MFMA_SCALE_F32_16X16X128_F8F6F4, weights in the A slot: a lane holds 4 consecutive
 // channels of one token row). A wave runs the MFMAs of RT tiles every step whether or
-// not the chunk has them (tiles past its end repeat its first tile, their results are
-// not stored): the chunk-size classes (RT = 2, 4, 5) keep that close to the chunk's own
+// not the chunk has them (tiles past its end load zeros, their results are not
+// stored): the chunk-size classes (RT = 2, 4, 5) keep that close to the chunk's own
 // tiles, so a chunk of a few rows costs little more than its weight stream.
 //
 // Per K step and wave: one fixed vmcnt wait (this step's weight slot, landed by every
@@ -36,8 +36,9 @@
 // the wait and the barrier come every second step and cover two steps' slots (the
 // waves then drift apart by up to a step between barriers); then the token loads of step + 3 and this wave's
 // share of the weight loads of step + kLead (always the same number of each, so the
-// wait count is a constant: loads past the last step or for tiles the wave does not own
-// read valid addresses again); then the MFMAs. The epilogue of an item (activation and
+// wait count is a constant: loads past the last step read valid addresses again, and
+// those of token tiles past the chunk's end fall outside the chunk's buffer resource,
+// whose range check returns zeros without touching memory); then the MFMAs. The epilogue of an item (activation and
 // requantization, or the O rows) runs after its last K step, while the next item's loads
 // are in flight. The item descriptions live in scalar registers, read through the scalar
 // cache an item ahead: an LDS read in the K loop would have to wait for every
@@ -272,8 +273,10 @@ __device__ __forceinline__ void issue_weights(const StreamArgs& p, const Item& c
   for (int i = 0; i < kCB / 4; ++i) issue_weight_tile<GMM, PACKED, WF>(L, i, slot, p.K, n16, i16, lo, wave);
 }
 
-// The token loads of step k of item c: descriptors of the chunk's tiles (tiles the wave
-// does not own load the chunk's first tile again).
+// The token loads of step k of item c: descriptors of exactly the chunk's tiles (a wave's
+// tiles past the chunk's end are addressed one past its last tile: the range check
+// returns zero codes and scales for them, measured on gfx950 for register and
+// direct-to-LDS buffer loads, with no memory traffic; zero operands also draw less power).
 struct TokenStep {
   __amdgpu_buffer_rsrc_t tr, sr;
   int ntt, k;
@@ -287,7 +290,7 @@ __device__ __forceinline__ TokenStep token_step(const StreamArgs& p, const Item&
 }
 
 __device__ __forceinline__ int wave_tile(const TokenStep& L, int j, int wave) {
-  return 4 * j + wave < L.ntt ? 4 * j + wave : 0;
+  return 4 * j + wave < L.ntt ? 4 * j + wave : L.ntt;
 }
 
 // This wave's j-th token tile of a step (chunk tile 4 j + wave): its codes into registers.
